@@ -1,0 +1,336 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+* literal tables and hand-derived cases (tests/golden/), from the OCP MX v1.0
+  element and scale definitions that the MXFP6 format on the pages follows;
+* exhaustive enumeration (all 64 codes of both formats);
+* brute force with exact rationals / Python integers on small inputs;
+* library routines for the special cases (torch's GELU-tanh, torch's fp32 ->
+  bf16 rounding);
+* invariants of the scale rule (power-of-two shifts, range of amax/2**shared).
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mx_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+# ---------------------------------------------------------------- element tables
+
+def test_magnitudes_match_literal_table():
+    for line in _golden_lines("mx_element_magnitudes.txt"):
+        fmt, *vals = line.split()
+        want = np.array([float(v) for v in vals])
+        assert want.shape == (32,)
+        np.testing.assert_array_equal(O.magnitudes(fmt), want)
+        # negative half mirrors the positive half (code c+32 = -value(c))
+        full = O.element_values(fmt)
+        np.testing.assert_array_equal(full[32:], -want)
+        assert math.copysign(1.0, full[32]) == -1.0  # code 32 is -0
+
+
+@pytest.mark.parametrize("fmt,emax,vmax,min_sub,min_norm", [
+    ("e2m3", 2, 7.5, 0.125, 1.0),
+    ("e3m2", 4, 28.0, 0.0625, 0.25),
+])
+def test_format_constants(fmt, emax, vmax, min_sub, min_norm):
+    mags = O.magnitudes(fmt)
+    assert O.emax_elem(fmt) == emax
+    assert mags.max() == vmax
+    assert mags[1] == min_sub
+    assert np.all(np.diff(mags) > 0), "codes 0..31 must increase strictly"
+    # smallest normal: exponent field 1, mantissa 0
+    mbits = {"e2m3": 3, "e3m2": 2}[fmt]
+    assert mags[1 << mbits] == min_norm
+    assert np.all(np.isfinite(O.element_values(fmt)))
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_exhaustive_round_trip(fmt):
+    """Every code decodes and re-encodes to itself, in a block whose scale is
+    fixed to 2**0 by a max-magnitude element (so the block scale byte is 127)."""
+    vals = O.element_values(fmt)
+    vmax = O.magnitudes(fmt).max()
+    for c in range(64):
+        blk = np.zeros((1, 32))
+        blk[0, 0] = vmax
+        blk[0, 5] = vals[c]
+        codes, scales = O.quantize(blk, fmt)
+        assert scales[0, 0] == 127
+        assert codes[0, 5] == c, (fmt, c, codes[0, 5])
+        back = O.dequantize(codes, scales, fmt)
+        assert back[0, 5] == vals[c]
+        assert math.copysign(1.0, back[0, 5]) == math.copysign(1.0, vals[c])
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("shift", [-130, -20, -1, 3, 60, 120])
+def test_round_trip_under_any_scale(fmt, shift):
+    """Scaling a block by 2**k changes only the scale byte (by k), never the codes."""
+    vals = O.element_values(fmt)
+    vmax = O.magnitudes(fmt).max()
+    base = np.zeros((2, 32))
+    base[:, 0] = vmax
+    base[0, 1:] = vals[1:32]
+    base[1, 1:] = vals[33:64]
+    c0, s0 = O.quantize(base, fmt)
+    scaled = np.ldexp(base, shift)
+    if not np.all(np.isfinite(scaled)) or shift < -120:
+        pytest.skip("scale outside the normal E8M0 range for this table")
+    c1, s1 = O.quantize(scaled, fmt)
+    np.testing.assert_array_equal(c0, c1)
+    np.testing.assert_array_equal(s1.astype(int), s0.astype(int) + shift)
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_element_rounding_cases():
+    for line in _golden_lines("element_rounding_cases.txt"):
+        fmt, r, want = line.split()
+        got = O.round_to_code(np.array([float(r)]), fmt)[0]
+        assert int(got) == int(want), (fmt, r, int(got), want)
+
+
+def test_block_cases():
+    for line in _golden_lines("block_cases.txt"):
+        head, vals, codes = (p.strip() for p in line.split("|"))
+        fmt, scale = head.split()
+        v = [float(x) for x in vals.split()]
+        c = [int(x) for x in codes.split()]
+        blk = np.zeros((1, 32))
+        blk[0, : len(v)] = v
+        got_c, got_s = O.quantize(blk, fmt)
+        assert int(got_s[0, 0]) == int(scale), (line, int(got_s[0, 0]))
+        assert got_c[0, : len(c)].tolist() == c, (line, got_c[0, : len(c)].tolist())
+        assert not np.any(got_c[0, len(c):] % 32), line  # zero padding stays +-0
+
+
+def _brute_code(r: Fraction, fmt: str, negative: bool) -> int:
+    """Exhaustive search over all 32 magnitudes with exact rationals."""
+    mags = [Fraction(x) for x in O.magnitudes(fmt)]
+    a = abs(r)
+    best = None
+    for c, m in enumerate(mags):
+        d = abs(a - m)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0 and best[1] % 2 == 1):
+            best = (d, c)
+    return best[1] + (32 if negative else 0)
+
+
+def _brute_shared(amax: Fraction, emax: int) -> int:
+    """The unique integer s with 2**(s+emax) <= amax < 2**(s+emax+1), by search."""
+    if amax == 0:
+        return -127
+    s = -400
+    while not (Fraction(2) ** (s + emax) <= amax < Fraction(2) ** (s + emax + 1)):
+        s += 1
+    return max(-127, min(127, s))
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_quantize_matches_exact_brute_force(fmt):
+    rng = np.random.default_rng(7)
+    emax = {"e2m3": 2, "e3m2": 4}[fmt]
+    # bf16-valued inputs over a wide range of magnitudes, incl. ties and zeros
+    x = rng.standard_normal((24, 32)).astype(np.float32)
+    x *= np.exp2(rng.integers(-40, 40, size=(24, 1))).astype(np.float32)
+    x[3, :] = 0.0
+    x[4, ::3] = -0.0
+    x[5, :] = np.float32(2.0 ** -133) * rng.integers(-3, 4, size=32)  # bf16 subnormals
+    x = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    codes, scales = O.quantize(x, fmt)
+    for i in range(x.shape[0]):
+        fr = [Fraction(float(v)) for v in x[i]]
+        s = _brute_shared(max(abs(v) for v in fr), emax)
+        assert int(scales[i, 0]) == s + 127
+        for j in range(32):
+            want = _brute_code(fr[j] / Fraction(2) ** s, fmt, math.copysign(1.0, x[i, j]) < 0)
+            assert int(codes[i, j]) == want, (fmt, i, j, x[i, j])
+
+
+def test_scale_invariant_on_random_blocks():
+    rng = np.random.default_rng(11)
+    for fmt in ("e2m3", "e3m2"):
+        emax = O.emax_elem(fmt)
+        x = rng.standard_t(3, size=(200, 64)) * np.exp2(rng.integers(-60, 60, size=(200, 1)))
+        x = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+        _, scales = O.quantize(x, fmt)
+        amax = np.abs(x).reshape(200, 2, 32).max(axis=2)
+        shared = scales.astype(np.int64) - 127
+        ratio = amax / np.ldexp(1.0, shared)
+        assert np.all(ratio >= 2.0 ** emax) and np.all(ratio < 2.0 ** (emax + 1))
+
+
+def test_nonfinite_block_gets_nan_scale():
+    x = np.zeros((1, 64))
+    x[0, 3] = np.inf
+    x[0, 40] = 1.0
+    codes, scales = O.quantize(x, "e2m3")
+    assert scales[0, 0] == 0xFF and not codes[0, :32].any()
+    assert scales[0, 1] == 125 and codes[0, 40] == 24
+    assert np.isnan(O.e8m0_value(0xFF))
+
+
+# ---------------------------------------------------------------- packing
+
+def test_pack_cases():
+    for line in _golden_lines("pack_cases.txt"):
+        codes, hexbytes = (p.strip() for p in line.split("|"))
+        c = np.array([[int(x) for x in codes.split()]], dtype=np.uint8)
+        want = np.array([[int(h, 16) for h in hexbytes.split()]], dtype=np.uint8)
+        np.testing.assert_array_equal(O.pack(c), want)
+        np.testing.assert_array_equal(O.unpack(want, 32), c)
+
+
+def test_pack_round_trip_random():
+    rng = np.random.default_rng(3)
+    c = rng.integers(0, 64, size=(7, 96), dtype=np.uint8)
+    p = O.pack(c)
+    assert p.shape == (7, 72)
+    np.testing.assert_array_equal(O.unpack(p, 96), c)
+
+
+# ---------------------------------------------------------------- GEMM
+
+def _int_decode(code: int, fmt: str) -> int:
+    """Integer n with value = n * 2**-3 (E2M3) or n * 2**-4 (E3M2), from the bits."""
+    s = -1 if code & 32 else 1
+    if fmt == "e2m3":
+        e, m = (code >> 3) & 3, code & 7
+        n = m if e == 0 else (8 + m) << (e - 1)
+    else:
+        e, m = (code >> 2) & 7, code & 3
+        n = m if e == 0 else (4 + m) << (e - 1)
+    return s * n
+
+
+@pytest.mark.parametrize("fa,fw", [("e2m3", "e2m3"), ("e2m3", "e3m2"), ("e3m2", "e3m2")])
+@pytest.mark.parametrize("m,n,k", [(4, 4, 32), (3, 5, 64), (2, 3, 96)])
+def test_gemm_exact_integer_brute_force(fa, fw, m, n, k):
+    rng = np.random.default_rng([m, n, k, len(fa + fw)])
+    ca = rng.integers(0, 64, size=(m, k), dtype=np.uint8)
+    cw = rng.integers(0, 64, size=(n, k), dtype=np.uint8)
+    sa = rng.integers(110, 145, size=(m, k // 32), dtype=np.uint8)
+    sw = rng.integers(110, 145, size=(n, k // 32), dtype=np.uint8)
+    frac = {"e2m3": 3, "e3m2": 4}
+    c_ref, s_ref = O.gemm_ref(O.dequantize(ca, sa, fa), O.dequantize(cw, sw, fw))
+    for i in range(m):
+        for j in range(n):
+            exact = Fraction(0)
+            absum = Fraction(0)
+            for b in range(k // 32):
+                acc = 0
+                aacc = 0
+                for t in range(32 * b, 32 * b + 32):
+                    p = _int_decode(int(ca[i, t]), fa) * _int_decode(int(cw[j, t]), fw)
+                    acc += p
+                    aacc += abs(p)
+                sc = Fraction(2) ** (int(sa[i, b]) + int(sw[j, b]) - 254 - frac[fa] - frac[fw])
+                exact += acc * sc
+                absum += aacc * sc
+            assert abs(Fraction(float(c_ref[i, j])) - exact) <= Fraction(1, 10 ** 12) * absum
+            assert abs(Fraction(float(s_ref[i, j])) - absum) <= Fraction(1, 10 ** 12) * absum
+
+
+def test_gemm_one_hot_selects_columns():
+    """W rows that are one-hot pick single columns of A times both scales;
+    guards against a transposed operand or a dropped scale."""
+    rng = np.random.default_rng(5)
+    k = 64
+    ca = rng.integers(0, 64, size=(3, k), dtype=np.uint8)
+    sa = rng.integers(120, 135, size=(3, 2), dtype=np.uint8)
+    a = O.dequantize(ca, sa, "e2m3")
+    cw = np.zeros((4, k), dtype=np.uint8)
+    cols = [0, 17, 40, 63]
+    for j, col in enumerate(cols):
+        cw[j, col] = 8  # 1.0
+    sw = np.full((4, 2), 129, dtype=np.uint8)  # x4
+    c, s = O.gemm_ref(a, O.dequantize(cw, sw, "e2m3"))
+    for j, col in enumerate(cols):
+        np.testing.assert_array_equal(c[:, j], 4.0 * a[:, col])
+        np.testing.assert_array_equal(s[:, j], 4.0 * np.abs(a[:, col]))
+
+
+# ---------------------------------------------------------------- GELU
+
+def test_gelu_matches_torch_tanh_gelu():
+    x = np.concatenate([np.linspace(-12, 12, 4801), np.random.default_rng(2).standard_normal(5000) * 4])
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    # torch evaluates 1 + tanh(u), which cancels for negative u: allow its
+    # absolute error there (about 1e-16 * |x|)
+    err = np.abs(O.gelu_tanh(x) - ref)
+    assert np.all(err <= 1e-13 * np.abs(ref) + 4e-16 * np.maximum(1.0, np.abs(x)))
+
+
+def test_gelu_identities():
+    x = np.linspace(-20, 20, 8001)
+    g = O.gelu_tanh(x)
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(g - O.gelu_tanh(-x), x, atol=1e-12)  # odd part is x/2
+    big = np.array([10.0, 30.0])
+    np.testing.assert_array_equal(O.gelu_tanh(big), big)  # tanh saturates to 1
+    # equivalent logistic form x * sigmoid(2u)
+    u = np.sqrt(2 / np.pi) * (x + 0.044715 * x ** 3)
+    np.testing.assert_allclose(g, x / (1 + np.exp(-2 * u)), rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- bf16 rounding / tolerance
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-140, 120, 200000))).astype(np.float32)
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_bf16_ties_and_ulp():
+    one = 1.0
+    assert O.round_bf16(np.array([one + 2 ** -8]))[0] == 1.0  # tie, even
+    assert O.round_bf16(np.array([one + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6  # tie, even
+    assert O.round_bf16(np.array([one + 2 ** -8 + 2 ** -40]))[0] == 1.0 + 2 ** -7
+    assert O.ulp_bf16(np.array([1.0]))[0] == 2 ** -7
+    assert O.ulp_bf16(np.array([1.99]))[0] == 2 ** -7
+    assert O.ulp_bf16(np.array([2.0 ** -130]))[0] == 2 ** -133
+    assert O.ulp_fp32(np.array([1.0]))[0] == 2 ** -23
+
+
+def test_tolerance_checks():
+    c = np.array([1.0, 1.0, 1e-6])
+    s = np.array([1.0, 1.0, 10.0])
+    ok, n2 = O.check_bf16(np.array([1.0 + 2 ** -7, 1.0 + 2 ** -6, 5e-5]), c, s)
+    assert ok.tolist() == [True, False, True] and n2 == 1
+    assert O.check_fp32(np.array([1.0 + 1e-6, 1.0 + 2e-5, 0.0]), c, s).tolist() == [True, False, True]
+
+
+def test_fc1_reference_is_quantized_gelu():
+    rng = np.random.default_rng(4)
+    a = O.dequantize(*O.quantize(rng.standard_normal((8, 64)), "e2m3"), "e2m3")
+    w = O.dequantize(*O.quantize(rng.standard_normal((64, 64)) * 0.05, "e2m3"), "e2m3")
+    codes, scales, c, s, g = O.fc1_gelu_mx_ref(a, w)
+    assert codes.shape == (8, 64) and scales.shape == (8, 2)
+    deq = O.dequantize(codes, scales, "e2m3")
+    g32 = g.astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(g, O.gelu_tanh(c))
+    # each output lies within half an element spacing (at its block scale) of
+    # fp32(GELU(C)); a value above 7.5 scale units saturates to 7.5
+    unit = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+    r = np.abs(g32) / unit
+    spacing = np.ldexp(1.0, np.maximum(O.floor_log2(np.where(r > 0, r, 1.0)), 0) - 3)
+    allowed = np.where(r > 7.5, r - 7.5, 0.5 * spacing) * unit
+    assert np.all(np.abs(deq - g32) <= allowed * (1 + 1e-12))
