@@ -1,0 +1,211 @@
+"""Benchmark: MXFP6 GEMM TFLOPS on the DiT MLP (one MI355X).
+
+A step is one forward pass of the MLP hot path over 20480 tokens:
+  mx_quantize(x)                     bf16 [20480, 3072] -> E2M3 codes + scales
+  h = mx_gemm(x_mx, W1, GELU -> MX)  fc1 20480 x 3072 x 12288, E2M3 intermediate
+  y = mx_gemm(h, W2, bf16 out)       fc2 20480 x 12288 x 3072
+with weights pre-quantized once (untimed) and inputs resident in HBM.  value =
+2*M*N*K summed over both GEMMs / step time.  The skinny split-K path
+(M in {16, 8} x 16384 x 13312, E3M2 weights) is measured beside it on rotating
+weight copies (the weights fit in the 256 MB last-level cache otherwise), and
+the CPU oracle is timed on a bounded sample of the same step.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import microscaled_precision_gemm_amd as mx  # noqa: E402
+from microscaled_precision_gemm_amd import synthetic as syn  # noqa: E402
+
+METRIC = "MXFP6 GEMM TFLOPS + % of 10.1 PF MFMA peak (DiT MLP 20480x3072x12288)"
+PEAK_MXFP6_TFLOPS = 10100.0
+PEAK_HBM_GBS = 8000.0
+
+
+def _events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_mlp(steps: int, warmup: int):
+    fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
+    m, d, hdim = fc1.m, fc1.k, fc1.n
+    dev = torch.device("cuda:0")
+    x = syn.make_a(fc1).to(dev)
+    w1 = mx.mx_quantize(syn.make_w(fc1).to(dev), "e2m3")
+    w2 = mx.mx_quantize(syn.make_w(fc2).to(dev), "e2m3")
+    xq = mx.MXTensor(torch.empty((m, 3 * d // 4), dtype=torch.uint8, device=dev),
+                     torch.empty((m, d // 32), dtype=torch.uint8, device=dev), "e2m3", d)
+    h = mx.MXTensor(torch.empty((m, 3 * hdim // 4), dtype=torch.uint8, device=dev),
+                    torch.empty((m, hdim // 32), dtype=torch.uint8, device=dev), "e2m3", hdim)
+    y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mx.mx_quantize(x, "e2m3", out=xq)
+        if ev is not None:
+            ev[1].record()
+        mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh", out=h)
+        if ev is not None:
+            ev[2].record()
+        mx.mx_gemm(h, w2, out_kind="bf16", out=y)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(4) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    f1_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    f2_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    flops_gemm = 2.0 * m * d * hdim
+    return {
+        "wall_ms_per_step": wall * 1e3 / steps,
+        "quantize_ms": float(q_ms.mean()),
+        "fc1_ms": float(f1_ms.mean()),
+        "fc2_ms": float(f2_ms.mean()),
+        "fc1_ms_min": float(f1_ms.min()),
+        "fc2_ms_min": float(f2_ms.min()),
+        "flops_per_step": 2 * flops_gemm,
+        "flops_per_gemm": flops_gemm,
+        "quantize_bytes": m * d * 2 + m * d * 3 // 4 + m * d // 32,
+        "fc1_bytes": m * d * 3 // 4 + m * d // 32 + hdim * d * 3 // 4 + hdim * d // 32 + m * hdim * 3 // 4 + m * hdim // 32,
+        "fc2_bytes": m * hdim * 3 // 4 + m * hdim // 32 + d * hdim * 3 // 4 + d * hdim // 32 + m * d * 2,
+    }
+
+
+def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
+    w = syn.WORKLOADS["skinny"]
+    dev = torch.device("cuda:0")
+    a = syn.make_a(w, m=m).to(dev)
+    wb = syn.make_w(w).to(dev)
+    ws = [mx.mx_quantize(wb, w.w_fmt) for _ in range(copies)]
+    del wb
+    out = torch.empty((m, w.n), dtype=torch.bfloat16, device=dev)
+    work = torch.empty(mx.mx_gemm_workspace_size(m, w.n, w.k, True, splits), dtype=torch.uint8, device=dev)
+    for i in range(5):
+        mx.mx_gemm_splitk(a, ws[i % copies], splits, out=out, workspace=work)
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for i in range(iters):
+        mx.mx_gemm_splitk(a, ws[i % copies], splits, out=out, workspace=work)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    wbytes = w.n * w.k * 3 // 4 + w.n * w.k // 32
+    alg = wbytes + m * w.k * 2 + m * w.n * 2
+    return {"m": m, "splits": splits, "ms": ms, "algorithmic_bytes": alg, "gb_s": alg / ms / 1e6,
+            "hbm_frac": alg / ms / 1e6 / PEAK_HBM_GBS, "tflops": 2.0 * m * w.n * w.k / ms / 1e9}
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The CPU oracle (as written, untuned) on a bounded sample of the step:
+    the same MLP pass for a sample of token rows (weights quantized once,
+    untimed, as on the GPU side)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import mx_oracle as O
+
+    fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
+    d, hdim = fc1.k, fc1.n
+    w1 = O.dequantize(*O.quantize(syn.as_f64(syn.make_w(fc1)), "e2m3"), "e2m3")
+    w2 = O.dequantize(*O.quantize(syn.as_f64(syn.make_w(fc2)), "e2m3"), "e2m3")
+    x_all = syn.make_a(fc1, m=4096)
+
+    def run(rows):
+        x = syn.as_f64(x_all[:rows])
+        t0 = time.perf_counter()
+        a = O.dequantize(*O.quantize(x, "e2m3"), "e2m3")
+        codes, scales, *_ = O.fc1_gelu_mx_ref(a, w1)
+        O.gemm_ref(O.dequantize(codes, scales, "e2m3"), w2)
+        return time.perf_counter() - t0
+
+    rows = 32
+    t = run(rows)
+    rows = int(min(4096, max(32, rows * target_s / max(t, 1e-3))) // 32 * 32)
+    t = run(rows)
+    flops = 2 * 2.0 * rows * d * hdim
+    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"MLP fc1(GELU->E2M3)+fc2 on {rows} of 20480 token rows, float64 numpy, weights pre-quantized",
+            "seconds": t, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--skinny-iters", type=int, default=100)
+    args = p.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+
+    r = bench_mlp(args.steps, args.warmup)
+    ms_step = r["wall_ms_per_step"]
+    value = r["flops_per_step"] / ms_step / 1e9  # TFLOP/s
+    # dominant kernel: the slower of the two GEMMs, timed with events on its own stream
+    dom = "fc1" if r["fc1_ms"] >= r["fc2_ms"] else "fc2"
+    dom_ms = r[f"{dom}_ms"]
+    achieved = r["flops_per_gemm"] / dom_ms / 1e9
+    skinny = [bench_skinny(16, 16, args.skinny_iters), bench_skinny(8, 16, args.skinny_iters)]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp6_e2m3",
+        "data": "synthetic",
+        "config": {"workload": "DiT MLP forward: quantize x, fc1 20480x3072x12288 (GELU-tanh -> E2M3), "
+                               "fc2 20480x12288x3072 (bf16 out)",
+                   "tokens": 20480, "d_model": 3072, "d_hidden": 12288, "frac_of_mxfp6_peak": round(value / PEAK_MXFP6_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "kernel": f"gemm_kernel ({dom})", "achieved": round(achieved, 1),
+                     "peak": PEAK_MXFP6_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MXFP6_TFLOPS, 4),
+                     "traffic": None},
+        "kernels_ms": {"quantize": round(r["quantize_ms"], 4), "fc1": round(r["fc1_ms"], 4), "fc2": round(r["fc2_ms"], 4),
+                       "fc1_tflops": round(r["flops_per_gemm"] / r["fc1_ms"] / 1e9, 1),
+                       "fc2_tflops": round(r["flops_per_gemm"] / r["fc2_ms"] / 1e9, 1),
+                       "quantize_gb_s": round(r["quantize_bytes"] / r["quantize_ms"] / 1e6, 1)},
+        "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cpu_baseline().items()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

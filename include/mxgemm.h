@@ -1,0 +1,175 @@
+/*
+ * mxgemm.h - C ABI of the MXFP6 block-scaled GEMM library for AMD Instinct
+ * MI355X (gfx950, CDNA4).
+ *
+ * What it computes.  The Hedra post "Optimizing Krea 3 on AMD Instinct MI355X
+ * with AI researchers" moves the diffusion transformer's MLPs to MXFP6
+ * (section "Quality set the precision limit": 6-bit floating-point elements
+ * that share one scale per block) and replaces the library GEMM with a custom
+ * MXFP6 GEMM (section "We built a faster MXFP6 kernel": packed 6-bit storage,
+ * no re-reads by neighbouring workgroups, Figure 1 timings).  Its section
+ * "Fusion cut intermediate memory traffic" has the down projection read the
+ * quantized intermediate directly.  The pages fix no element variant, block
+ * size or rounding; this library follows the OCP Microscaling (MX) v1.0
+ * definition:
+ *
+ *   - a block is 32 consecutive elements of one row along the reduction
+ *     dimension K (for a quantized GEMM output: along N);
+ *   - each block has one E8M0 scale byte u, value 2^(u-127); u = 0xFF is NaN;
+ *   - u = clamp(floor(log2(max |v|)) - emax_elem, -127, 127) + 127, with
+ *     emax_elem = 2 for E2M3 and 4 for E3M2; an all-zero block gets u = 0;
+ *   - each element is v / 2^(u-127) rounded to the nearest FP6 value, ties to
+ *     even, magnitudes above the largest (7.5 for E2M3, 28 for E3M2)
+ *     saturate; the sign bit is the source's sign bit (so -0.0 -> 0b100000);
+ *   - a block containing a NaN or an infinity gets u = 0xFF and codes 0.
+ *
+ * The skinny split-K GEMM follows the split-K technique of the page "Creating
+ * Custom Kernels for the AMD MI300" (section "Skinny GEMM Kernel"): K is cut
+ * into contiguous chunks computed concurrently and their fp32 partial sums are
+ * reduced in a fixed order.
+ *
+ * Storage (all buffers row-major, owned by the caller, in device memory):
+ *   codes   [rows, 3*K/4] bytes.  Element i of a row occupies bits [6i, 6i+6)
+ *           of the row read as a little-endian bit string, so a 32-element
+ *           block is 24 bytes and four codes c0..c3 form the 24-bit word
+ *           c0 | c1<<6 | c2<<12 | c3<<18.  Code bits: sign (bit 5), then the
+ *           exponent field, then the mantissa field.
+ *   scales  [rows, K/32] E8M0 bytes.
+ *   Weights use the PyTorch Linear layout [N, K]; the GEMM computes
+ *   C[M, N] = A[M, K] * W[N, K]^T with exact block-scaled products and fp32
+ *   accumulation.
+ *
+ * Conventions:
+ *   - every call is asynchronous on the given HIP stream; the library never
+ *     allocates, frees or synchronizes device memory, and keeps no mutable
+ *     global state, so calls on different streams may run concurrently as
+ *     long as their buffers do not overlap;
+ *   - argument errors are detected on the host before anything is launched
+ *     and return a negative status; nothing is written in that case;
+ *   - MX_ERR_HIP reports a failed launch (hipGetLastError); a fault inside a
+ *     kernel surfaces at the caller's next synchronization instead;
+ *   - device pointers must be 16-byte aligned unless stated otherwise.
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MX_OK 0
+#define MX_ERR_NULL (-1)        /* a required pointer is NULL                        */
+#define MX_ERR_SHAPE (-2)       /* negative size, K % 32 != 0, ld too small, ...     */
+#define MX_ERR_FORMAT (-3)      /* unknown element format / source / output kind     */
+#define MX_ERR_ALIGN (-4)       /* a pointer or leading dimension breaks alignment   */
+#define MX_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than required           */
+#define MX_ERR_UNSUPPORTED (-6) /* valid request with no kernel variant              */
+#define MX_ERR_HIP (-7)         /* a kernel launch failed                            */
+
+/* Element formats.  The values equal the format codes of the gfx950 scaled
+ * f8f6f4 MFMA instructions. */
+#define MX_FMT_E2M3 2
+#define MX_FMT_E3M2 3
+
+/* Source types for quantization. */
+#define MX_SRC_BF16 0
+#define MX_SRC_F32 1
+
+/* GEMM output kinds. */
+#define MX_OUT_F32 0  /* fp32 C                                              */
+#define MX_OUT_BF16 1 /* bf16 C, round-to-nearest-even                        */
+#define MX_OUT_MX 2   /* MX codes + scales of the epilogue's result, along N  */
+
+/* GEMM epilogues. */
+#define MX_EPI_NONE 0
+#define MX_EPI_GELU_TANH 1 /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+
+/*
+ * mx_quantize - MX-quantize a [rows, k] matrix along its rows.
+ *
+ *   src       device pointer to bf16 (src_type MX_SRC_BF16) or fp32
+ *             (MX_SRC_F32) values, row r starting at src + r * ld_src
+ *             elements; 16-byte aligned, ld_src * element size a multiple of 16.
+ *   rows, k   rows >= 0, k >= 0, k % 32 == 0.  rows == 0 or k == 0 is a
+ *             no-op that returns MX_OK.
+ *   fmt       MX_FMT_E2M3 or MX_FMT_E3M2.
+ *   codes     device output [rows, 3k/4] bytes, 8-byte aligned.
+ *   scales    device output [rows, k/32] bytes.
+ * The result is exactly the rule in the header comment (bit-exact).
+ */
+int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
+                void* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * mx_gemm - C = A * W^T on MX operands, fp32 accumulation, optional epilogue.
+ *
+ * Activations: exactly one of
+ *   a_src  (bf16 or fp32 [m, k] at a_src + r * lda elements, quantized to
+ *          a_fmt inside the call into the workspace before the GEMM), or
+ *   a_codes / a_scales (already quantized, format a_fmt).
+ * Weights: w_codes [n, 3k/4], w_scales [n, k/32], format w_fmt.
+ * Alignment: a_src and code pointers 16 bytes, scale pointers 4 bytes, the
+ *   workspace 256 bytes, f32/bf16 outputs their element size (16 bytes and
+ *   ldo * element size % 16 == 0 enable vector stores), MX outputs 4 bytes.
+ * Formats: E2M3 x E2M3, E2M3 x E3M2 and E3M2 x E2M3; E3M2 activations with
+ *   E3M2 weights return MX_ERR_UNSUPPORTED (the scaled MFMA does not keep
+ *   fp32 accuracy for that pair).
+ * m, n, k: >= 0, k % 32 == 0.  m == 0 or n == 0 is a no-op; k == 0 writes
+ *   C = 0 (epilogue applied).
+ * epilogue: MX_EPI_NONE or MX_EPI_GELU_TANH (applied to the fp32 accumulator).
+ * out_kind:
+ *   MX_OUT_F32 / MX_OUT_BF16: out is [m, ldo] elements (ldo >= n), C is
+ *     written to its first n columns; out_scales, out_fmt are ignored.
+ *   MX_OUT_MX: the epilogue result is MX-quantized along N in blocks of 32
+ *     (n % 32 == 0) into out (codes [m, 3n/4] bytes, 4-byte aligned) and
+ *     out_scales ([m, n/32]) with element format out_fmt; ldo is ignored.
+ *     This output is directly the a_codes / a_scales of a following GEMM.
+ * workspace: device memory of at least mx_gemm_workspace_size(m, n, k, a_src
+ *   != NULL, 0) bytes (may be NULL when that size is 0).
+ */
+int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
+            int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n,
+            int64_t k, int32_t epilogue, int32_t out_kind, void* out, int64_t ldo, uint8_t* out_scales,
+            int32_t out_fmt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mx_gemm_splitk - the same product for skinny m (0 <= m <= 16), split along
+ * K into `splits` contiguous chunks whose fp32 partial sums are added in the
+ * fixed order 0, 1, ..., splits-1 (deterministic) before the output rounding.
+ *
+ * Arguments as mx_gemm, with:
+ *   splits    >= 1; k % splits == 0 and each chunk k/splits a multiple of
+ *             512 (else MX_ERR_UNSUPPORTED); m <= 16 (else MX_ERR_SHAPE).
+ *   epilogue  MX_EPI_NONE only; out_kind MX_OUT_F32 or MX_OUT_BF16.
+ *   workspace at least mx_gemm_workspace_size(m, n, k, a_src != NULL, splits)
+ *             bytes (quantized activations plus fp32 partials).
+ */
+int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+                   const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
+                   int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t splits, int32_t out_kind, void* out,
+                   int64_t ldo, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mx_gemm_workspace_size - bytes of workspace needed by mx_gemm (splits == 0)
+ * or mx_gemm_splitk (splits >= 1) for these sizes; a_is_src != 0 when the
+ * activations are passed unquantized.  Returns 0 for invalid sizes.
+ */
+size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t a_is_src, int32_t splits);
+
+/* mx_status_string - static, human-readable text for a status code. */
+const char* mx_status_string(int status);
+
+/* mx_version - library version as major * 10000 + minor * 100 + patch. */
+int mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

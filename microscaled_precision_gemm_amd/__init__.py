@@ -1,0 +1,19 @@
+"""MXFP6 block-scaled GEMM for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libmxgemm.so`` (hand-written HIP kernels behind a C
+ABI, declared in ``include/mxgemm.h``); this package is its ctypes binding.
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    MXError,
+    MXTensor,
+    lib,
+    mx_gemm,
+    mx_gemm_splitk,
+    mx_gemm_workspace_size,
+    mx_quantize,
+    mx_status_string,
+    mx_version,
+)

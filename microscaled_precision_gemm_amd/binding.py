@@ -1,0 +1,247 @@
+"""ctypes binding of libmxgemm.so, with the same names as the C ABI.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and workspaces are allocated with torch (device memory is
+torch's job here), and every computation runs in the library's HIP kernels on
+torch's current stream.  There is no CPU fallback: without the built library
+every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxgemm.so")
+
+MX_OK = 0
+MX_ERR_NULL = -1
+MX_ERR_SHAPE = -2
+MX_ERR_FORMAT = -3
+MX_ERR_ALIGN = -4
+MX_ERR_WORKSPACE = -5
+MX_ERR_UNSUPPORTED = -6
+MX_ERR_HIP = -7
+
+MX_FMT_E2M3 = 2
+MX_FMT_E3M2 = 3
+MX_SRC_BF16 = 0
+MX_SRC_F32 = 1
+MX_OUT_F32 = 0
+MX_OUT_BF16 = 1
+MX_OUT_MX = 2
+MX_EPI_NONE = 0
+MX_EPI_GELU_TANH = 1
+
+FMT_CODES = {"e2m3": MX_FMT_E2M3, "e3m2": MX_FMT_E3M2}
+OUT_KINDS = {"f32": MX_OUT_F32, "bf16": MX_OUT_BF16, "mx": MX_OUT_MX}
+EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH}
+
+EXPORTED = ("mx_quantize", "mx_gemm", "mx_gemm_splitk", "mx_gemm_workspace_size", "mx_status_string", "mx_version")
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mx_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxgemm.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built: run `python -m microscaled_precision_gemm_amd.build` "
+            "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.mx_quantize.argtypes = [c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_p, c_p, c_p]
+    L.mx_quantize.restype = ctypes.c_int
+    L.mx_gemm.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32,
+                          c_p, c_i64, c_p, c_i32, c_p, c_sz, c_p]
+    L.mx_gemm.restype = ctypes.c_int
+    L.mx_gemm_splitk.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32,
+                                 c_i32, c_p, c_i64, c_p, c_sz, c_p]
+    L.mx_gemm_splitk.restype = ctypes.c_int
+    L.mx_gemm_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i32]
+    L.mx_gemm_workspace_size.restype = c_sz
+    L.mx_status_string.argtypes = [ctypes.c_int]
+    L.mx_status_string.restype = ctypes.c_char_p
+    L.mx_version.argtypes = []
+    L.mx_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def mx_status_string(status: int) -> str:
+    return lib().mx_status_string(int(status)).decode()
+
+
+def mx_version() -> int:
+    return int(lib().mx_version())
+
+
+def mx_gemm_workspace_size(m: int, n: int, k: int, a_is_src: bool, splits: int = 0) -> int:
+    return int(lib().mx_gemm_workspace_size(m, n, k, int(bool(a_is_src)), splits))
+
+
+@dataclass
+class MXTensor:
+    """Packed MX matrix: codes [rows, 3k/4] uint8, scales [rows, k/32] uint8."""
+
+    codes: torch.Tensor
+    scales: torch.Tensor
+    fmt: str
+    k: int
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else None)
+
+
+def _check(status: int, where: str) -> None:
+    if status != MX_OK:
+        raise MXError(status, where)
+
+
+def _fmt(fmt: str) -> int:
+    try:
+        return FMT_CODES[fmt]
+    except KeyError:
+        raise ValueError(f"unknown MX format {fmt!r}") from None
+
+
+def _src_type(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MX_SRC_BF16
+    if t.dtype == torch.float32:
+        return MX_SRC_F32
+    raise TypeError(f"unsupported source dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _require_cuda(*ts: torch.Tensor) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (no CPU fallback)")
+        dev = t.device if dev is None else dev
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _check_mx(x: MXTensor, name: str) -> None:
+    if x.codes.dtype != torch.uint8 or x.scales.dtype != torch.uint8:
+        raise TypeError(f"{name}: codes and scales must be uint8")
+    if not (x.codes.is_contiguous() and x.scales.is_contiguous()):
+        raise ValueError(f"{name}: codes and scales must be contiguous")
+    if x.codes.dim() != 2 or x.codes.shape[1] != 3 * x.k // 4 or tuple(x.scales.shape) != (x.rows, x.k // 32):
+        raise ValueError(f"{name}: codes must be [rows, 3k/4] and scales [rows, k/32]")
+
+
+def mx_quantize(src: torch.Tensor, fmt: str = "e2m3", out: MXTensor | None = None) -> MXTensor:
+    """MX-quantize a 2-D bf16/fp32 GPU tensor along its rows (blocks of 32)."""
+    if src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be 2-D with unit stride along K")
+    dev = _require_cuda(src)
+    rows, k = src.shape
+    if out is None:
+        out = MXTensor(torch.empty((rows, 3 * k // 4), dtype=torch.uint8, device=dev),
+                       torch.empty((rows, k // 32), dtype=torch.uint8, device=dev), fmt, k)
+    _check_mx(out, "out")
+    st = lib().mx_quantize(_ptr(src), _src_type(src), rows, k, src.stride(0), _fmt(fmt), _ptr(out.codes),
+                           _ptr(out.scales), _stream(dev))
+    _check(st, "mx_quantize")
+    return out
+
+
+def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epilogue: str = "none",
+            out_fmt: str = "e2m3", a_fmt: str = "e2m3", out: torch.Tensor | MXTensor | None = None,
+            workspace: torch.Tensor | None = None):
+    """C = A W^T.  ``a`` is a bf16/fp32 tensor (quantized to ``a_fmt`` inside the
+    call) or an MXTensor.  Returns a [m, n] tensor, or an MXTensor for out_kind="mx"."""
+    _check_mx(w, "w")
+    n, k = w.rows, w.k
+    if isinstance(a, MXTensor):
+        _check_mx(a, "a")
+        a_src, a_codes, a_scales, af, lda, m = None, a.codes, a.scales, _fmt(a.fmt), 0, a.rows
+        if a.k != k:
+            raise ValueError("A and W disagree on K")
+        src_type = MX_SRC_BF16
+    else:
+        if a.dim() != 2 or a.stride(1) != 1 or a.shape[1] != k:
+            raise ValueError("a must be [m, k] with unit stride along K")
+        a_src, a_codes, a_scales, af, lda, m = a, None, None, _fmt(a_fmt), a.stride(0), a.shape[0]
+        src_type = _src_type(a)
+    dev = _require_cuda(a_src, a_codes, w.codes)
+    kind = OUT_KINDS[out_kind]
+    if kind == MX_OUT_MX:
+        if out is None:
+            out = MXTensor(torch.empty((m, 3 * n // 4), dtype=torch.uint8, device=dev),
+                           torch.empty((m, n // 32), dtype=torch.uint8, device=dev), out_fmt, n)
+        out_data, out_scales, ldo = out.codes, out.scales, 0
+    else:
+        dtype = torch.float32 if kind == MX_OUT_F32 else torch.bfloat16
+        if out is None:
+            out = torch.empty((m, n), dtype=dtype, device=dev)
+        if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (m, n):
+            raise ValueError("out must be [m, n] of the output dtype with unit stride")
+        out_data, out_scales, ldo = out, None, out.stride(0)
+    need = mx_gemm_workspace_size(m, n, k, a_src is not None, 0)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = lib().mx_gemm(_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af, _ptr(w.codes),
+                       _ptr(w.scales), _fmt(w.fmt), m, n, k, EPILOGUES[epilogue], kind, _ptr(out_data), ldo,
+                       _ptr(out_scales), _fmt(out_fmt), _ptr(workspace), ws_bytes, _stream(dev))
+    _check(st, "mx_gemm")
+    return out
+
+
+def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kind: str = "bf16",
+                   a_fmt: str = "e2m3", out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Skinny C = A W^T (m <= 16) with K split into ``splits`` chunks, fp32
+    partials summed in a fixed order."""
+    _check_mx(w, "w")
+    n, k = w.rows, w.k
+    if isinstance(a, MXTensor):
+        _check_mx(a, "a")
+        a_src, a_codes, a_scales, af, lda, m = None, a.codes, a.scales, _fmt(a.fmt), 0, a.rows
+        src_type = MX_SRC_BF16
+    else:
+        if a.dim() != 2 or a.stride(1) != 1 or a.shape[1] != k:
+            raise ValueError("a must be [m, k] with unit stride along K")
+        a_src, a_codes, a_scales, af, lda, m = a, None, None, _fmt(a_fmt), a.stride(0), a.shape[0]
+        src_type = _src_type(a)
+    dev = _require_cuda(a_src, a_codes, w.codes)
+    kind = OUT_KINDS[out_kind]
+    dtype = torch.float32 if kind == MX_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((m, n), dtype=dtype, device=dev)
+    need = mx_gemm_workspace_size(m, n, k, a_src is not None, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().mx_gemm_splitk(_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af, _ptr(w.codes),
+                              _ptr(w.scales), _fmt(w.fmt), m, n, k, splits, kind, _ptr(out), out.stride(0),
+                              _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "mx_gemm_splitk")
+    return out

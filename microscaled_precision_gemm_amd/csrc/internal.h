@@ -1,0 +1,57 @@
+// Launchers shared between the C ABI front end and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+constexpr int kSrcBf16 = 0;
+constexpr int kSrcF32 = 1;
+
+constexpr int kOutF32 = 0;
+constexpr int kOutBf16 = 1;
+constexpr int kOutMx = 2;
+
+constexpr int kEpiNone = 0;
+constexpr int kEpiGeluTanh = 1;
+
+// Main GEMM tile: 256 tokens x 256 output features, K staged 128 at a time.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kStageK = 128;
+
+struct GemmArgs {
+  const uint8_t* x_codes;   // activations [M, 3K/4]
+  const uint8_t* x_scales;  // [M, K/32]
+  const uint8_t* w_codes;   // weights [N, 3K/4]
+  const uint8_t* w_scales;  // [N, K/32]
+  void* out;                // f32 / bf16 [M, ldo] or MX codes [M, 3N/4]
+  uint8_t* out_scales;      // MX output scales [M, N/32]
+  int64_t ldo;
+  int32_t M, N, K;
+  int32_t tiles_m, tiles_n;
+  int32_t vec_store;        // 1 when 16-byte vector stores of a row segment are aligned
+};
+
+hipError_t launch_quantize(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, int out_kind, int out_fmt,
+                       hipStream_t stream);
+
+struct SplitKArgs {
+  const uint8_t* x_codes;   // activations [M, 3K/4], M <= 16
+  const uint8_t* x_scales;  // [M, K/32]
+  const uint8_t* w_codes;   // weights [N, 3K/4]
+  const uint8_t* w_scales;  // [N, K/32]
+  float* partial;           // [splits, 16, N] fp32 workspace
+  void* out;                // f32 / bf16 [M, ldo]
+  int64_t ldo;
+  int32_t M, N, K, splits;
+  int32_t vec_store;
+};
+
+hipError_t launch_gemm_splitk(const SplitKArgs& a, int x_fmt, int w_fmt, int out_kind, hipStream_t stream);
+
+}  // namespace mxg

@@ -1,0 +1,112 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the MX scale
+// rule on raw float bits, and the hardware FP6 conversions.
+//
+// The MX rule (OCP Microscaling v1.0, the format the Krea 3 / MI355X post uses
+// for its MLPs, section "Quality set the precision limit"): for a block of 32
+// values, shared = clamp(floor(log2 amax) - emax_elem, -127, 127), scale byte =
+// shared + 127, elements = RNE(v / 2^shared) saturated.  floor(log2 amax) is
+// read exactly from the exponent bits (leading-one position for subnormals).
+// The element rounding is done by gfx950's v_cvt_scalef32_* instructions,
+// which divide by the fp32 scale operand and round to nearest even with
+// saturation and a kept sign bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFmtE2M3 = 2;
+constexpr int kFmtE3M2 = 3;
+
+// floor(log2(max magnitude)) of the element format: 7.5 = 1.875 * 2^2, 28 = 1.75 * 2^4.
+template <int FMT>
+__device__ __forceinline__ constexpr int emax_elem() {
+  return FMT == kFmtE2M3 ? 2 : 4;
+}
+
+// Result of the scale rule for one block.
+struct BlockScale {
+  float scale;     // 2^shared as an fp32 operand for the convert (2^-127 is the subnormal 0x00400000)
+  uint32_t byte;   // E8M0 byte; 0xFF marks a non-finite block
+  bool nonfinite;
+};
+
+// shared exponent -> (E8M0 byte, fp32 scale operand), shared already clamped to [-127, 127].
+__device__ __forceinline__ BlockScale make_scale(int shared) {
+  BlockScale s;
+  s.byte = (uint32_t)(shared + 127);
+  s.scale = shared >= -126 ? __uint_as_float((uint32_t)(shared + 127) << 23) : __uint_as_float(0x00400000u);
+  s.nonfinite = false;
+  return s;
+}
+
+// Scale rule from the magnitude bits of an fp32 amax (sign bit clear).
+template <int FMT>
+__device__ __forceinline__ BlockScale scale_from_f32_bits(uint32_t amax_bits) {
+  if (amax_bits >= 0x7f800000u) {
+    BlockScale s;
+    s.byte = 0xFFu;
+    s.scale = 1.0f;
+    s.nonfinite = true;
+    return s;
+  }
+  int fl;
+  const uint32_t e = amax_bits >> 23;
+  if (e != 0) {
+    fl = (int)e - 127;
+  } else {
+    const uint32_t m = amax_bits & 0x7fffffu;
+    fl = m ? (-149 + 31 - __clz((int)m)) : -100000;  // subnormal: m * 2^-149
+  }
+  int shared = fl - emax_elem<FMT>();
+  shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
+  return make_scale(shared);
+}
+
+// Scale rule from the magnitude bits of a bf16 amax (sign bit clear, in the low 16 bits).
+template <int FMT>
+__device__ __forceinline__ BlockScale scale_from_bf16_bits(uint32_t amax_bits) {
+  return scale_from_f32_bits<FMT>(amax_bits << 16);
+}
+
+// 32 bf16 values -> 32 FP6 codes packed as 6 dwords (element i at bits [6i, 6i+6)).
+template <int FMT>
+__device__ __forceinline__ v6u cvt_bf16x32(v32bf x, float scale) {
+  if constexpr (FMT == kFmtE2M3)
+    return __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, scale);
+  else
+    return __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(x, scale);
+}
+
+// Two 16-float vectors -> 32 FP6 codes; output element 2i comes from a[i] and
+// element 2i+1 from b[i] (the instruction interleaves its two sources).
+template <int FMT>
+__device__ __forceinline__ v6u cvt_f32x2x16(v16f a, v16f b, float scale) {
+  if constexpr (FMT == kFmtE2M3)
+    return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, scale);
+  else
+    return __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, scale);
+}
+
+// GELU, tanh form, in fp32: 0.5 x (1 + tanh(u)) = x / (1 + e^{-2u}) with
+// u = sqrt(2/pi) (x + 0.044715 x^3) (Hendrycks & Gimpel).  e^{-2u} is taken as
+// 2^{-2u log2 e} with the hardware exp2 and the quotient with the hardware
+// reciprocal; for very negative x, 2^{...} overflows to +inf and the result is
+// x * 0 = -0.
+__device__ __forceinline__ float gelu_tanh_f32(float x) {
+  constexpr float kNeg2SqrtTwoOverPiLog2e = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  const float p = __builtin_fmaf(0.044715f * x, x, 1.0f);
+  const float t = __builtin_amdgcn_exp2f(kNeg2SqrtTwoOverPiLog2e * x * p);
+  return x * __builtin_amdgcn_rcpf(1.0f + t);
+}
+
+}  // namespace mxg

@@ -1,0 +1,153 @@
+"""Helpers for the GPU parity tests: oracle-side references and comparisons.
+
+The oracle side only ever sees the seeded host inputs; GPU results are only
+compared against it, never fed into it.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import mx_oracle as O
+
+
+def say(msg: str) -> None:
+    """Name the case before a GPU step (and flush), so a hang or fault names it."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def oracle_mx(x64: np.ndarray, fmt: str):
+    """Oracle quantization of float64 source values: (codes, scales, dequantized)."""
+    codes, scales = O.quantize(x64, fmt)
+    return codes, scales, O.dequantize(codes, scales, fmt)
+
+
+def assert_mx_equal(gpu_mx, codes_o: np.ndarray, scales_o: np.ndarray, what: str, rows=None) -> None:
+    """GPU packed codes + scales must equal the oracle's bit for bit."""
+    gc = to_np(gpu_mx.codes)
+    gs = to_np(gpu_mx.scales)
+    if rows is not None:
+        gc, gs = gc[rows], gs[rows]
+    k = codes_o.shape[1]
+    packed_o = O.pack(codes_o)
+    bad_s = np.argwhere(gs != scales_o)
+    assert bad_s.size == 0, f"{what}: {len(bad_s)} scale bytes differ, first {bad_s[:5].tolist()}"
+    if not np.array_equal(gc, packed_o):
+        cg = O.unpack(gc, k)
+        bad = np.argwhere(cg != codes_o)
+        raise AssertionError(f"{what}: {len(bad)} codes differ, first {bad[:5].tolist()} "
+                             f"gpu {[int(cg[tuple(b)]) for b in bad[:5]]} oracle {[int(codes_o[tuple(b)]) for b in bad[:5]]}")
+
+
+def assert_fp32_close(gpu: np.ndarray, c: np.ndarray, s: np.ndarray, what: str) -> None:
+    ok = O.check_fp32(gpu, c, s)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} fp32 outputs outside 1e-5*S; first {i}: "
+                             f"gpu {gpu[i]!r} oracle {c[i]!r} S {s[i]!r}")
+
+
+def assert_bf16_close(gpu: np.ndarray, c: np.ndarray, s: np.ndarray, what: str) -> int:
+    ok, n2 = O.check_bf16(gpu, c, s)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} bf16 outputs outside tolerance; first {i}: "
+                             f"gpu {gpu[i]!r} oracle {c[i]!r} S {s[i]!r}")
+    return n2
+
+
+def bf16_tensor_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+GELU_DERIV_MAX = 1.13  # max |d/dx GELU_tanh(x)| is about 1.129
+
+
+def gelu_eval_slack(c: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Bound on the fp32 device GELU's own error at exact input c: a few ulps of
+    g plus the exp2 argument's rounding amplified by |argument| (relative error
+    of 2^a is |a| ln2 times that of a)."""
+    arg = 2.0 * np.sqrt(2.0 / np.pi) * np.log2(np.e) * np.abs(c) * (1.0 + 0.044715 * c * c)
+    return (8.0 + 1.2 * arg) * O.ulp_fp32(g) + 1e-44
+
+
+def check_mx_epilogue(gpu_codes: np.ndarray, gpu_scales: np.ndarray, c: np.ndarray, s: np.ndarray, gelu: bool,
+                      fmt: str = "e2m3") -> dict:
+    """Compare a fused-epilogue MX output (GELU or identity, then MX along N)
+    with the oracle.
+
+    The oracle quantizes fp32(epilogue(C_exact)); the device quantizes its own
+    fp32 result, which differs from that by the accumulation error (<= 1e-5 S,
+    times |GELU'| <= 1.13) plus the GELU evaluation error.  Where the oracle's
+    value is within that distance delta of a rounding midpoint, one element
+    step either way is a correct result; where the block's amax is within delta
+    of a power of two, the scale byte may differ by one.  Everything else must
+    match exactly.  Returns counts of exact and tolerated differences.
+    """
+    n = c.shape[1]
+    g64 = O.gelu_tanh(c) if gelu else c
+    g32 = g64.astype(np.float32).astype(np.float64)
+    codes_o, scales_o = O.quantize(g32, fmt)
+    codes_g = O.unpack(gpu_codes, n)
+    deq_o = O.dequantize(codes_o, scales_o, fmt)
+    deq_g = O.dequantize(codes_g, gpu_scales, fmt)
+    delta = O.GEMM_RTOL * s * (GELU_DERIV_MAX if gelu else 1.0) + (gelu_eval_slack(c, g32) if gelu else 0.0)
+    delta = delta + O.ulp_fp32(g32)  # the oracle's own fp32 rounding of g
+    rows, nb = scales_o.shape
+    su_o = scales_o.astype(np.int64)
+    su_g = gpu_scales.astype(np.int64)
+    emax = O.emax_elem(fmt)
+    mags = O.magnitudes(fmt)
+
+    stats = {"elements": codes_o.size, "code_steps": 0, "scale_steps": 0, "exact": 0}
+    # --- scales
+    diff_s = su_g != su_o
+    if diff_s.any():
+        amax = np.abs(g32).reshape(rows, nb, 32).max(axis=2)
+        dblk = delta.reshape(rows, nb, 32).max(axis=2)
+        thr = np.ldexp(1.0, np.maximum(su_o, su_g) - 127 + emax)  # power of two between the two choices
+        ok = (np.abs(su_g - su_o) == 1) & (np.abs(amax - thr) <= dblk)
+        bad = np.argwhere(diff_s & ~ok)
+        assert bad.size == 0, f"{len(bad)} scale bytes differ beyond the boundary rule, first {bad[:4].tolist()}"
+        stats["scale_steps"] = int(diff_s.sum())
+    same_scale = np.repeat(~diff_s, 32, axis=1)
+    # --- elements under equal scales: equal values, or one step across a midpoint within delta
+    dv = np.abs(deq_g - deq_o)
+    exact = dv == 0
+    unit = np.ldexp(1.0, np.repeat(su_o, 32, axis=1) - 127)
+    rg = np.abs(deq_g) / unit
+    ro = np.abs(deq_o) / unit
+    idx_g = np.searchsorted(mags, rg)
+    idx_o = np.searchsorted(mags, ro)
+    same_sign_or_zero = (np.sign(deq_g) == np.sign(deq_o)) | (deq_g == 0) | (deq_o == 0)
+    adjacent = (np.abs(idx_g - idx_o) == 1) & same_sign_or_zero
+    mid = 0.5 * (deq_g + deq_o)
+    near_mid = np.abs(g32 - mid) <= delta
+    ok_elem = exact | (adjacent & near_mid)
+    bad = np.argwhere(same_scale & ~ok_elem)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError(f"{len(bad)} MX codes differ beyond one step at a midpoint; first {i}: "
+                             f"gpu {deq_g[i]!r} oracle {deq_o[i]!r} g {g32[i]!r} delta {delta[i]!r}")
+    stats["code_steps"] = int((same_scale & ~exact).sum())
+    # --- elements of blocks whose scale legitimately differs: a valid rounding of a value within delta of g
+    if diff_s.any():
+        unit_g = np.ldexp(1.0, np.repeat(su_g, 32, axis=1) - 127)
+        r = np.abs(g32) / unit_g
+        spacing = np.ldexp(1.0, np.maximum(O.floor_log2(np.where(r > 0, r, 1.0)), 1 - {"e2m3": 1, "e3m2": 3}[fmt])
+                           - {"e2m3": 3, "e3m2": 2}[fmt]) * unit_g
+        ok_other = np.abs(deq_g - g32) <= 0.5 * spacing + delta + np.maximum(np.abs(g32) - mags[-1] * unit_g, 0)
+        bad = np.argwhere(~same_scale & ~ok_other)
+        assert bad.size == 0, f"{len(bad)} codes in scale-flipped blocks are not valid roundings"
+    stats["exact"] = int((exact & same_scale).sum())
+    return stats

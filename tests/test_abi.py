@@ -1,0 +1,158 @@
+"""The C ABI library on a host without a GPU: it loads, exports every symbol
+that include/mxgemm.h declares, and rejects invalid arguments on the host
+before any HIP call (status codes, nothing launched)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import microscaled_precision_gemm_amd as mx
+from microscaled_precision_gemm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxgemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libmxgemm.so not built")
+    return mx.lib()
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(mx.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mx_[a-z_0-9]+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_version_and_status_strings(L):
+    assert mx.mx_version() == 100
+    for st in range(-7, 1):
+        assert mx.mx_status_string(st) and mx.mx_status_string(st) != "unknown status"
+    assert mx.mx_status_string(-99) == "unknown status"
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+NULL = None
+
+try:
+    import torch as _torch
+
+    _HAS_GPU = _torch.cuda.is_available()
+except Exception:  # pragma: no cover
+    _HAS_GPU = False
+
+# The calls below pass made-up device addresses that host validation must
+# reject.  They are host-logic tests: run them where no GPU is visible, so a
+# validation regression can never turn into a launch on bogus pointers.
+host_only = pytest.mark.skipif(_HAS_GPU, reason="fake-pointer validation tests run on GPU-less hosts only")
+
+
+def q(*a):
+    return mx.lib().mx_quantize(*a)
+
+
+@host_only
+def test_quantize_validation(L):
+    s = NULL
+    assert q(FAKE, 5, 4, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_FORMAT
+    assert q(FAKE, 0, 4, 64, 64, 7, FAKE, FAKE, s) == B.MX_ERR_FORMAT
+    assert q(FAKE, 0, -1, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert q(FAKE, 0, 4, 48, 48, 2, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert q(FAKE, 0, 4, 64, 32, 2, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert q(NULL, 0, 4, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_NULL
+    assert q(FAKE, 0, 4, 64, 64, 2, NULL, FAKE, s) == B.MX_ERR_NULL
+    assert q(FAKE + 2, 0, 4, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_ALIGN
+    assert q(FAKE, 0, 4, 64, 68, 2, FAKE, FAKE, s) == B.MX_ERR_ALIGN
+    assert q(FAKE, 0, 4, 64, 64, 2, FAKE + 4, FAKE, s) == B.MX_ERR_ALIGN
+    assert q(NULL, 0, 0, 64, 64, 2, NULL, NULL, s) == B.MX_OK  # empty is a no-op
+    assert q(NULL, 0, 4, 0, 0, 2, NULL, NULL, s) == B.MX_OK
+
+
+def g(**kw):
+    a = dict(a_src=NULL, a_src_type=0, lda=0, a_codes=FAKE, a_scales=FAKE, a_fmt=2, w_codes=FAKE, w_scales=FAKE,
+             w_fmt=2, m=64, n=64, k=128, epi=0, out_kind=1, out=FAKE, ldo=64, out_scales=NULL, out_fmt=2,
+             ws=NULL, ws_bytes=0, stream=NULL)
+    a.update(kw)
+    return mx.lib().mx_gemm(*a.values())
+
+
+@host_only
+def test_gemm_validation(L):
+    assert g(k=100) == B.MX_ERR_SHAPE
+    assert g(m=-1) == B.MX_ERR_SHAPE
+    assert g(a_fmt=4) == B.MX_ERR_FORMAT
+    assert g(a_src=FAKE) == B.MX_ERR_NULL  # both activation forms
+    assert g(a_codes=NULL) == B.MX_ERR_NULL  # neither
+    assert g(a_scales=NULL) == B.MX_ERR_NULL
+    assert g(w_scales=NULL) == B.MX_ERR_NULL
+    assert g(a_codes=FAKE + 8) == B.MX_ERR_ALIGN
+    assert g(w_scales=FAKE + 1) == B.MX_ERR_ALIGN
+    assert g(a_fmt=3, w_fmt=3) == B.MX_ERR_UNSUPPORTED
+    assert g(epi=5) == B.MX_ERR_FORMAT
+    assert g(out_kind=9) == B.MX_ERR_FORMAT
+    assert g(out=NULL) == B.MX_ERR_NULL
+    assert g(ldo=32) == B.MX_ERR_SHAPE
+    assert g(out_kind=2, out_scales=FAKE, n=48) == B.MX_ERR_UNSUPPORTED
+    assert g(out_kind=2, out_scales=NULL) == B.MX_ERR_NULL
+    assert g(out_kind=2, out_scales=FAKE, out_fmt=1) == B.MX_ERR_FORMAT
+    # bf16 activations need a workspace for the quantized copy
+    assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=128) == B.MX_ERR_WORKSPACE
+    need = mx.mx_gemm_workspace_size(64, 64, 128, True, 0)
+    assert need >= 64 * 96 + 64 * 4
+    assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=128, ws=FAKE, ws_bytes=need - 1) == B.MX_ERR_WORKSPACE
+    assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=120, ws=FAKE, ws_bytes=need) == B.MX_ERR_SHAPE
+    assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=130, ws=FAKE, ws_bytes=need) == B.MX_ERR_ALIGN
+    assert g(m=0) == B.MX_OK and g(n=0) == B.MX_OK  # empty is a no-op
+
+
+def sk(**kw):
+    a = dict(a_src=NULL, a_src_type=0, lda=0, a_codes=FAKE, a_scales=FAKE, a_fmt=2, w_codes=FAKE, w_scales=FAKE,
+             w_fmt=3, m=16, n=64, k=4096, splits=8, out_kind=1, out=FAKE, ldo=64, ws=FAKE, ws_bytes=1 << 30,
+             stream=NULL)
+    a.update(kw)
+    return mx.lib().mx_gemm_splitk(*a.values())
+
+
+@host_only
+def test_splitk_validation(L):
+    assert sk(m=17) == B.MX_ERR_SHAPE
+    assert sk(splits=0) == B.MX_ERR_SHAPE
+    assert sk(splits=3) == B.MX_ERR_UNSUPPORTED
+    assert sk(splits=16) == B.MX_ERR_UNSUPPORTED  # 256-element chunks
+    assert sk(out_kind=2) == B.MX_ERR_FORMAT
+    assert sk(ws_bytes=10) == B.MX_ERR_WORKSPACE
+    assert sk(ws=NULL) == B.MX_ERR_WORKSPACE
+    assert sk(ws=FAKE + 16) == B.MX_ERR_ALIGN
+    assert sk(a_fmt=3) == B.MX_ERR_UNSUPPORTED
+    assert sk(m=0) == B.MX_OK
+
+
+def test_workspace_sizes(L):
+    assert mx.mx_gemm_workspace_size(64, 64, 128, False, 0) == 0
+    assert mx.mx_gemm_workspace_size(64, 64, 100, True, 0) == 0  # invalid K
+    assert mx.mx_gemm_workspace_size(17, 64, 128, True, 4) == 0  # splitk needs m <= 16
+    sz = mx.mx_gemm_workspace_size(16, 13312, 16384, True, 16)
+    assert sz >= 16 * 13312 * 4 * 16 + 16 * 12288 + 16 * 512
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    with pytest.raises(ValueError):
+        mx.mx_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
