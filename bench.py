@@ -47,17 +47,15 @@ def bench_mlp(steps: int, warmup: int):
     x = syn.make_a(fc1).to(dev)
     w1 = mx.mx_quantize(syn.make_w(fc1).to(dev), "e2m3")
     w2 = mx.mx_quantize(syn.make_w(fc2).to(dev), "e2m3")
-    xq = mx.MXTensor(torch.empty((m, 3 * d // 4), dtype=torch.uint8, device=dev),
-                     torch.empty((m, d // 32), dtype=torch.uint8, device=dev), "e2m3", d)
-    h = mx.MXTensor(torch.empty((m, 3 * hdim // 4), dtype=torch.uint8, device=dev),
-                    torch.empty((m, hdim // 32), dtype=torch.uint8, device=dev), "e2m3", hdim)
+    xq = mx.MXTensor.empty(m, d, "e2m3", "tiled", dev)
+    h = mx.MXTensor.empty(m, hdim, "e2m3", "tiled", dev)
     y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        mx.mx_quantize(x, "e2m3", out=xq)
+        mx.mx_quantize(x, "e2m3", "tiled", out=xq)
         if ev is not None:
             ev[1].record()
         mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh", out=h)
@@ -101,7 +99,7 @@ def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
     dev = torch.device("cuda:0")
     a = syn.make_a(w, m=m).to(dev)
     wb = syn.make_w(w).to(dev)
-    ws = [mx.mx_quantize(wb, w.w_fmt) for _ in range(copies)]
+    ws = [mx.mx_quantize(wb, w.w_fmt, "rows") for _ in range(copies)]
     del wb
     out = torch.empty((m, w.n), dtype=torch.bfloat16, device=dev)
     work = torch.empty(mx.mx_gemm_workspace_size(m, w.n, w.k, True, splits), dtype=torch.uint8, device=dev)

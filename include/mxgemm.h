@@ -28,16 +28,32 @@
  * into contiguous chunks computed concurrently and their fp32 partial sums are
  * reduced in a fixed order.
  *
- * Storage (all buffers row-major, owned by the caller, in device memory):
- *   codes   [rows, 3*K/4] bytes.  Element i of a row occupies bits [6i, 6i+6)
- *           of the row read as a little-endian bit string, so a 32-element
- *           block is 24 bytes and four codes c0..c3 form the 24-bit word
- *           c0 | c1<<6 | c2<<12 | c3<<18.  Code bits: sign (bit 5), then the
- *           exponent field, then the mantissa field.
- *   scales  [rows, K/32] E8M0 bytes.
- *   Weights use the PyTorch Linear layout [N, K]; the GEMM computes
- *   C[M, N] = A[M, K] * W[N, K]^T with exact block-scaled products and fp32
- *   accumulation.
+ * Packing.  Element i of a row occupies bits [6i, 6i+6) of the row read as a
+ * little-endian bit string, so a 32-element block is 24 bytes and four codes
+ * c0..c3 form the 24-bit word c0 | c1<<6 | c2<<12 | c3<<18.  Code bits: sign
+ * (bit 5), then the exponent field, then the mantissa field.  Weights use the
+ * PyTorch Linear layout [N, K]; the GEMM computes C[M, N] = A[M, K] * W[N, K]^T
+ * with exact block-scaled products and fp32 accumulation.  All buffers are
+ * owned by the caller and live in device memory.  Two storage layouts:
+ *
+ * MX_LAYOUT_ROWS (interchange; the split-K GEMM's operands):
+ *   codes   [rows, 3K/4] bytes, row-major (row r is the packed row above);
+ *   scales  [rows, K/32] bytes, row-major.
+ *
+ * MX_LAYOUT_TILED (the mx_gemm operand and MX-output layout): the matrix is
+ * cut into stages of 128 K-elements (S = ceil(K/128)) and groups of 32 rows
+ * (G = ceil(rows/32)).  Each (stage s, group g) pair owns
+ *   codes   3072 bytes at offset (s*G + g) * 3072: 6 pieces of 512 bytes;
+ *           piece p holds, for rows j = 0..31 of the group in turn, bytes
+ *           [16p, 16p+16) of that row's 96-byte packed slice of K-elements
+ *           [128s, 128s+128) (byte 16p+b of row 32g+j is at offset
+ *           (s*G + g)*3072 + p*512 + j*16 + b);
+ *   scales  128 bytes at offset (s*G + g) * 128: byte j*4 + q is the scale of
+ *           block 4s+q of row 32g+j.
+ *   Rows >= rows and blocks >= K/32 are padding: codes 0, scale byte 127.
+ *   Total: codes S*G*3072 bytes, scales S*G*128 bytes (mx_packed_bytes).
+ *   Each stage of 256 rows is one contiguous 24 KB run, which the GEMM copies
+ *   straight into its LDS ring.
  *
  * Conventions:
  *   - every call is asynchronous on the given HIP stream; the library never
@@ -77,6 +93,10 @@ extern "C" {
 #define MX_FMT_E2M3 2
 #define MX_FMT_E3M2 3
 
+/* Storage layouts of packed MX matrices. */
+#define MX_LAYOUT_ROWS 0
+#define MX_LAYOUT_TILED 1
+
 /* Source types for quantization. */
 #define MX_SRC_BF16 0
 #define MX_SRC_F32 1
@@ -99,12 +119,22 @@ extern "C" {
  *   rows, k   rows >= 0, k >= 0, k % 32 == 0.  rows == 0 or k == 0 is a
  *             no-op that returns MX_OK.
  *   fmt       MX_FMT_E2M3 or MX_FMT_E3M2.
- *   codes     device output [rows, 3k/4] bytes, 8-byte aligned.
- *   scales    device output [rows, k/32] bytes.
+ *   layout    MX_LAYOUT_ROWS or MX_LAYOUT_TILED (padding included).
+ *   codes     device output of mx_packed_bytes(rows, k, layout, 0) bytes,
+ *             16-byte aligned.
+ *   scales    device output of mx_packed_bytes(rows, k, layout, 1) bytes,
+ *             4-byte aligned.
  * The result is exactly the rule in the header comment (bit-exact).
  */
 int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
-                void* codes, uint8_t* scales, hipStream_t stream);
+                int32_t layout, void* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * mx_packed_bytes - size in bytes of the codes (which == 0) or scales
+ * (which == 1) buffer of a [rows, k] MX matrix in the given layout; 0 for
+ * invalid arguments.
+ */
+size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which);
 
 /*
  * mx_gemm - C = A * W^T on MX operands, fp32 accumulation, optional epilogue.
@@ -112,8 +142,9 @@ int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int6
  * Activations: exactly one of
  *   a_src  (bf16 or fp32 [m, k] at a_src + r * lda elements, quantized to
  *          a_fmt inside the call into the workspace before the GEMM), or
- *   a_codes / a_scales (already quantized, format a_fmt).
- * Weights: w_codes [n, 3k/4], w_scales [n, k/32], format w_fmt.
+ *   a_codes / a_scales (already quantized, format a_fmt, MX_LAYOUT_TILED).
+ * Weights: w_codes / w_scales of the [n, k] weights in MX_LAYOUT_TILED,
+ *   format w_fmt.
  * Alignment: a_src and code pointers 16 bytes, scale pointers 4 bytes, the
  *   workspace 256 bytes, f32/bf16 outputs their element size (16 bytes and
  *   ldo * element size % 16 == 0 enable vector stores), MX outputs 4 bytes.
@@ -127,9 +158,10 @@ int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int6
  *   MX_OUT_F32 / MX_OUT_BF16: out is [m, ldo] elements (ldo >= n), C is
  *     written to its first n columns; out_scales, out_fmt are ignored.
  *   MX_OUT_MX: the epilogue result is MX-quantized along N in blocks of 32
- *     (n % 32 == 0) into out (codes [m, 3n/4] bytes, 4-byte aligned) and
- *     out_scales ([m, n/32]) with element format out_fmt; ldo is ignored.
- *     This output is directly the a_codes / a_scales of a following GEMM.
+ *     (n % 32 == 0) into out / out_scales as an [m, n] matrix in
+ *     MX_LAYOUT_TILED (padding written too), element format out_fmt; ldo is
+ *     ignored.  This output is directly the a_codes / a_scales of a
+ *     following GEMM (the down projection reads the quantized intermediate).
  * workspace: device memory of at least mx_gemm_workspace_size(m, n, k, a_src
  *   != NULL, 0) bytes (may be NULL when that size is 0).
  */
@@ -143,7 +175,8 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
  * K into `splits` contiguous chunks whose fp32 partial sums are added in the
  * fixed order 0, 1, ..., splits-1 (deterministic) before the output rounding.
  *
- * Arguments as mx_gemm, with:
+ * Arguments as mx_gemm, except that a_codes / a_scales and w_codes /
+ * w_scales are in MX_LAYOUT_ROWS, and with:
  *   splits    >= 1; k % splits == 0 and each chunk k/splits a multiple of
  *             512 (else MX_ERR_UNSUPPORTED); m <= 16 (else MX_ERR_SHAPE).
  *   epilogue  MX_EPI_NONE only; out_kind MX_OUT_F32 or MX_OUT_BF16.

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     mx_gemm,
     mx_gemm_splitk,
     mx_gemm_workspace_size,
+    mx_packed_bytes,
     mx_quantize,
     mx_status_string,
     mx_version,

@@ -36,12 +36,16 @@ MX_OUT_BF16 = 1
 MX_OUT_MX = 2
 MX_EPI_NONE = 0
 MX_EPI_GELU_TANH = 1
+MX_LAYOUT_ROWS = 0
+MX_LAYOUT_TILED = 1
 
 FMT_CODES = {"e2m3": MX_FMT_E2M3, "e3m2": MX_FMT_E3M2}
 OUT_KINDS = {"f32": MX_OUT_F32, "bf16": MX_OUT_BF16, "mx": MX_OUT_MX}
 EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH}
+LAYOUTS = {"rows": MX_LAYOUT_ROWS, "tiled": MX_LAYOUT_TILED}
 
-EXPORTED = ("mx_quantize", "mx_gemm", "mx_gemm_splitk", "mx_gemm_workspace_size", "mx_status_string", "mx_version")
+EXPORTED = ("mx_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_splitk", "mx_gemm_workspace_size",
+            "mx_status_string", "mx_version")
 
 
 class MXError(RuntimeError):
@@ -64,8 +68,10 @@ def lib() -> ctypes.CDLL:
             "(or __graft_entry__.build()) first")
     L = ctypes.CDLL(LIB_PATH)
     c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
-    L.mx_quantize.argtypes = [c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_p, c_p, c_p]
+    L.mx_quantize.argtypes = [c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_p, c_p, c_p]
     L.mx_quantize.restype = ctypes.c_int
+    L.mx_packed_bytes.argtypes = [c_i64, c_i64, c_i32, c_i32]
+    L.mx_packed_bytes.restype = c_sz
     L.mx_gemm.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32,
                           c_p, c_i64, c_p, c_i32, c_p, c_sz, c_p]
     L.mx_gemm.restype = ctypes.c_int
@@ -94,18 +100,36 @@ def mx_gemm_workspace_size(m: int, n: int, k: int, a_is_src: bool, splits: int =
     return int(lib().mx_gemm_workspace_size(m, n, k, int(bool(a_is_src)), splits))
 
 
+def mx_packed_bytes(rows: int, k: int, layout: str = "tiled", which: int = 0) -> int:
+    """Bytes of the codes (which=0) or scales (which=1) buffer of a [rows, k] MX matrix."""
+    return int(lib().mx_packed_bytes(rows, k, LAYOUTS[layout], which))
+
+
 @dataclass
 class MXTensor:
-    """Packed MX matrix: codes [rows, 3k/4] uint8, scales [rows, k/32] uint8."""
+    """Packed MX matrix of logical shape [rows, k].
+
+    layout "rows": codes [rows, 3k/4] and scales [rows, k/32] uint8 tensors.
+    layout "tiled": codes and scales are flat uint8 tensors in the tiled GEMM
+    layout (128-element stages x 32-row groups, see include/mxgemm.h).
+    """
 
     codes: torch.Tensor
     scales: torch.Tensor
     fmt: str
+    rows: int
     k: int
+    layout: str = "tiled"
 
-    @property
-    def rows(self) -> int:
-        return self.codes.shape[0]
+    @staticmethod
+    def empty(rows: int, k: int, fmt: str = "e2m3", layout: str = "tiled", device=None) -> "MXTensor":
+        if layout == "rows":
+            codes = torch.empty((rows, 3 * k // 4), dtype=torch.uint8, device=device)
+            scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=device)
+        else:
+            codes = torch.empty(mx_packed_bytes(rows, k, layout, 0), dtype=torch.uint8, device=device)
+            scales = torch.empty(mx_packed_bytes(rows, k, layout, 1), dtype=torch.uint8, device=device)
+        return MXTensor(codes, scales, fmt, rows, k, layout)
 
 
 def _stream(device: torch.device) -> ctypes.c_void_p:
@@ -149,27 +173,35 @@ def _require_cuda(*ts: torch.Tensor) -> torch.device:
     return dev
 
 
-def _check_mx(x: MXTensor, name: str) -> None:
+def _check_mx(x: MXTensor, name: str, layout: str | None = None) -> None:
+    if layout is not None and x.layout != layout:
+        raise ValueError(f"{name}: expected the {layout!r} layout, got {x.layout!r}")
     if x.codes.dtype != torch.uint8 or x.scales.dtype != torch.uint8:
         raise TypeError(f"{name}: codes and scales must be uint8")
     if not (x.codes.is_contiguous() and x.scales.is_contiguous()):
         raise ValueError(f"{name}: codes and scales must be contiguous")
-    if x.codes.dim() != 2 or x.codes.shape[1] != 3 * x.k // 4 or tuple(x.scales.shape) != (x.rows, x.k // 32):
-        raise ValueError(f"{name}: codes must be [rows, 3k/4] and scales [rows, k/32]")
+    if x.layout == "rows":
+        ok = tuple(x.codes.shape) == (x.rows, 3 * x.k // 4) and tuple(x.scales.shape) == (x.rows, x.k // 32)
+    else:
+        ok = (x.codes.numel() == mx_packed_bytes(x.rows, x.k, x.layout, 0)
+              and x.scales.numel() == mx_packed_bytes(x.rows, x.k, x.layout, 1))
+    if not ok:
+        raise ValueError(f"{name}: buffer sizes do not match a [{x.rows}, {x.k}] {x.layout} MX matrix")
 
 
-def mx_quantize(src: torch.Tensor, fmt: str = "e2m3", out: MXTensor | None = None) -> MXTensor:
+def mx_quantize(src: torch.Tensor, fmt: str = "e2m3", layout: str = "tiled", out: MXTensor | None = None) -> MXTensor:
     """MX-quantize a 2-D bf16/fp32 GPU tensor along its rows (blocks of 32)."""
     if src.dim() != 2 or src.stride(1) != 1:
         raise ValueError("src must be 2-D with unit stride along K")
     dev = _require_cuda(src)
     rows, k = src.shape
     if out is None:
-        out = MXTensor(torch.empty((rows, 3 * k // 4), dtype=torch.uint8, device=dev),
-                       torch.empty((rows, k // 32), dtype=torch.uint8, device=dev), fmt, k)
+        out = MXTensor.empty(rows, k, fmt, layout, dev)
+    if out.rows != rows or out.k != k or out.layout != layout:
+        raise ValueError("out does not match the source shape / layout")
     _check_mx(out, "out")
-    st = lib().mx_quantize(_ptr(src), _src_type(src), rows, k, src.stride(0), _fmt(fmt), _ptr(out.codes),
-                           _ptr(out.scales), _stream(dev))
+    st = lib().mx_quantize(_ptr(src), _src_type(src), rows, k, src.stride(0), _fmt(fmt), LAYOUTS[layout],
+                           _ptr(out.codes), _ptr(out.scales), _stream(dev))
     _check(st, "mx_quantize")
     return out
 
@@ -179,10 +211,10 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
             workspace: torch.Tensor | None = None):
     """C = A W^T.  ``a`` is a bf16/fp32 tensor (quantized to ``a_fmt`` inside the
     call) or an MXTensor.  Returns a [m, n] tensor, or an MXTensor for out_kind="mx"."""
-    _check_mx(w, "w")
+    _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
     if isinstance(a, MXTensor):
-        _check_mx(a, "a")
+        _check_mx(a, "a", "tiled")
         a_src, a_codes, a_scales, af, lda, m = None, a.codes, a.scales, _fmt(a.fmt), 0, a.rows
         if a.k != k:
             raise ValueError("A and W disagree on K")
@@ -196,8 +228,10 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
     kind = OUT_KINDS[out_kind]
     if kind == MX_OUT_MX:
         if out is None:
-            out = MXTensor(torch.empty((m, 3 * n // 4), dtype=torch.uint8, device=dev),
-                           torch.empty((m, n // 32), dtype=torch.uint8, device=dev), out_fmt, n)
+            out = MXTensor.empty(m, n, out_fmt, "tiled", dev)
+        _check_mx(out, "out", "tiled")
+        if out.rows != m or out.k != n:
+            raise ValueError("out must be an [m, n] MX matrix")
         out_data, out_scales, ldo = out.codes, out.scales, 0
     else:
         dtype = torch.float32 if kind == MX_OUT_F32 else torch.bfloat16
@@ -221,10 +255,10 @@ def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kin
                    a_fmt: str = "e2m3", out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Skinny C = A W^T (m <= 16) with K split into ``splits`` chunks, fp32
     partials summed in a fixed order."""
-    _check_mx(w, "w")
+    _check_mx(w, "w", "rows")
     n, k = w.rows, w.k
     if isinstance(a, MXTensor):
-        _check_mx(a, "a")
+        _check_mx(a, "a", "rows")
         a_src, a_codes, a_scales, af, lda, m = None, a.codes, a.scales, _fmt(a.fmt), 0, a.rows
         src_type = MX_SRC_BF16
     else:

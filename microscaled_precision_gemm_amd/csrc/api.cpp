@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "mx_device.h"
 
 namespace {
 
@@ -34,18 +35,33 @@ QuantWs quant_ws(int64_t rows, int64_t k) {
   return w;
 }
 
+bool valid_layout(int32_t l) { return l == MX_LAYOUT_ROWS || l == MX_LAYOUT_TILED; }
+
 int check_quantize_args(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
-                        const void* codes, const void* scales) {
+                        int32_t layout, const void* codes, const void* scales) {
   if (src_type != MX_SRC_BF16 && src_type != MX_SRC_F32) return MX_ERR_FORMAT;
-  if (!valid_fmt(fmt)) return MX_ERR_FORMAT;
+  if (!valid_fmt(fmt) || !valid_layout(layout)) return MX_ERR_FORMAT;
   if (rows < 0 || k < 0 || k % 32 != 0 || rows > kMaxDim || k > kMaxDim) return MX_ERR_SHAPE;
   if (rows == 0 || k == 0) return MX_OK;
   if (!src || !codes || !scales) return MX_ERR_NULL;
   if (ld_src < k) return MX_ERR_SHAPE;
   const int64_t esize = src_type == MX_SRC_BF16 ? 2 : 4;
   if (!aligned(src, 16) || (ld_src * esize) % 16 != 0) return MX_ERR_ALIGN;
-  if (!aligned(codes, 8)) return MX_ERR_ALIGN;
+  if (!aligned(codes, 16) || !aligned(scales, 4)) return MX_ERR_ALIGN;
   return MX_OK;
+}
+
+// Workspace for activations quantized inside mx_gemm: tiled codes then scales.
+struct TiledWs {
+  size_t codes_off, scales_off, end;
+};
+
+TiledWs tiled_ws(int64_t rows, int64_t k) {
+  TiledWs w;
+  w.codes_off = 0;
+  w.scales_off = round_up((size_t)tiled_codes_bytes(rows, k), kWsAlign);
+  w.end = w.scales_off + round_up((size_t)tiled_scales_bytes(rows, k), kWsAlign);
+  return w;
 }
 
 // Common checks of the GEMM operands; fills the quantized-activation pointers.
@@ -79,6 +95,16 @@ int check_gemm_common(const void* a_src, int32_t a_src_type, int64_t lda, const 
 
 }  // namespace
 
+namespace mxg {
+hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, int out_kind, int out_fmt,
+                       hipStream_t stream) {
+  if (w_fmt == kFmtE2M3 && x_fmt == kFmtE2M3) return launch_gemm_formats<kFmtE2M3, kFmtE2M3>(a, epilogue, out_kind, out_fmt, stream);
+  if (w_fmt == kFmtE3M2 && x_fmt == kFmtE2M3) return launch_gemm_formats<kFmtE3M2, kFmtE2M3>(a, epilogue, out_kind, out_fmt, stream);
+  if (w_fmt == kFmtE2M3 && x_fmt == kFmtE3M2) return launch_gemm_formats<kFmtE2M3, kFmtE3M2>(a, epilogue, out_kind, out_fmt, stream);
+  return hipErrorInvalidValue;  // E3M2 x E3M2 is rejected before this point
+}
+}  // namespace mxg
+
 extern "C" {
 
 int mx_version(void) { return 100; }
@@ -97,18 +123,30 @@ const char* mx_status_string(int status) {
   }
 }
 
+size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which) {
+  if (rows < 0 || k < 0 || k % 32 != 0 || rows > kMaxDim || k > kMaxDim || !valid_layout(layout)) return 0;
+  if (which != 0 && which != 1) return 0;
+  if (layout == MX_LAYOUT_ROWS) return (size_t)(which == 0 ? rows * (k / 32) * 24 : rows * (k / 32));
+  return (size_t)(which == 0 ? tiled_codes_bytes(rows, k) : tiled_scales_bytes(rows, k));
+}
+
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t a_is_src, int32_t splits) {
   if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || splits < 0) return 0;
-  if (splits == 0) return a_is_src ? quant_ws(m, k).end : 0;
+  if (splits == 0) return a_is_src ? tiled_ws(m, k).end : 0;
   if (m > 16) return 0;
   const size_t q = a_is_src ? quant_ws(m, k).end : 0;
   return q + round_up((size_t)splits * 16 * (size_t)n * 4, kWsAlign);
 }
 
-int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt, void* codes,
-                uint8_t* scales, hipStream_t stream) {
-  const int st = check_quantize_args(src, src_type, rows, k, ld_src, fmt, codes, scales);
+int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
+                int32_t layout, void* codes, uint8_t* scales, hipStream_t stream) {
+  const int st = check_quantize_args(src, src_type, rows, k, ld_src, fmt, layout, codes, scales);
   if (st != MX_OK || rows == 0 || k == 0) return st;
+  if (layout == MX_LAYOUT_TILED) {
+    if (tiled_codes_bytes(rows, k) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
+    return hip_status(
+        launch_quantize_tiled(src, src_type, rows, k, ld_src, fmt, static_cast<uint8_t*>(codes), scales, stream));
+  }
   return hip_status(launch_quantize(src, src_type, rows, k, ld_src, fmt, static_cast<uint8_t*>(codes), scales, stream));
 }
 
@@ -125,7 +163,7 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
     if (!valid_fmt(out_fmt)) return MX_ERR_FORMAT;
     if (!out_scales) return MX_ERR_NULL;
     if (n % 32 != 0) return MX_ERR_UNSUPPORTED;
-    if (!aligned(out, 4)) return MX_ERR_ALIGN;
+    if (!aligned(out, 16) || !aligned(out_scales, 4)) return MX_ERR_ALIGN;
   } else {
     if (ldo < n) return MX_ERR_SHAPE;
     if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
@@ -138,10 +176,10 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
   const uint8_t* xc = static_cast<const uint8_t*>(a_codes);
   const uint8_t* xs = a_scales;
   if (a_src && k > 0) {
-    const QuantWs w = quant_ws(m, k);
+    const TiledWs w = tiled_ws(m, k);
     uint8_t* base = static_cast<uint8_t*>(workspace);
-    const hipError_t e = launch_quantize(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off, base + w.scales_off,
-                                         stream);
+    const hipError_t e = launch_quantize_tiled(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off,
+                                               base + w.scales_off, stream);
     if (e != hipSuccess) return MX_ERR_HIP;
     xc = base + w.codes_off;
     xs = base + w.scales_off;
@@ -157,11 +195,16 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
   g.M = (int32_t)m;
   g.N = (int32_t)n;
   g.K = (int32_t)k;
-  g.tiles_m = (int32_t)((m + kTileM - 1) / kTileM);
-  g.tiles_n = (int32_t)((n + kTileN - 1) / kTileN);
+  g.tiles_m = (int32_t)ceil_div(m, kTileM);
+  g.tiles_n = (int32_t)ceil_div(n, kTileN);
+  g.gx = (int32_t)ceil_div(m, kTileGroupRows);
+  g.gw = (int32_t)ceil_div(n, kTileGroupRows);
   const int64_t esize = out_kind == MX_OUT_F32 ? 4 : 2;
   g.vec_store = out_kind != MX_OUT_MX && aligned(out, 16) && (ldo * esize) % 16 == 0;
   if ((int64_t)g.tiles_m * g.tiles_n > INT32_MAX) return MX_ERR_SHAPE;
+  // the kernel addresses one stage of an operand with 32-bit offsets
+  if ((int64_t)g.gx * kChunkCodes >= ((int64_t)1 << 32) || (int64_t)g.gw * kChunkCodes >= ((int64_t)1 << 32))
+    return MX_ERR_UNSUPPORTED;
   return hip_status(launch_gemm(g, a_fmt, w_fmt, epilogue, out_kind, out_fmt, stream));
 }
 

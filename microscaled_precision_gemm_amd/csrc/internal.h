@@ -13,6 +13,16 @@ constexpr int kOutF32 = 0;
 constexpr int kOutBf16 = 1;
 constexpr int kOutMx = 2;
 
+constexpr int kLayoutRows = 0;
+constexpr int kLayoutTiled = 1;
+
+// Tiled MX layout: 128-element stages x 32-row groups, 3072 code bytes and
+// 128 scale bytes per (stage, group).
+constexpr int kTileStageK = 128;
+constexpr int kTileGroupRows = 32;
+constexpr int kChunkCodes = 3072;
+constexpr int kChunkScales = 128;
+
 constexpr int kEpiNone = 0;
 constexpr int kEpiGeluTanh = 1;
 
@@ -22,20 +32,23 @@ constexpr int kTileN = 256;
 constexpr int kStageK = 128;
 
 struct GemmArgs {
-  const uint8_t* x_codes;   // activations [M, 3K/4]
-  const uint8_t* x_scales;  // [M, K/32]
-  const uint8_t* w_codes;   // weights [N, 3K/4]
-  const uint8_t* w_scales;  // [N, K/32]
-  void* out;                // f32 / bf16 [M, ldo] or MX codes [M, 3N/4]
-  uint8_t* out_scales;      // MX output scales [M, N/32]
+  const uint8_t* x_codes;   // activations [M, K], tiled layout
+  const uint8_t* x_scales;
+  const uint8_t* w_codes;   // weights [N, K], tiled layout
+  const uint8_t* w_scales;
+  void* out;                // f32 / bf16 [M, ldo], or MX codes of [M, N] in the tiled layout
+  uint8_t* out_scales;      // MX output scales (tiled layout)
   int64_t ldo;
   int32_t M, N, K;
   int32_t tiles_m, tiles_n;
+  int32_t gx, gw;           // 32-row groups of the activations (ceil(M/32)) and weights (ceil(N/32))
   int32_t vec_store;        // 1 when 16-byte vector stores of a row segment are aligned
 };
 
 hipError_t launch_quantize(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,
                            uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_tiled(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, int out_kind, int out_fmt,
                        hipStream_t stream);
@@ -54,4 +67,17 @@ struct SplitKArgs {
 
 hipError_t launch_gemm_splitk(const SplitKArgs& a, int x_fmt, int w_fmt, int out_kind, hipStream_t stream);
 
+}  // namespace mxg
+
+namespace mxg {
+template <int WF, int XF>
+hipError_t launch_gemm_formats(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t tiled_codes_bytes(int64_t rows, int64_t k) {
+  return ceil_div(k, kTileStageK) * ceil_div(rows, kTileGroupRows) * kChunkCodes;
+}
+inline int64_t tiled_scales_bytes(int64_t rows, int64_t k) {
+  return ceil_div(k, kTileStageK) * ceil_div(rows, kTileGroupRows) * kChunkScales;
+}
 }  // namespace mxg

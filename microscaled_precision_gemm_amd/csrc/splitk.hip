@@ -34,32 +34,52 @@ constexpr int kWgFeatures = 4 * kWaveFeatures;         // 128 features per workg
 constexpr int kGroupK = 512;                           // K per group of 4 MFMAs
 constexpr int kGroupBytes = 384;                       // packed bytes per row per group
 
-struct Frag {
-  u32x4 d[6];
-  uint32_t s;
+// One 16-row fragment over one 512-K group: the four MFMA operands (step s
+// uses the lane's bytes [24 s, 24 s + 24)) and the lane's 4 scale bytes.
+struct Ops {
+  v8i s0, s1, s2, s3;
+  uint32_t sc;
 };
 
-template <int WF, int XF>
-__device__ __forceinline__ void mfma_group(v4f& acc, const Frag& w, const Frag& x) {
-  // step s uses bytes [24 s, 24 s + 24) of the lane's 96 bytes: dwords 6s .. 6s+5
-  const uint32_t* wd = reinterpret_cast<const uint32_t*>(w.d);
-  const uint32_t* xd = reinterpret_cast<const uint32_t*>(x.d);
-#define MXG_STEP(S)                                                                                             \
-  {                                                                                                             \
-    const v8i a = v8i{(int)wd[6 * S], (int)wd[6 * S + 1], (int)wd[6 * S + 2], (int)wd[6 * S + 3],           \
-                      (int)wd[6 * S + 4], (int)wd[6 * S + 5], 0, 0};                                          \
-    const v8i b = v8i{(int)xd[6 * S], (int)xd[6 * S + 1], (int)xd[6 * S + 2], (int)xd[6 * S + 3],           \
-                      (int)xd[6 * S + 4], (int)xd[6 * S + 5], 0, 0};                                          \
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, WF, XF, S, (int)w.s, S, (int)x.s);       \
-  }
-  MXG_STEP(0)
-  MXG_STEP(1)
-  MXG_STEP(2)
-  MXG_STEP(3)
-#undef MXG_STEP
+__device__ __forceinline__ Ops ops_from(const u32x4 d0, const u32x4 d1, const u32x4 d2, const u32x4 d3,
+                                       const u32x4 d4, const u32x4 d5, uint32_t sc) {
+  Ops o;
+  o.s0 = v8i{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], 0, 0};
+  o.s1 = v8i{(int)d1[2], (int)d1[3], (int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3], 0, 0};
+  o.s2 = v8i{(int)d3[0], (int)d3[1], (int)d3[2], (int)d3[3], (int)d4[0], (int)d4[1], 0, 0};
+  o.s3 = v8i{(int)d4[2], (int)d4[3], (int)d5[0], (int)d5[1], (int)d5[2], (int)d5[3], 0, 0};
+  o.sc = sc;
+  return o;
 }
 
-// grid: (ceil(N / 128), splits).  Each wave: 32 features x one K-chunk.
+// Streamed weights: non-temporal 128-bit loads (each byte is read once).
+__device__ __forceinline__ Ops load_w(const uint8_t* p, const uint8_t* sp) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  return ops_from(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1), __builtin_nontemporal_load(q + 2),
+                  __builtin_nontemporal_load(q + 3), __builtin_nontemporal_load(q + 4),
+                  __builtin_nontemporal_load(q + 5), *reinterpret_cast<const uint32_t*>(sp));
+}
+
+// Activations (a few hundred KB, shared by every workgroup: cached loads).
+__device__ __forceinline__ Ops load_x(const uint8_t* p, const uint8_t* sp, bool valid) {
+  if (!valid) {
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    return ops_from(z, z, z, z, z, z, 0x7f7f7f7fu);
+  }
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  return ops_from(q[0], q[1], q[2], q[3], q[4], q[5], *reinterpret_cast<const uint32_t*>(sp));
+}
+
+template <int WF, int XF>
+__device__ __forceinline__ v4f mfma_group(v4f acc, const Ops& w, const Ops& x) {
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s0, x.s0, acc, WF, XF, 0, (int)w.sc, 0, (int)x.sc);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s1, x.s1, acc, WF, XF, 1, (int)w.sc, 1, (int)x.sc);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s2, x.s2, acc, WF, XF, 2, (int)w.sc, 2, (int)x.sc);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s3, x.s3, acc, WF, XF, 3, (int)w.sc, 3, (int)x.sc);
+  return acc;
+}
+
+// grid: (ceil(N / 128), splits).  Each wave: 32 features (2 fragments) x one K-chunk.
 template <int WF, int XF>
 __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -71,70 +91,53 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
   const int kblocks = g.K / 32;
   const int nbase = blockIdx.x * kWgFeatures + wave * kWaveFeatures;
 
-  // this lane's rows: token r16 of the activations, feature nbase + 16f + r16 of the weights
+  // this lane's rows: token r16 of the activations, features nbase + 16 f + r16 of the weights
   const bool xvalid = r16 < g.M;
   const int64_t kbyte0 = (int64_t)split * kchunk * 3 / 4 + 96 * q;
   const int kblk0 = split * (kchunk / 32) + 4 * q;
   const uint8_t* xp = g.x_codes + (int64_t)(xvalid ? r16 : 0) * rowbytes + kbyte0;
   const uint8_t* xs = g.x_scales + (int64_t)(xvalid ? r16 : 0) * kblocks + kblk0;
-  const uint8_t* wp[kFragsPerWave];
-  const uint8_t* wsp[kFragsPerWave];
-#pragma unroll
-  for (int f = 0; f < kFragsPerWave; ++f) {
-    const int n = min(nbase + 16 * f + r16, g.N - 1);
-    wp[f] = g.w_codes + (int64_t)n * rowbytes + kbyte0;
-    wsp[f] = g.w_scales + (int64_t)n * kblocks + kblk0;
-  }
+  const int n0 = min(nbase + r16, g.N - 1), n1 = min(nbase + 16 + r16, g.N - 1);
+  const uint8_t* wp0 = g.w_codes + (int64_t)n0 * rowbytes + kbyte0;
+  const uint8_t* wp1 = g.w_codes + (int64_t)n1 * rowbytes + kbyte0;
+  const uint8_t* ws0 = g.w_scales + (int64_t)n0 * kblocks + kblk0;
+  const uint8_t* ws1 = g.w_scales + (int64_t)n1 * kblocks + kblk0;
 
-  auto load = [&](int grp, Frag& x, Frag (&w)[kFragsPerWave]) {
-    const int64_t bo = (int64_t)grp * kGroupBytes;
-    const int so = grp * 16;
-#pragma unroll
-    for (int f = 0; f < kFragsPerWave; ++f) {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) w[f].d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[f] + bo) + i);
-      w[f].s = *reinterpret_cast<const uint32_t*>(wsp[f] + so);
-    }
-    if (xvalid) {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) x.d[i] = *(reinterpret_cast<const u32x4*>(xp + bo) + i);
-      x.s = *reinterpret_cast<const uint32_t*>(xs + so);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) x.d[i] = u32x4{0u, 0u, 0u, 0u};
-      x.s = 0x7f7f7f7fu;
-    }
-  };
-
-  v4f acc[kFragsPerWave];
-#pragma unroll
-  for (int f = 0; f < kFragsPerWave; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  Frag xa, xb, wa[kFragsPerWave], wb[kFragsPerWave];
-  if (ngroups > 0) load(0, xa, wa);
-  for (int grp = 0; grp < ngroups; grp += 2) {
-    if (grp + 1 < ngroups) load(grp + 1, xb, wb);
-#pragma unroll
-    for (int f = 0; f < kFragsPerWave; ++f) mfma_group<WF, XF>(acc[f], wa[f], xa);
-    if (grp + 1 < ngroups) {
-      if (grp + 2 < ngroups) load(grp + 2, xa, wa);
-#pragma unroll
-      for (int f = 0; f < kFragsPerWave; ++f) mfma_group<WF, XF>(acc[f], wb[f], xb);
+  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  if (ngroups > 0) {
+    Ops x = load_x(xp, xs, xvalid);
+    Ops w0 = load_w(wp0, ws0);
+    Ops w1 = load_w(wp1, ws1);
+    for (int grp = 0; grp < ngroups; ++grp) {
+      Ops xn = x, w0n = w0, w1n = w1;
+      if (grp + 1 < ngroups) {  // next group's loads in flight during this group's MFMAs
+        const int64_t bo = (int64_t)(grp + 1) * kGroupBytes;
+        const int so = (grp + 1) * 16;
+        w0n = load_w(wp0 + bo, ws0 + so);
+        w1n = load_w(wp1 + bo, ws1 + so);
+        xn = load_x(xp + bo, xs + so, xvalid);
+      }
+      acc0 = mfma_group<WF, XF>(acc0, w0, x);
+      acc1 = mfma_group<WF, XF>(acc1, w1, x);
+      x = xn;
+      w0 = w0n;
+      w1 = w1n;
     }
   }
 
-  // lane holds features nbase + 16f + 4q + (0..3) for token r16
+  // lane holds features nbase + 16 f + 4 q + (0..3) for token r16
   if (r16 < g.M) {
     float* part = g.partial + ((int64_t)split * 16 + r16) * g.N;
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; ++f) {
+      const v4f a = f == 0 ? acc0 : acc1;
       const int n = nbase + 16 * f + 4 * q;
       if (n + 4 <= g.N && (g.N & 3) == 0) {
-        *reinterpret_cast<v4f*>(part + n) = acc[f];
+        *reinterpret_cast<v4f*>(part + n) = a;
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (n + i < g.N) part[n + i] = acc[f][i];
+          if (n + i < g.N) part[n + i] = a[i];
       }
     }
   }

@@ -30,10 +30,34 @@ def oracle_mx(x64: np.ndarray, fmt: str):
     return codes, scales, O.dequantize(codes, scales, fmt)
 
 
+def tiled_to_rows(codes_t: np.ndarray, scales_t: np.ndarray, rows: int, k: int):
+    """Rearrange the tiled MX layout (128-element stages x 32-row groups, as the
+    library's header defines it) into row-major packed codes [rows, 3k/4] and
+    scales [rows, k/32].  Also returns the padding (codes and scale bytes of
+    rows >= rows or blocks >= k/32), which must be 0 and 127."""
+    stages, groups = -(-k // 128), -(-rows // 32)
+    c = np.asarray(codes_t).reshape(stages, groups, 6, 32, 16)   # [stage, group, piece, row, byte]
+    c = c.transpose(1, 3, 0, 2, 4).reshape(groups * 32, stages * 96)
+    s = np.asarray(scales_t).reshape(stages, groups, 32, 4)       # [stage, group, row, block]
+    s = s.transpose(1, 2, 0, 3).reshape(groups * 32, stages * 4)
+    pad_c = np.concatenate([c[rows:].ravel(), c[:rows, 3 * k // 4:].ravel()])
+    pad_s = np.concatenate([s[rows:].ravel(), s[:rows, k // 32:].ravel()])
+    return c[:rows, :3 * k // 4], s[:rows, :k // 32], pad_c, pad_s
+
+
+def mx_rows_view(gpu_mx):
+    """Row-major (codes, scales) of a GPU MXTensor, checking tiled padding."""
+    gc, gs = to_np(gpu_mx.codes), to_np(gpu_mx.scales)
+    if gpu_mx.layout == "tiled":
+        gc, gs, pad_c, pad_s = tiled_to_rows(gc, gs, gpu_mx.rows, gpu_mx.k)
+        assert not pad_c.any(), "tiled padding codes must be 0"
+        assert np.all(pad_s == 127), "tiled padding scales must be 127"
+    return gc, gs
+
+
 def assert_mx_equal(gpu_mx, codes_o: np.ndarray, scales_o: np.ndarray, what: str, rows=None) -> None:
     """GPU packed codes + scales must equal the oracle's bit for bit."""
-    gc = to_np(gpu_mx.codes)
-    gs = to_np(gpu_mx.scales)
+    gc, gs = mx_rows_view(gpu_mx)
     if rows is not None:
         gc, gs = gc[rows], gs[rows]
     k = codes_o.shape[1]

@@ -71,18 +71,20 @@ def q(*a):
 @host_only
 def test_quantize_validation(L):
     s = NULL
-    assert q(FAKE, 5, 4, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_FORMAT
-    assert q(FAKE, 0, 4, 64, 64, 7, FAKE, FAKE, s) == B.MX_ERR_FORMAT
-    assert q(FAKE, 0, -1, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_SHAPE
-    assert q(FAKE, 0, 4, 48, 48, 2, FAKE, FAKE, s) == B.MX_ERR_SHAPE
-    assert q(FAKE, 0, 4, 64, 32, 2, FAKE, FAKE, s) == B.MX_ERR_SHAPE
-    assert q(NULL, 0, 4, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_NULL
-    assert q(FAKE, 0, 4, 64, 64, 2, NULL, FAKE, s) == B.MX_ERR_NULL
-    assert q(FAKE + 2, 0, 4, 64, 64, 2, FAKE, FAKE, s) == B.MX_ERR_ALIGN
-    assert q(FAKE, 0, 4, 64, 68, 2, FAKE, FAKE, s) == B.MX_ERR_ALIGN
-    assert q(FAKE, 0, 4, 64, 64, 2, FAKE + 4, FAKE, s) == B.MX_ERR_ALIGN
-    assert q(NULL, 0, 0, 64, 64, 2, NULL, NULL, s) == B.MX_OK  # empty is a no-op
-    assert q(NULL, 0, 4, 0, 0, 2, NULL, NULL, s) == B.MX_OK
+    assert q(FAKE, 5, 4, 64, 64, 2, 1, FAKE, FAKE, s) == B.MX_ERR_FORMAT
+    assert q(FAKE, 0, 4, 64, 64, 7, 1, FAKE, FAKE, s) == B.MX_ERR_FORMAT
+    assert q(FAKE, 0, -1, 64, 64, 2, 1, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert q(FAKE, 0, 4, 48, 48, 2, 1, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert q(FAKE, 0, 4, 64, 32, 2, 1, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert q(NULL, 0, 4, 64, 64, 2, 1, FAKE, FAKE, s) == B.MX_ERR_NULL
+    assert q(FAKE, 0, 4, 64, 64, 2, 1, NULL, FAKE, s) == B.MX_ERR_NULL
+    assert q(FAKE + 2, 0, 4, 64, 64, 2, 1, FAKE, FAKE, s) == B.MX_ERR_ALIGN
+    assert q(FAKE, 0, 4, 64, 68, 2, 1, FAKE, FAKE, s) == B.MX_ERR_ALIGN
+    assert q(FAKE, 0, 4, 64, 64, 2, 1, FAKE + 4, FAKE, s) == B.MX_ERR_ALIGN
+    assert q(FAKE, 0, 4, 64, 64, 2, 7, FAKE, FAKE, s) == B.MX_ERR_FORMAT  # layout
+    assert q(FAKE, 0, 4, 64, 64, 2, 0, FAKE, FAKE + 2, s) == B.MX_ERR_ALIGN  # scales
+    assert q(NULL, 0, 0, 64, 64, 2, 1, NULL, NULL, s) == B.MX_OK  # empty is a no-op
+    assert q(NULL, 0, 4, 0, 0, 2, 1, NULL, NULL, s) == B.MX_OK
 
 
 def g(**kw):
@@ -112,10 +114,11 @@ def test_gemm_validation(L):
     assert g(out_kind=2, out_scales=FAKE, n=48) == B.MX_ERR_UNSUPPORTED
     assert g(out_kind=2, out_scales=NULL) == B.MX_ERR_NULL
     assert g(out_kind=2, out_scales=FAKE, out_fmt=1) == B.MX_ERR_FORMAT
+    assert g(out_kind=2, out_scales=FAKE, out=FAKE + 4) == B.MX_ERR_ALIGN
     # bf16 activations need a workspace for the quantized copy
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=128) == B.MX_ERR_WORKSPACE
     need = mx.mx_gemm_workspace_size(64, 64, 128, True, 0)
-    assert need >= 64 * 96 + 64 * 4
+    assert need >= 2 * 3072 + 2 * 128  # 1 stage x 2 row groups, tiled
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=128, ws=FAKE, ws_bytes=need - 1) == B.MX_ERR_WORKSPACE
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=120, ws=FAKE, ws_bytes=need) == B.MX_ERR_SHAPE
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=130, ws=FAKE, ws_bytes=need) == B.MX_ERR_ALIGN
@@ -142,6 +145,17 @@ def test_splitk_validation(L):
     assert sk(ws=FAKE + 16) == B.MX_ERR_ALIGN
     assert sk(a_fmt=3) == B.MX_ERR_UNSUPPORTED
     assert sk(m=0) == B.MX_OK
+
+
+def test_packed_bytes(L):
+    assert mx.mx_packed_bytes(300, 416, "rows", 0) == 300 * 416 * 3 // 4
+    assert mx.mx_packed_bytes(300, 416, "rows", 1) == 300 * 13
+    # tiled: ceil(416/128) = 4 stages x ceil(300/32) = 10 groups
+    assert mx.mx_packed_bytes(300, 416, "tiled", 0) == 4 * 10 * 3072
+    assert mx.mx_packed_bytes(300, 416, "tiled", 1) == 4 * 10 * 128
+    assert mx.mx_packed_bytes(300, 100, "tiled", 0) == 0  # invalid K
+    assert mx.lib().mx_packed_bytes(10, 64, 5, 0) == 0
+    assert mx.lib().mx_packed_bytes(10, 64, 1, 2) == 0
 
 
 def test_workspace_sizes(L):

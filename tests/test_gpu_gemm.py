@@ -9,7 +9,7 @@ import microscaled_precision_gemm_amd as mx
 from microscaled_precision_gemm_amd import synthetic as syn
 from oracle import mx_oracle as O
 from tests.parity import (assert_bf16_close, assert_fp32_close, assert_mx_equal, bf16_tensor_to_f64,
-                          check_mx_epilogue, say, to_np)
+                          check_mx_epilogue, mx_rows_view, say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +27,8 @@ def _operands(m, n, k, a_fmt, w_fmt, seed=0, a_std=1.0, w_std=0.02, t_outliers=F
     return a, w, (ca, sa), (cw, sw), c, s
 
 
-def _gpu_weights(w, w_fmt, ref):
-    wq = mx.mx_quantize(w.cuda(), w_fmt)
+def _gpu_weights(w, w_fmt, ref, layout="tiled"):
+    wq = mx.mx_quantize(w.cuda(), w_fmt, layout)
     torch.cuda.synchronize()
     assert_mx_equal(wq, ref[0], ref[1], "weights")
     return wq
@@ -68,7 +68,8 @@ def test_gemm_mx_epilogue(a_fmt, w_fmt, out_fmt, gelu):
     o = mx.mx_gemm(a.cuda(), wq, out_kind="mx", epilogue="gelu_tanh" if gelu else "none", out_fmt=out_fmt,
                    a_fmt=a_fmt)
     torch.cuda.synchronize()
-    stats = check_mx_epilogue(to_np(o.codes), to_np(o.scales), c, s, gelu, out_fmt)
+    oc, os_ = mx_rows_view(o)
+    stats = check_mx_epilogue(oc, os_, c, s, gelu, out_fmt)
     print("mx epilogue", stats)
     assert stats["code_steps"] <= 1e-3 * stats["elements"]
 
@@ -109,7 +110,7 @@ def test_chained_fc1_fc2_small():
     da = O.dequantize(*O.quantize(a64, "e2m3"), "e2m3")
     dw1 = O.dequantize(*O.quantize(rng_w1.to(torch.float64).numpy(), "e2m3"), "e2m3")
     c1, s1 = O.gemm_ref(da, dw1)
-    check_mx_epilogue(to_np(hq.codes), to_np(hq.scales), c1, s1, True, "e2m3")
+    check_mx_epilogue(*mx_rows_view(hq), c1, s1, True, "e2m3")
     # fc2 stage: oracle chain (its own intermediate) vs GPU chain; a tolerated
     # one-step difference of an intermediate code moves an output by at most
     # that step times |w|, so compare with the oracle's fc2 on its own codes and
@@ -148,13 +149,15 @@ def test_determinism_guard_bands_and_poison():
     assert torch.all(big[m:, :] == 12345.0) and torch.all(big[:, n:] == 12345.0)
     assert_fp32_close(to_np(view).astype(np.float64), c, s, "strided output")
     # MX output poisoned with 0xFF
-    o = mx.MXTensor(torch.full((m, 3 * n // 4), 0xFF, dtype=torch.uint8, device="cuda"),
-                    torch.full((m, n // 32), 0xFF, dtype=torch.uint8, device="cuda"), "e2m3", n)
+    o = mx.MXTensor.empty(m, n, "e2m3", "tiled", "cuda")
+    o.codes.fill_(0xFF)
+    o.scales.fill_(0xFF)
     mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", out=o)
     o2 = mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh")
     torch.cuda.synchronize()
     assert torch.equal(o.codes, o2.codes) and torch.equal(o.scales, o2.scales)
     assert not torch.any(o.scales == 0xFF)
+    mx_rows_view(o)  # padding of the tiled output written as 0 codes / 127 scales
 
 
 def test_edge_shapes():
@@ -167,14 +170,14 @@ def test_edge_shapes():
         torch.cuda.synchronize()
         assert_fp32_close(to_np(o).astype(np.float64), c, s, f"edge {m}x{n}x{k}")
     # K = 0: C = 0, GELU(0) = 0, MX output: zero blocks
-    wq = mx.MXTensor(torch.zeros((64, 0), dtype=torch.uint8, device="cuda"),
-                     torch.zeros((64, 0), dtype=torch.uint8, device="cuda"), "e2m3", 0)
+    wq = mx.MXTensor.empty(64, 0, "e2m3", "tiled", "cuda")
     a = torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda")
     o = mx.mx_gemm(a, wq, out_kind="f32", epilogue="gelu_tanh")
     om = mx.mx_gemm(a, wq, out_kind="mx", epilogue="gelu_tanh")
     torch.cuda.synchronize()
     assert torch.all(o == 0)
-    assert torch.all(om.codes == 0) and torch.all(om.scales == 0)
+    oc, os_ = mx_rows_view(om)  # also checks the padding (0 codes, 127 scales)
+    assert not oc.any() and not os_.any()  # zero blocks: codes 0, scale byte 0
 
 
 @pytest.mark.parametrize("m", [8, 16, 5])
@@ -184,7 +187,7 @@ def test_splitk_small(m, splits, w_fmt):
     n, k = 400, 4096
     a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", w_fmt, seed=31 + m)
     say(f"splitk m={m} n={n} k={k} S={splits} w={w_fmt}")
-    wq = _gpu_weights(w, w_fmt, qw)
+    wq = _gpu_weights(w, w_fmt, qw, "rows")
     o = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="bf16")
     o32 = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="f32")
     o_again = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="bf16")
@@ -199,10 +202,11 @@ def test_splitk_matches_plain_gemm_property():
     reorders the fp32 sum)."""
     m, n, k = 16, 256, 8192
     a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", "e3m2", seed=41)
-    wq = _gpu_weights(w, "e3m2", qw)
+    wq = _gpu_weights(w, "e3m2", qw, "rows")
+    wt = _gpu_weights(w, "e3m2", qw, "tiled")
     say("splitk vs plain")
     outs = [mx.mx_gemm_splitk(a.cuda(), wq, sp, out_kind="f32") for sp in (1, 2, 16)]
-    plain = mx.mx_gemm(a.cuda(), wq, out_kind="f32")
+    plain = mx.mx_gemm(a.cuda(), wt, out_kind="f32")
     torch.cuda.synchronize()
     for o in outs + [plain]:
         assert_fp32_close(to_np(o).astype(np.float64), c, s, "split count")

@@ -12,6 +12,7 @@ from tests.parity import assert_mx_equal, say
 pytestmark = pytest.mark.gpu
 
 FMTS = ["e2m3", "e3m2"]
+LAYOUTS = ["tiled", "rows"]
 
 
 def _all_bf16_patterns() -> torch.Tensor:
@@ -19,20 +20,24 @@ def _all_bf16_patterns() -> torch.Tensor:
     return bits.view(torch.bfloat16)
 
 
-def _quantize_both(x_bf16_cpu: torch.Tensor, fmt: str, what: str):
-    say(f"quantize {what} {tuple(x_bf16_cpu.shape)} {fmt}")
-    g = mx.mx_quantize(x_bf16_cpu.cuda(), fmt)
+def _quantize_both(x_bf16_cpu: torch.Tensor, fmt: str, what: str, layout: str = "tiled"):
+    say(f"quantize {what} {tuple(x_bf16_cpu.shape)} {fmt} {layout}")
+    g = mx.mx_quantize(x_bf16_cpu.cuda(), fmt, layout)
     torch.cuda.synchronize()
     c, s = O.quantize(x_bf16_cpu.to(torch.float64).numpy(), fmt)
     assert_mx_equal(g, c, s, what)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
-def test_all_bf16_patterns_consecutive_blocks(fmt):
+def test_all_bf16_patterns_consecutive_blocks(fmt, layout):
     """All 65536 bf16 bit patterns, 32 consecutive patterns per block (shared
     sign and exponent: exercises the top binade, saturation, subnormal and
     zero blocks, and the Inf / NaN blocks)."""
-    _quantize_both(_all_bf16_patterns().reshape(2048, 32), fmt, "all-bf16 consecutive")
+    x = _all_bf16_patterns().reshape(2048, 32)
+    _quantize_both(x, fmt, "all-bf16 consecutive", layout)
+    # the same patterns as 128-wide rows (4 blocks per row), a ragged row count
+    _quantize_both(x.reshape(512, 128)[:500], fmt, "all-bf16 rows of 128", layout)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -52,8 +57,9 @@ def test_all_bf16_patterns_fixed_scale_blocks(fmt, shift):
     _quantize_both(x, fmt, f"fixed-scale shift {shift}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
-def test_f32_source_full_mantissa(fmt):
+def test_f32_source_full_mantissa(fmt, layout):
     """fp32 sources (the fc1 epilogue's input type): random full-mantissa values
     over 200 binades, exact fp32 midpoints, subnormal and tiny blocks."""
     rng = np.random.default_rng(21)
@@ -69,8 +75,8 @@ def test_f32_source_full_mantissa(fmt):
     x[::89, :32] = 0.0
     x[5, 3] = -0.0
     t = torch.from_numpy(x)
-    say(f"quantize f32 {t.shape} {fmt}")
-    g = mx.mx_quantize(t.cuda(), fmt)
+    say(f"quantize f32 {t.shape} {fmt} {layout}")
+    g = mx.mx_quantize(t.cuda(), fmt, layout)
     torch.cuda.synchronize()
     c, s = O.quantize(x.astype(np.float64), fmt)
     assert_mx_equal(g, c, s, "f32 source")
@@ -84,11 +90,12 @@ def test_nonfinite_and_zero_blocks(fmt):
     x[2, 70] = -float("inf")
     x[3, :] = -0.0
     for dt in (torch.bfloat16, torch.float32):
-        say(f"quantize non-finite {dt} {fmt}")
-        g = mx.mx_quantize(x.to(dt).cuda(), fmt)
+      for layout in LAYOUTS:
+        say(f"quantize non-finite {dt} {fmt} {layout}")
+        g = mx.mx_quantize(x.to(dt).cuda(), fmt, layout)
         torch.cuda.synchronize()
         c, s = O.quantize(x.to(dt).to(torch.float64).numpy(), fmt)
-        assert_mx_equal(g, c, s, f"non-finite {dt}")
+        assert_mx_equal(g, c, s, f"non-finite {dt} {layout}")
         assert s[0, 0] == 0xFF and s[1, 1] == 0xFF and s[2, 2] == 0xFF and s[3, 0] == 0
 
 
@@ -98,20 +105,22 @@ def test_strided_rows_and_ragged_shapes():
     rng = np.random.default_rng(3)
     base = torch.from_numpy(rng.standard_normal((37, 200)).astype(np.float32)).to(torch.bfloat16)
     for k in (32, 96, 160):
-        view = base.cuda()[:, :k]  # row stride 200 elements = 400 bytes (16-byte multiple)
-        say(f"quantize strided k={k}")
-        g = mx.mx_quantize(view, "e2m3")
-        torch.cuda.synchronize()
-        c, s = O.quantize(base[:, :k].to(torch.float64).numpy(), "e2m3")
-        assert_mx_equal(g, c, s, f"strided k={k}")
+        for layout in LAYOUTS:
+            view = base.cuda()[:, :k]  # row stride 200 elements = 400 bytes (16-byte multiple)
+            say(f"quantize strided k={k} {layout}")
+            g = mx.mx_quantize(view, "e2m3", layout)
+            torch.cuda.synchronize()
+            c, s = O.quantize(base[:, :k].to(torch.float64).numpy(), "e2m3")
+            assert_mx_equal(g, c, s, f"strided k={k} {layout}")
 
 
 def test_empty_inputs_are_noops():
     for shape in ((0, 64), (5, 0)):
-        say(f"quantize empty {shape}")
-        g = mx.mx_quantize(torch.zeros(shape, dtype=torch.bfloat16, device="cuda"), "e2m3")
-        torch.cuda.synchronize()
-        assert g.codes.numel() == 0 and g.scales.numel() == 0
+        for layout in LAYOUTS:
+            say(f"quantize empty {shape} {layout}")
+            g = mx.mx_quantize(torch.zeros(shape, dtype=torch.bfloat16, device="cuda"), "e2m3", layout)
+            torch.cuda.synchronize()
+            assert g.codes.numel() == 0 and g.scales.numel() == 0
 
 
 @pytest.mark.parametrize("name", ["proj", "fc1", "fc2", "skinny"])
@@ -120,11 +129,12 @@ def test_workload_activations_and_weights(name):
     oracle checks a seeded sample of rows plus the first and last rows)."""
     w = syn.WORKLOADS[name]
     rng = np.random.default_rng(5)
+    layout = "rows" if name == "skinny" else "tiled"  # the split-K path reads the row-major layout
     for which, fmt in (("a", "e2m3"), ("w", w.w_fmt)):
         t = syn.make_a(w) if which == "a" else syn.make_w(w)
         rows = np.unique(np.concatenate([[0, t.shape[0] - 1], rng.choice(t.shape[0], size=min(64, t.shape[0]), replace=False)]))
-        say(f"quantize {name}.{which} {tuple(t.shape)} {fmt}")
-        g = mx.mx_quantize(t.cuda(), fmt)
+        say(f"quantize {name}.{which} {tuple(t.shape)} {fmt} {layout}")
+        g = mx.mx_quantize(t.cuda(), fmt, layout)
         torch.cuda.synchronize()
         c, s = O.quantize(t[torch.from_numpy(rows)].to(torch.float64).numpy(), fmt)
         assert_mx_equal(g, c, s, f"{name}.{which}", rows=rows)
