@@ -99,7 +99,7 @@ def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
     dev = torch.device("cuda:0")
     a = syn.make_a(w, m=m).to(dev)
     wb = syn.make_w(w).to(dev)
-    ws = [mx.mx_quantize(wb, w.w_fmt, "rows") for _ in range(copies)]
+    ws = [mx.mx_quantize(wb, w.w_fmt, "tiled") for _ in range(copies)]
     del wb
     out = torch.empty((m, w.n), dtype=torch.bfloat16, device=dev)
     work = torch.empty(mx.mx_gemm_workspace_size(m, w.n, w.k, True, splits), dtype=torch.uint8, device=dev)

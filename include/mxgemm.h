@@ -36,11 +36,11 @@
  * with exact block-scaled products and fp32 accumulation.  All buffers are
  * owned by the caller and live in device memory.  Two storage layouts:
  *
- * MX_LAYOUT_ROWS (interchange; the split-K GEMM's operands):
+ * MX_LAYOUT_ROWS (interchange):
  *   codes   [rows, 3K/4] bytes, row-major (row r is the packed row above);
  *   scales  [rows, K/32] bytes, row-major.
  *
- * MX_LAYOUT_TILED (the mx_gemm operand and MX-output layout): the matrix is
+ * MX_LAYOUT_TILED (the operand layout of both GEMMs and of the MX output): the matrix is
  * cut into stages of 128 K-elements (S = ceil(K/128)) and groups of 32 rows
  * (G = ceil(rows/32)).  Each (stage s, group g) pair owns
  *   codes   3072 bytes at offset (s*G + g) * 3072: 6 pieces of 512 bytes;
@@ -175,10 +175,9 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
  * K into `splits` contiguous chunks whose fp32 partial sums are added in the
  * fixed order 0, 1, ..., splits-1 (deterministic) before the output rounding.
  *
- * Arguments as mx_gemm, except that a_codes / a_scales and w_codes /
- * w_scales are in MX_LAYOUT_ROWS, and with:
- *   splits    >= 1; k % splits == 0 and each chunk k/splits a multiple of
- *             512 (else MX_ERR_UNSUPPORTED); m <= 16 (else MX_ERR_SHAPE).
+ * Arguments as mx_gemm (operands in MX_LAYOUT_TILED), with:
+ *   splits    >= 1; k % (128 * splits) == 0, i.e. each chunk is whole 128-element
+ *             stages (else MX_ERR_UNSUPPORTED); m <= 16 (else MX_ERR_SHAPE).
  *   epilogue  MX_EPI_NONE only; out_kind MX_OUT_F32 or MX_OUT_BF16.
  *   workspace at least mx_gemm_workspace_size(m, n, k, a_src != NULL, splits)
  *             bytes (quantized activations plus fp32 partials).

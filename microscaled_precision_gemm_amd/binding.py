@@ -255,10 +255,10 @@ def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kin
                    a_fmt: str = "e2m3", out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Skinny C = A W^T (m <= 16) with K split into ``splits`` chunks, fp32
     partials summed in a fixed order."""
-    _check_mx(w, "w", "rows")
+    _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
     if isinstance(a, MXTensor):
-        _check_mx(a, "a", "rows")
+        _check_mx(a, "a", "tiled")
         a_src, a_codes, a_scales, af, lda, m = None, a.codes, a.scales, _fmt(a.fmt), 0, a.rows
         src_type = MX_SRC_BF16
     else:

@@ -22,19 +22,6 @@ bool valid_fmt(int32_t f) { return f == MX_FMT_E2M3 || f == MX_FMT_E3M2; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
-// Workspace for activations quantized inside a call: codes then scales.
-struct QuantWs {
-  size_t codes_off, scales_off, end;
-};
-
-QuantWs quant_ws(int64_t rows, int64_t k) {
-  QuantWs w;
-  w.codes_off = 0;
-  w.scales_off = round_up((size_t)(rows * (k / 32) * 24), kWsAlign);
-  w.end = w.scales_off + round_up((size_t)(rows * (k / 32)), kWsAlign);
-  return w;
-}
-
 bool valid_layout(int32_t l) { return l == MX_LAYOUT_ROWS || l == MX_LAYOUT_TILED; }
 
 int check_quantize_args(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
@@ -134,7 +121,7 @@ size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t a_is_src,
   if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || splits < 0) return 0;
   if (splits == 0) return a_is_src ? tiled_ws(m, k).end : 0;
   if (m > 16) return 0;
-  const size_t q = a_is_src ? quant_ws(m, k).end : 0;
+  const size_t q = a_is_src ? tiled_ws(m, k).end : 0;
   return q + round_up((size_t)splits * 16 * (size_t)n * 4, kWsAlign);
 }
 
@@ -220,7 +207,7 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
   if (!out) return MX_ERR_NULL;
   if (ldo < n) return MX_ERR_SHAPE;
   if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
-  if (k % splits != 0 || (k / splits) % 512 != 0) return MX_ERR_UNSUPPORTED;
+  if (k % (kTileStageK * (int64_t)splits) != 0) return MX_ERR_UNSUPPORTED;
   const size_t need = mx_gemm_workspace_size(m, n, k, a_src != nullptr, splits);
   if (!workspace || workspace_bytes < need) return MX_ERR_WORKSPACE;
   if (!aligned(workspace, kWsAlign)) return MX_ERR_ALIGN;
@@ -231,9 +218,9 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
   const uint8_t* xs = a_scales;
   size_t part_off = 0;
   if (a_src && k > 0) {
-    const QuantWs w = quant_ws(m, k);
-    const hipError_t e = launch_quantize(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off, base + w.scales_off,
-                                         stream);
+    const TiledWs w = tiled_ws(m, k);
+    const hipError_t e = launch_quantize_tiled(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off,
+                                               base + w.scales_off, stream);
     if (e != hipSuccess) return MX_ERR_HIP;
     xc = base + w.codes_off;
     xs = base + w.scales_off;
@@ -251,7 +238,7 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
   g.N = (int32_t)n;
   g.K = (int32_t)k;
   g.splits = splits;
-  g.vec_store = 0;
+  g.gw = (int32_t)ceil_div(n, kTileGroupRows);
   return hip_status(launch_gemm_splitk(g, a_fmt, w_fmt, out_kind, stream));
 }
 

@@ -54,15 +54,15 @@ hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, in
                        hipStream_t stream);
 
 struct SplitKArgs {
-  const uint8_t* x_codes;   // activations [M, 3K/4], M <= 16
-  const uint8_t* x_scales;  // [M, K/32]
-  const uint8_t* w_codes;   // weights [N, 3K/4]
-  const uint8_t* w_scales;  // [N, K/32]
+  const uint8_t* x_codes;   // activations [M, K], M <= 16, tiled layout (one 32-row group)
+  const uint8_t* x_scales;
+  const uint8_t* w_codes;   // weights [N, K], tiled layout
+  const uint8_t* w_scales;
   float* partial;           // [splits, 16, N] fp32 workspace
   void* out;                // f32 / bf16 [M, ldo]
   int64_t ldo;
   int32_t M, N, K, splits;
-  int32_t vec_store;
+  int32_t gw;               // 32-row groups of the weights
 };
 
 hipError_t launch_gemm_splitk(const SplitKArgs& a, int x_fmt, int w_fmt, int out_kind, hipStream_t stream);

@@ -7,15 +7,15 @@
 // (0.78 bytes per weight), so the kernel is built for memory-level
 // parallelism, not for the matrix cores:
 //
-//  * V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the weights as the A operand
-//    (16 feature rows) and the tokens as the B operand (16 columns, rows
-//    >= M fed as zeros, so M = 8 costs no extra bytes).
-//  * Inside a group of 4 consecutive MFMAs (512 K), lane group q of step s
-//    handles K-block 4q + s.  Each lane therefore loads 96 contiguous bytes
-//    (6 x 128-bit loads) and its 4 scale bytes as one dword; op_sel = s picks
-//    the byte.
-//  * Each wave streams 2 fragments (32 features) of its K-chunk with the next
-//    group's loads in flight; there is no LDS and no barrier.
+//  * Both operands are in the tiled MX layout.  A wave owns one 32-feature
+//    group of the weights and one K-chunk; per 128-element stage each lane
+//    loads 3 x 16 bytes of its row (pieces 3h .. 3h+2), so every load
+//    instruction reads two runs of 512 contiguous bytes.
+//  * V_MFMA_SCALE_F32_32X32X64_F8F6F4 with the weights as the A operand and
+//    the tokens as the B operand; token rows 16..31 are layout padding (zero
+//    codes), so M = 8 or 16 costs no extra weight bytes and no branches.
+//  * A window of kWindow stages of loads stays in flight per wave (no LDS, no
+//    barrier); the activations (a few hundred KB) come from L2.
 //  * fp32 partial sums go to a workspace [S, 16, N]; a second kernel adds the
 //    S partials in the fixed order 0..S-1 and rounds once (deterministic).
 #include "internal.h"
@@ -28,116 +28,81 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kSkThreads = 256;
-constexpr int kFragsPerWave = 2;                       // 16-feature fragments per wave
-constexpr int kWaveFeatures = 16 * kFragsPerWave;      // 32
-constexpr int kWgFeatures = 4 * kWaveFeatures;         // 128 features per workgroup
-constexpr int kGroupK = 512;                           // K per group of 4 MFMAs
-constexpr int kGroupBytes = 384;                       // packed bytes per row per group
+constexpr int kWgGroups = 4;          // 32-feature groups per workgroup (one per wave)
+constexpr int kWindow = 4;            // stages of loads in flight per wave
 
-// One 16-row fragment over one 512-K group: the four MFMA operands (step s
-// uses the lane's bytes [24 s, 24 s + 24)) and the lane's 4 scale bytes.
-struct Ops {
-  v8i s0, s1, s2, s3;
-  uint32_t sc;
+struct StageOps {
+  v8i w0, w1, x0, x1;  // sub-step 0 / 1 operands
+  int ws, xs;          // scale pairs (bytes 2h, 2h+1 of the lane's row)
 };
 
-__device__ __forceinline__ Ops ops_from(const u32x4 d0, const u32x4 d1, const u32x4 d2, const u32x4 d3,
-                                       const u32x4 d4, const u32x4 d5, uint32_t sc) {
-  Ops o;
-  o.s0 = v8i{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], 0, 0};
-  o.s1 = v8i{(int)d1[2], (int)d1[3], (int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3], 0, 0};
-  o.s2 = v8i{(int)d3[0], (int)d3[1], (int)d3[2], (int)d3[3], (int)d4[0], (int)d4[1], 0, 0};
-  o.s3 = v8i{(int)d4[2], (int)d4[3], (int)d5[0], (int)d5[1], (int)d5[2], (int)d5[3], 0, 0};
-  o.sc = sc;
-  return o;
+__device__ __forceinline__ void split_pieces(const u32x4 d0, const u32x4 d1, const u32x4 d2, v8i& s0, v8i& s1) {
+  s0 = v8i{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], 0, 0};
+  s1 = v8i{(int)d1[2], (int)d1[3], (int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3], 0, 0};
 }
 
-// Streamed weights: non-temporal 128-bit loads (each byte is read once).
-__device__ __forceinline__ Ops load_w(const uint8_t* p, const uint8_t* sp) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  return ops_from(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1), __builtin_nontemporal_load(q + 2),
-                  __builtin_nontemporal_load(q + 3), __builtin_nontemporal_load(q + 4),
-                  __builtin_nontemporal_load(q + 5), *reinterpret_cast<const uint32_t*>(sp));
-}
-
-// Activations (a few hundred KB, shared by every workgroup: cached loads).
-__device__ __forceinline__ Ops load_x(const uint8_t* p, const uint8_t* sp, bool valid) {
-  if (!valid) {
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-    return ops_from(z, z, z, z, z, z, 0x7f7f7f7fu);
-  }
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  return ops_from(q[0], q[1], q[2], q[3], q[4], q[5], *reinterpret_cast<const uint32_t*>(sp));
-}
-
-template <int WF, int XF>
-__device__ __forceinline__ v4f mfma_group(v4f acc, const Ops& w, const Ops& x) {
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s0, x.s0, acc, WF, XF, 0, (int)w.sc, 0, (int)x.sc);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s1, x.s1, acc, WF, XF, 1, (int)w.sc, 1, (int)x.sc);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s2, x.s2, acc, WF, XF, 2, (int)w.sc, 2, (int)x.sc);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.s3, x.s3, acc, WF, XF, 3, (int)w.sc, 3, (int)x.sc);
-  return acc;
-}
-
-// grid: (ceil(N / 128), splits).  Each wave: 32 features (2 fragments) x one K-chunk.
+// grid: (ceil(N / 128), splits).  Wave w: weight group blockIdx.x * 4 + w, K-chunk blockIdx.y.
 template <int WF, int XF>
 __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = lane >> 4, r16 = lane & 15;
+  const int h = lane >> 5, j = lane & 31;
+  const int grp = blockIdx.x * kWgGroups + wave;
+  if (grp >= g.gw) return;  // whole wave; the kernel has no barriers
   const int split = blockIdx.y;
-  const int kchunk = g.K / g.splits;
-  const int ngroups = kchunk / kGroupK;
-  const int64_t rowbytes = (int64_t)g.K * 3 / 4;
-  const int kblocks = g.K / 32;
-  const int nbase = blockIdx.x * kWgFeatures + wave * kWaveFeatures;
+  const int sps = g.K / kTileStageK / g.splits;  // stages per split
+  const int s0 = split * sps;
+  const int lane_off = 3 * h * 512 + j * 16;
+  const int scale_off = j * 4 + 2 * h;
+  const uint8_t* wc = g.w_codes + ((int64_t)s0 * g.gw + grp) * kChunkCodes + lane_off;
+  const uint8_t* ws = g.w_scales + ((int64_t)s0 * g.gw + grp) * kChunkScales + scale_off;
+  const uint8_t* xc = g.x_codes + (int64_t)s0 * kChunkCodes + lane_off;  // activations: one 32-row group
+  const uint8_t* xs = g.x_scales + (int64_t)s0 * kChunkScales + scale_off;
+  const int64_t w_step = (int64_t)g.gw * kChunkCodes, ws_step = (int64_t)g.gw * kChunkScales;
 
-  // this lane's rows: token r16 of the activations, features nbase + 16 f + r16 of the weights
-  const bool xvalid = r16 < g.M;
-  const int64_t kbyte0 = (int64_t)split * kchunk * 3 / 4 + 96 * q;
-  const int kblk0 = split * (kchunk / 32) + 4 * q;
-  const uint8_t* xp = g.x_codes + (int64_t)(xvalid ? r16 : 0) * rowbytes + kbyte0;
-  const uint8_t* xs = g.x_scales + (int64_t)(xvalid ? r16 : 0) * kblocks + kblk0;
-  const int n0 = min(nbase + r16, g.N - 1), n1 = min(nbase + 16 + r16, g.N - 1);
-  const uint8_t* wp0 = g.w_codes + (int64_t)n0 * rowbytes + kbyte0;
-  const uint8_t* wp1 = g.w_codes + (int64_t)n1 * rowbytes + kbyte0;
-  const uint8_t* ws0 = g.w_scales + (int64_t)n0 * kblocks + kblk0;
-  const uint8_t* ws1 = g.w_scales + (int64_t)n1 * kblocks + kblk0;
+  auto load = [&](int i) {
+    StageOps o;
+    const u32x4* wp = reinterpret_cast<const u32x4*>(wc + i * w_step);
+    const u32x4* xp = reinterpret_cast<const u32x4*>(xc + (int64_t)i * kChunkCodes);
+    split_pieces(__builtin_nontemporal_load(wp), __builtin_nontemporal_load(wp + 32), __builtin_nontemporal_load(wp + 64),
+                 o.w0, o.w1);
+    split_pieces(xp[0], xp[32], xp[64], o.x0, o.x1);
+    o.ws = *reinterpret_cast<const uint16_t*>(ws + i * ws_step);
+    o.xs = *reinterpret_cast<const uint16_t*>(xs + (int64_t)i * kChunkScales);
+    return o;
+  };
 
-  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  if (ngroups > 0) {
-    Ops x = load_x(xp, xs, xvalid);
-    Ops w0 = load_w(wp0, ws0);
-    Ops w1 = load_w(wp1, ws1);
-    for (int grp = 0; grp < ngroups; ++grp) {
-      Ops xn = x, w0n = w0, w1n = w1;
-      if (grp + 1 < ngroups) {  // next group's loads in flight during this group's MFMAs
-        const int64_t bo = (int64_t)(grp + 1) * kGroupBytes;
-        const int so = (grp + 1) * 16;
-        w0n = load_w(wp0 + bo, ws0 + so);
-        w1n = load_w(wp1 + bo, ws1 + so);
-        xn = load_x(xp + bo, xs + so, xvalid);
+  v16f acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  StageOps win[kWindow];
+#pragma unroll
+  for (int i = 0; i < kWindow; ++i)
+    if (i < sps) win[i] = load(i);
+  for (int i = 0; i < sps; i += kWindow) {
+#pragma unroll
+    for (int k = 0; k < kWindow; ++k) {
+      if (i + k < sps) {
+        const StageOps o = win[k];
+        if (i + k + kWindow < sps) win[k] = load(i + k + kWindow);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.w0, o.x0, acc, WF, XF, 0, o.ws, 0, o.xs);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.w1, o.x1, acc, WF, XF, 1, o.ws, 1, o.xs);
       }
-      acc0 = mfma_group<WF, XF>(acc0, w0, x);
-      acc1 = mfma_group<WF, XF>(acc1, w1, x);
-      x = xn;
-      w0 = w0n;
-      w1 = w1n;
     }
   }
 
-  // lane holds features nbase + 16 f + 4 q + (0..3) for token r16
-  if (r16 < g.M) {
-    float* part = g.partial + ((int64_t)split * 16 + r16) * g.N;
+  // lane (h, j) holds, for token j, features grp * 32 + 8a + 4h + b in register 4a + b
+  if (j < g.M) {
+    float* part = g.partial + ((int64_t)split * 16 + j) * g.N;
 #pragma unroll
-    for (int f = 0; f < kFragsPerWave; ++f) {
-      const v4f a = f == 0 ? acc0 : acc1;
-      const int n = nbase + 16 * f + 4 * q;
+    for (int a = 0; a < 4; ++a) {
+      const int n = grp * 32 + 8 * a + 4 * h;
+      const v4f v = v4f{acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
       if (n + 4 <= g.N && (g.N & 3) == 0) {
-        *reinterpret_cast<v4f*>(part + n) = a;
+        *reinterpret_cast<v4f*>(part + n) = v;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (n + i < g.N) part[n + i] = a[i];
+        for (int b = 0; b < 4; ++b)
+          if (n + b < g.N) part[n + b] = v[b];
       }
     }
   }
@@ -182,7 +147,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const SplitKArgs g) 
 }  // namespace
 
 hipError_t launch_gemm_splitk(const SplitKArgs& a, int x_fmt, int w_fmt, int out_kind, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.N + kWgFeatures - 1) / kWgFeatures), (unsigned)a.splits), block(kSkThreads);
+  const dim3 grid((unsigned)ceil_div(a.gw, kWgGroups), (unsigned)a.splits), block(kSkThreads);
   if (w_fmt == kFmtE2M3 && x_fmt == kFmtE2M3)
     hipLaunchKernelGGL((splitk_kernel<kFmtE2M3, kFmtE2M3>), grid, block, 0, stream, a);
   else if (w_fmt == kFmtE3M2 && x_fmt == kFmtE2M3)

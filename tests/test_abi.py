@@ -138,7 +138,7 @@ def test_splitk_validation(L):
     assert sk(m=17) == B.MX_ERR_SHAPE
     assert sk(splits=0) == B.MX_ERR_SHAPE
     assert sk(splits=3) == B.MX_ERR_UNSUPPORTED
-    assert sk(splits=16) == B.MX_ERR_UNSUPPORTED  # 256-element chunks
+    assert sk(splits=64) == B.MX_ERR_UNSUPPORTED  # 64-element chunks (not whole 128-element stages)
     assert sk(out_kind=2) == B.MX_ERR_FORMAT
     assert sk(ws_bytes=10) == B.MX_ERR_WORKSPACE
     assert sk(ws=NULL) == B.MX_ERR_WORKSPACE

@@ -180,14 +180,14 @@ def test_edge_shapes():
     assert not oc.any() and not os_.any()  # zero blocks: codes 0, scale byte 0
 
 
-@pytest.mark.parametrize("m", [8, 16, 5])
-@pytest.mark.parametrize("splits", [1, 4, 8])
+@pytest.mark.parametrize("m", [8, 16, 5, 1])
+@pytest.mark.parametrize("splits", [1, 4, 8, 32])
 @pytest.mark.parametrize("w_fmt", ["e3m2", "e2m3"])
 def test_splitk_small(m, splits, w_fmt):
-    n, k = 400, 4096
+    n, k = 400, 4096  # ragged N (12.5 groups of 32), 32 stages of 128
     a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", w_fmt, seed=31 + m)
     say(f"splitk m={m} n={n} k={k} S={splits} w={w_fmt}")
-    wq = _gpu_weights(w, w_fmt, qw, "rows")
+    wq = _gpu_weights(w, w_fmt, qw)
     o = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="bf16")
     o32 = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="f32")
     o_again = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="bf16")
@@ -202,10 +202,12 @@ def test_splitk_matches_plain_gemm_property():
     reorders the fp32 sum)."""
     m, n, k = 16, 256, 8192
     a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", "e3m2", seed=41)
-    wq = _gpu_weights(w, "e3m2", qw, "rows")
-    wt = _gpu_weights(w, "e3m2", qw, "tiled")
+    wq = _gpu_weights(w, "e3m2", qw)
+    wt = wq
     say("splitk vs plain")
+    aq = mx.mx_quantize(a.cuda(), "e2m3")  # pre-quantized activations too
     outs = [mx.mx_gemm_splitk(a.cuda(), wq, sp, out_kind="f32") for sp in (1, 2, 16)]
+    outs.append(mx.mx_gemm_splitk(aq, wq, 8, out_kind="f32"))
     plain = mx.mx_gemm(a.cuda(), wt, out_kind="f32")
     torch.cuda.synchronize()
     for o in outs + [plain]:

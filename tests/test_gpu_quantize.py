@@ -129,7 +129,7 @@ def test_workload_activations_and_weights(name):
     oracle checks a seeded sample of rows plus the first and last rows)."""
     w = syn.WORKLOADS[name]
     rng = np.random.default_rng(5)
-    layout = "rows" if name == "skinny" else "tiled"  # the split-K path reads the row-major layout
+    layout = "tiled"
     for which, fmt in (("a", "e2m3"), ("w", w.w_fmt)):
         t = syn.make_a(w) if which == "a" else syn.make_w(w)
         rows = np.unique(np.concatenate([[0, t.shape[0] - 1], rng.choice(t.shape[0], size=min(64, t.shape[0]), replace=False)]))
