@@ -16,8 +16,10 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,6 +36,13 @@ from microscaled_precision_gemm_amd import synthetic as syn  # noqa: E402
 METRIC = "MXFP6 GEMM TFLOPS + % of 10.1 PF MFMA peak (DiT MLP 20480x3072x12288)"
 PEAK_MXFP6_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
+
+# rocprofv3 names of the two GEMM instantiations (E2M3 x E2M3; fc1: MX out + GELU, fc2: bf16 out)
+KERNEL_NAMES = {"fc1": "gemm_kernel<2, 2, 2, true, 2>", "fc2": "gemm_kernel<2, 2, 1, false, 2>"}
+# the sources the GEMM kernel is built from: measured HBM traffic is only reported
+# while they are unchanged since the counters were taken
+GEMM_SOURCES = ["gemm_kernel.h", "internal.h", "mx_device.h", "gemm_we2m3_e2m3.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fc1_fc2_hbm_traffic.txt")
 
 
 def _events(n):
@@ -119,6 +128,42 @@ def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
             "hbm_frac": alg / ms / 1e6 / PEAK_HBM_GBS, "tflops": 2.0 * m * w.n * w.k / ms / 1e9}
 
 
+def gemm_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "microscaled_precision_gemm_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` ("fc1" / "fc2") from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same
+    counter's reading for a copy of known size), or None when the summary is
+    missing or the GEMM sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"^kernel_sources_sha256: ([0-9a-f]{64})$", text, re.M)
+    t = re.search(rf"^{kernel}_traffic_bytes_per_launch: (\d+)$", text, re.M)
+    if not m or not t or m.group(1) != gemm_sources_sha256():
+        return None
+    return int(t.group(1))
+
+
+def copy_calibration(mib: int = 1024, reps: int = 3):
+    """A plain device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (each copy reads and writes `mib` MiB once)."""
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_each_way": mib << 20, "reps": reps}
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The CPU oracle (as written, untuned) on a bounded sample of the step:
     the same MLP pass for a sample of token rows (weights quantized once,
@@ -159,6 +204,8 @@ def main():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skinny-iters", type=int, default=100)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = p.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
@@ -191,15 +238,18 @@ def main():
         "config": {"workload": "DiT MLP forward: quantize x, fc1 20480x3072x12288 (GELU-tanh -> E2M3), "
                                "fc2 20480x12288x3072 (bf16 out)",
                    "tokens": 20480, "d_model": 3072, "d_hidden": 12288, "frac_of_mxfp6_peak": round(value / PEAK_MXFP6_TFLOPS, 4)},
-        "roofline": {"bound": "mfma", "kernel": f"gemm_kernel ({dom})", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": f"{KERNEL_NAMES[dom]} ({dom})", "achieved": round(achieved, 1),
                      "peak": PEAK_MXFP6_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MXFP6_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(dom), "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes": r[f"{dom}_bytes"], "avg_launch_ms": round(dom_ms, 4)},
         "kernels_ms": {"quantize": round(r["quantize_ms"], 4), "fc1": round(r["fc1_ms"], 4), "fc2": round(r["fc2_ms"], 4),
                        "fc1_tflops": round(r["flops_per_gemm"] / r["fc1_ms"] / 1e9, 1),
                        "fc2_tflops": round(r["flops_per_gemm"] / r["fc2_ms"] / 1e9, 1),
                        "quantize_gb_s": round(r["quantize_bytes"] / r["quantize_ms"] / 1e6, 1)},
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
     }
+    if args.copy_calibration:
+        line["copy_calibration"] = copy_calibration()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cpu_baseline().items()}
     print(json.dumps(line), flush=True)
