@@ -40,14 +40,19 @@
  *   codes   [rows, 3K/4] bytes, row-major (row r is the packed row above);
  *   scales  [rows, K/32] bytes, row-major.
  *
- * MX_LAYOUT_TILED (the operand layout of both GEMMs and of the MX output): the matrix is
- * cut into stages of 128 K-elements (S = ceil(K/128)) and groups of 32 rows
- * (G = ceil(rows/32)).  Each (stage s, group g) pair owns
- *   codes   3072 bytes at offset (s*G + g) * 3072: 6 pieces of 512 bytes;
- *           piece p holds, for rows j = 0..31 of the group in turn, bytes
- *           [16p, 16p+16) of that row's 96-byte packed slice of K-elements
- *           [128s, 128s+128) (byte 16p+b of row 32g+j is at offset
- *           (s*G + g)*3072 + p*512 + j*16 + b);
+ * MX_LAYOUT_TILED (the operand layout of both GEMMs and of the MX output): the
+ * matrix is cut into stages of 128 K-elements (S = ceil(K/128)) and groups of
+ * 32 rows (G = ceil(rows/32)).  Each (stage s, group g) pair owns
+ *   codes   3072 bytes at offset (s*G + g) * 3072.  For each row j = 0..31 of
+ *           the group, the row's 96-byte packed slice of K-elements
+ *           [128s, 128s+128) is four 24-byte blocks q = 0..3.  Half h = 0, 1
+ *           of the chunk (bytes [1536h, 1536h+1536)) holds blocks 2h and 2h+1
+ *           of all 32 rows in four planes:
+ *             +0     plane A: bytes 0..15 of block 2h,   row j at j*16;
+ *             +512   plane L: bytes 16..23 of block 2h,  row j at j*8;
+ *             +768   plane H: bytes 0..7 of block 2h+1,  row j at j*8;
+ *             +1024  plane B: bytes 8..23 of block 2h+1, row j at j*16;
+ *           so each block of a row is one 16-byte and one 8-byte run;
  *   scales  128 bytes at offset (s*G + g) * 128: byte j*4 + q is the scale of
  *           block 4s+q of row 32g+j.
  *   Rows >= rows and blocks >= K/32 are padding: codes 0, scale byte 127.

@@ -12,17 +12,19 @@
 //  * K advances in stages of 128.  In the tiled layout one stage of 256 rows
 //    is a contiguous 24 KB run, so each stage is brought in by
 //    global_load_lds_dwordx4 copies straight into LDS (no VGPR staging), into
-//    a ring of 3 stages: two stages are in flight while the third is
-//    consumed.  The waits on those copies are explicit (s_waitcnt vmcnt) and
-//    the barrier is a bare s_barrier, so a stage only waits for its own data.
-//    The copies are issued one after every second MFMA of the current stage,
-//    so the address path and the matrix cores work side by side.
+//    a ring of 3 slots.  The waits on those copies are explicit (s_waitcnt
+//    vmcnt) and the barrier is a bare s_barrier, so a stage only waits for its
+//    own data.
 //  * Inside a stage, lane half h of sub-step s handles K-block 2h + s (the K
-//    order inside one accumulation is free as long as both operands agree):
-//    each lane reads 3 consecutive 16-byte pieces (48 bytes) and a 16-bit
-//    scale pair; op_sel = s picks the byte.  The tiled layout stores piece p
-//    of a 32-row group contiguously, so the 32 lanes of a half read 512
-//    consecutive bytes (no LDS bank conflicts from row strides).
+//    order inside one accumulation is free as long as both operands agree).
+//    The layout's planes make each sub-step operand one 16-byte and one
+//    8-byte LDS read into adjacent registers, conflict-free (the 32 lanes of a
+//    half read 512 or 256 consecutive bytes), with one 16-bit scale pair per
+//    fragment; op_sel = s picks the byte.
+//  * Operand registers are double buffered per half stage: the MFMAs of one
+//    sub-step run while the operands of the next are read from LDS, and the
+//    copies of stage ks+3 are interleaved one per MFMA into the slot stage ks
+//    came from, so the LDS, the address path and the matrix cores overlap.
 //  * W is the MFMA A operand (output rows = features n), the activations the
 //    B operand (columns = tokens m), so each lane's 16 accumulators belong to
 //    one token.  The W rows fed to the A operand are permuted so that a lane
@@ -167,18 +169,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     for (int i = 0; i < kCopiesPerStage; ++i) issue_one(i, ks, slot);
   };
 
-  // ---- per-lane LDS read offsets for the MFMA operands
+  // ---- per-lane LDS bases in ring slot 0; fragment f (32 rows) adds
+  // f * kChunkCodes.  Half h of a chunk holds this lane's blocks 2h (sub-step
+  // 0: plane A + plane L) and 2h+1 (sub-step 1: plane H + plane B).
   const int wn = wave & 1, wm = wave >> 1;
   const int h = lane >> 5, j = lane & 31;
   const int wrow = feature_of_row<kLayout>(j);
-  int w_off[4], x_off[4], ws_off[4], xs_off[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    w_off[f] = kOffW + (wn * 4 + f) * kChunkCodes + 3 * h * 512 + wrow * 16;
-    x_off[f] = kOffX + (wm * 4 + f) * kChunkCodes + 3 * h * 512 + j * 16;
-    ws_off[f] = kOffWs + (wn * 4 + f) * kChunkScales + wrow * 4 + 2 * h;
-    xs_off[f] = kOffXs + (wm * 4 + f) * kChunkScales + j * 4 + 2 * h;
-  }
+  const int w16 = kOffW + wn * 4 * kChunkCodes + h * kHalfBytes + wrow * 16;
+  const int x16 = kOffX + wm * 4 * kChunkCodes + h * kHalfBytes + j * 16;
+  const int w8 = kOffW + wn * 4 * kChunkCodes + h * kHalfBytes + wrow * 8;
+  const int x8 = kOffX + wm * 4 * kChunkCodes + h * kHalfBytes + j * 8;
+  const int wsc = kOffWs + wn * 4 * kChunkScales + wrow * 4 + 2 * h;
+  const int xsc = kOffXs + wm * 4 * kChunkScales + j * 4 + 2 * h;
 
   v16f acc[4][4];
 #pragma unroll
@@ -188,103 +190,178 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fn][fm][r] = 0.0f;
 
-  // pieces 3h, 3h+1, 3h+2 of a row (48 bytes) -> the 6-dword operands of sub-steps 0 and 1
-  auto read_operands = [](const uint8_t* p, v8i& s0, v8i& s1) {
-    const u32x4 d0 = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 d1 = *reinterpret_cast<const u32x4*>(p + 512);
-    const u32x4 d2 = *reinterpret_cast<const u32x4*>(p + 1024);
-    s0 = v8i{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], 0, 0};
-    s1 = v8i{(int)d1[2], (int)d1[3], (int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3], 0, 0};
+  // One sub-step operand is a 16-byte and an 8-byte LDS read landing in
+  // adjacent registers (the MFMA reads 6 of the 8).  The 8-byte reads are
+  // volatile so they are not fused into one 16-byte read whose halves would
+  // belong to different operands (that costs register moves).
+  typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2_t;
+  auto rd16 = [&](int off) { return *reinterpret_cast<const u32x4*>(lds + off); };
+  auto rd8 = [&](int off) { return (u32x2)(*(lds_u32x2_t*)(lds + off)); };
+  auto op0 = [&](int b16, int b8) {
+    const u32x4 a = rd16(b16 + kPlaneA);
+    const u32x2 c = rd8(b8 + kPlaneL);
+    return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], 0, 0};
   };
-
-  // One stage: read this lane's operands, then 32 MFMAs.  With COPY, the 14
-  // copies of a later stage are interleaved one after every second MFMA: the
-  // vector-memory address path then works beside the matrix cores instead of
-  // holding up the first MFMAs of the stage behind a burst of copies.
-  auto compute = [&](auto copy_tag, int slot, int ks2, int slot2) {
-    constexpr bool COPY = decltype(copy_tag)::value;
-    const uint8_t* st = lds + slot * kSlotBytes;
-    v8i wa0, wa1, wb0, wb1, wc0, wc1, wd0, wd1;
-    v8i xa0, xa1, xb0, xb1, xc0, xc1, xd0, xd1;
-    read_operands(st + w_off[0], wa0, wa1);
-    read_operands(st + x_off[0], xa0, xa1);
-    read_operands(st + w_off[1], wb0, wb1);
-    read_operands(st + x_off[1], xb0, xb1);
-    read_operands(st + w_off[2], wc0, wc1);
-    read_operands(st + x_off[2], xc0, xc1);
-    read_operands(st + w_off[3], wd0, wd1);
-    read_operands(st + x_off[3], xd0, xd1);
-    const int ws0 = *reinterpret_cast<const uint16_t*>(st + ws_off[0]);
-    const int ws1 = *reinterpret_cast<const uint16_t*>(st + ws_off[1]);
-    const int ws2 = *reinterpret_cast<const uint16_t*>(st + ws_off[2]);
-    const int ws3 = *reinterpret_cast<const uint16_t*>(st + ws_off[3]);
-    const int xs0 = *reinterpret_cast<const uint16_t*>(st + xs_off[0]);
-    const int xs1 = *reinterpret_cast<const uint16_t*>(st + xs_off[1]);
-    const int xs2 = *reinterpret_cast<const uint16_t*>(st + xs_off[2]);
-    const int xs3 = *reinterpret_cast<const uint16_t*>(st + xs_off[3]);
-#define MXG_MFMA(FN, FM, W, X, WS, XS, S) \
-  acc[FN][FM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(W, X, acc[FN][FM], WF, XF, S, WS, S, XS)
-#define MXG_COPY(I) \
-  if constexpr (COPY && (I) < kCopiesPerStage) issue_one(I, ks2, slot2)
-#define MXG_ROW(FN, W, WS, S, I0)                                                   \
-  MXG_MFMA(FN, 0, W, xa##S, WS, xs0, S);                                           \
-  MXG_MFMA(FN, 1, W, xb##S, WS, xs1, S);                                           \
-  MXG_COPY(I0);                                                                    \
-  MXG_MFMA(FN, 2, W, xc##S, WS, xs2, S);                                           \
-  MXG_MFMA(FN, 3, W, xd##S, WS, xs3, S);                                           \
-  MXG_COPY(I0 + 1)
-    MXG_ROW(0, wa0, ws0, 0, 0);
-    MXG_ROW(1, wb0, ws1, 0, 2);
-    MXG_ROW(2, wc0, ws2, 0, 4);
-    MXG_ROW(3, wd0, ws3, 0, 6);
-    MXG_ROW(0, wa1, ws0, 1, 8);
-    MXG_ROW(1, wb1, ws1, 1, 10);
-    MXG_ROW(2, wc1, ws2, 1, 12);
-    MXG_ROW(3, wd1, ws3, 1, 14);
-#undef MXG_ROW
-#undef MXG_COPY
-#undef MXG_MFMA
-    if constexpr (COPY) {
-      // all LDS reads first, then {2 MFMA, 1 copy} x 14, then the last 4 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);
+  auto op1 = [&](int b16, int b8) {
+    const u32x2 c = rd8(b8 + kPlaneH);
+    const u32x4 a = rd16(b16 + kPlaneB);
+    return v8i{(int)c[0], (int)c[1], (int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0};
+  };
+  struct Half {  // one sub-step's operands: 4 weight and 4 activation fragments
+    v8i w0, w1, w2, w3, x0, x1, x2, x3;
+  };
+  struct Scales {  // scale byte pairs (blocks 2h, 2h+1) of the 8 fragments
+    int w0, w1, w2, w3, x0, x1, x2, x3;
+  };
+  auto read_half = [&](int sl, auto sub_tag) {
+    constexpr int SUB = decltype(sub_tag)::value;
+    const int so = sl * kSlotBytes;
+    auto op = [&](int b16, int b8, int f) {
+      return SUB == 0 ? op0(so + b16 + f * kChunkCodes, so + b8 + f * kChunkCodes)
+                      : op1(so + b16 + f * kChunkCodes, so + b8 + f * kChunkCodes);
+    };
+    Half r;
+    r.w0 = op(w16, w8, 0);
+    r.x0 = op(x16, x8, 0);
+    r.w1 = op(w16, w8, 1);
+    r.x1 = op(x16, x8, 1);
+    r.w2 = op(w16, w8, 2);
+    r.x2 = op(x16, x8, 2);
+    r.w3 = op(w16, w8, 3);
+    r.x3 = op(x16, x8, 3);
+    return r;
+  };
+  auto scale_at = [&](int so, int base, int f) {
+    return (int)*reinterpret_cast<const uint16_t*>(lds + so + base + f * kChunkScales);
+  };
+  auto read_scales = [&](int sl) {
+    const int so = sl * kSlotBytes;
+    Scales c;
+    c.w0 = scale_at(so, wsc, 0);
+    c.w1 = scale_at(so, wsc, 1);
+    c.w2 = scale_at(so, wsc, 2);
+    c.w3 = scale_at(so, wsc, 3);
+    c.x0 = scale_at(so, xsc, 0);
+    c.x1 = scale_at(so, xsc, 1);
+    c.x2 = scale_at(so, xsc, 2);
+    c.x3 = scale_at(so, xsc, 3);
+    return c;
+  };
+#define MXG_MFMA(FN, FM, S) \
+  acc[FN][FM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(r.w##FN, r.x##FM, acc[FN][FM], WF, XF, S, c.w##FN, S, c.x##FM)
+  // the 16 MFMAs of one sub-step
+  auto mfmas = [&](const Half& r, const Scales& c, auto sub_tag) {
+    constexpr int S = decltype(sub_tag)::value;
+    MXG_MFMA(0, 0, S); MXG_MFMA(0, 1, S); MXG_MFMA(0, 2, S); MXG_MFMA(0, 3, S);
+    MXG_MFMA(1, 0, S); MXG_MFMA(1, 1, S); MXG_MFMA(1, 2, S); MXG_MFMA(1, 3, S);
+    MXG_MFMA(2, 0, S); MXG_MFMA(2, 1, S); MXG_MFMA(2, 2, S); MXG_MFMA(2, 3, S);
+    MXG_MFMA(3, 0, S); MXG_MFMA(3, 1, S); MXG_MFMA(3, 2, S); MXG_MFMA(3, 3, S);
+  };
+  // Steady-state phase 1 written in issue order (the LDS reads and the copies
+  // into LDS keep their program order): per MFMA one operand (or two scale)
+  // reads of the next stage and one copy of stage ks2 into slot slot2.
+  auto phase1 = [&](const Half& r, const Scales& c, int ks2, int slot2, int nsl, Half& nr, Scales& ns) {
+    const int so = nsl * kSlotBytes;
+#define MXG_RD(DST, B16, B8, F) nr.DST = op0(so + B16 + (F) * kChunkCodes, so + B8 + (F) * kChunkCodes)
+    MXG_MFMA(0, 0, 1); MXG_RD(w0, w16, w8, 0); issue_one(0, ks2, slot2);
+    MXG_MFMA(0, 1, 1); MXG_RD(x0, x16, x8, 0); issue_one(1, ks2, slot2);
+    MXG_MFMA(0, 2, 1); MXG_RD(w1, w16, w8, 1); issue_one(2, ks2, slot2);
+    MXG_MFMA(0, 3, 1); MXG_RD(x1, x16, x8, 1); issue_one(3, ks2, slot2);
+    MXG_MFMA(1, 0, 1); MXG_RD(w2, w16, w8, 2); issue_one(4, ks2, slot2);
+    MXG_MFMA(1, 1, 1); MXG_RD(x2, x16, x8, 2); issue_one(5, ks2, slot2);
+    MXG_MFMA(1, 2, 1); MXG_RD(w3, w16, w8, 3); issue_one(6, ks2, slot2);
+    MXG_MFMA(1, 3, 1); MXG_RD(x3, x16, x8, 3); issue_one(7, ks2, slot2);
+    MXG_MFMA(2, 0, 1); ns.w0 = scale_at(so, wsc, 0); ns.w1 = scale_at(so, wsc, 1); issue_one(8, ks2, slot2);
+    MXG_MFMA(2, 1, 1); ns.w2 = scale_at(so, wsc, 2); ns.w3 = scale_at(so, wsc, 3); issue_one(9, ks2, slot2);
+    MXG_MFMA(2, 2, 1); ns.x0 = scale_at(so, xsc, 0); ns.x1 = scale_at(so, xsc, 1); issue_one(10, ks2, slot2);
+    MXG_MFMA(2, 3, 1); ns.x2 = scale_at(so, xsc, 2); ns.x3 = scale_at(so, xsc, 3); issue_one(11, ks2, slot2);
+    MXG_MFMA(3, 0, 1); issue_one(12, ks2, slot2);
+    MXG_MFMA(3, 1, 1); issue_one(13, ks2, slot2);
+    MXG_MFMA(3, 2, 1);
+    MXG_MFMA(3, 3, 1);
+#undef MXG_RD
+    // pin that order for the scheduler: {MFMA, 2 LDS reads, copy} x 12,
+    // {MFMA, copy} x 2, then 2 MFMAs
 #pragma unroll
-      for (int i = 0; i < kCopiesPerStage; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 32 - 2 * kCopiesPerStage, 0);
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+#undef MXG_MFMA
+  static_assert(kCopiesPerStage == 14, "phase 1 interleaves exactly 14 copies");
+  // phase 0 order: {MFMA, LDS read} x 16
+  auto pattern0 = []() {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  using with_copies = std::integral_constant<bool, true>;
-  using no_copies = std::integral_constant<bool, false>;
+  auto next_slot = [](int sl) { return sl == 2 ? 0 : sl + 1; };
+  using sub0 = std::integral_constant<int, 0>;
+  using sub1 = std::integral_constant<int, 1>;
 
-  // ---- main loop over the ring.  At the top of step ks the copies of stages
-  // ks and ks+1 are in flight; waiting until at most one stage's copies are
-  // outstanding (they complete in order) means stage ks has landed, and the
-  // barrier makes every wave's part of it visible and retires the reads of the
-  // slot that stage ks+2 is about to overwrite.  The last two steps are peeled
-  // so the steady-state body is one basic block.
+  // ---- main loop over the 3-slot ring, with the operand registers double
+  // buffered at half-stage granularity.  At the top of stage ks the lane holds
+  // stage ks's sub-step 0 operands (ra) and scales (sc); copies of stages ks+1
+  // and ks+2 are in flight.  Phase 0: sub-step 0 MFMAs while reading stage
+  // ks's sub-step 1 operands (rb).  Then wait until at most one stage's copies
+  // are outstanding (they complete in order: stage ks+1 has landed), and
+  // barrier: every wave's part of stage ks+1 is visible and every wave is done
+  // reading slot ks.  Phase 1: sub-step 1 MFMAs while reading stage ks+1's
+  // sub-step 0 operands and scales, and copying stage ks+3 into slot ks.
   if (nk > 0) issue(0, 0);
   if (nk > 1) issue(1, 1);
-  int ks = 0, slot = 0;
-  for (; ks + 2 < nk; ++ks) {
+  if (nk > 2) issue(2, 2);
+  if (nk > 2)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kCopiesPerStage));
+  else if (nk > 1)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
-    __builtin_amdgcn_s_barrier();
-    compute(with_copies{}, slot, ks + 2, slot == 0 ? 2 : slot - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    slot = slot == 2 ? 0 : slot + 1;
-  }
-  if (ks + 1 < nk) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
-    __builtin_amdgcn_s_barrier();
-    compute(no_copies{}, slot, 0, 0);
-    slot = slot == 2 ? 0 : slot + 1;
-    ++ks;
-  }
-  if (ks < nk) {
+  else
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __builtin_amdgcn_s_barrier();
+  Half ra = read_half(0, sub0{});
+  Scales sc = read_scales(0);
+  int ks = 0, slot = 0;
+  for (; ks + 3 < nk; ++ks) {
+    const Half rb = read_half(slot, sub1{});
+    mfmas(ra, sc, sub0{});
+    pattern0();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
     __builtin_amdgcn_s_barrier();
-    compute(no_copies{}, slot, 0, 0);
+    const int nsl = next_slot(slot);
+    Scales sn;
+    phase1(rb, sc, ks + 3, slot, nsl, ra, sn);
+    __builtin_amdgcn_sched_barrier(0);
+    sc = sn;
+    slot = nsl;
+  }
+  // the last (up to) three stages: no more copies
+  for (; ks < nk; ++ks) {
+    const Half rb = read_half(slot, sub1{});
+    mfmas(ra, sc, sub0{});
+    Scales sn = sc;
+    const int nsl = next_slot(slot);
+    if (ks + 1 < nk) {
+      if (ks + 2 < nk)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      __builtin_amdgcn_s_barrier();
+      ra = read_half(nsl, sub0{});
+      sn = read_scales(nsl);
+    }
+    mfmas(rb, sc, sub1{});
+    sc = sn;
+    slot = nsl;
   }
 
   // ---- epilogue
@@ -326,12 +403,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
             q = v6u{0, 0, 0, 0, 0, 0};
             sbyte = 127u;
           }
-          uint8_t* chunk = static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes;
-          const int o = 24 * qb + 12 * h;  // this lane's 12 bytes of the row's 96-byte slice
+          // this lane's 12 code bytes are bytes [12h, 12h+12) of block qb of
+          // row j; each dword lies in one plane of half qb/2 of the chunk
+          uint8_t* half = static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes +
+                          (qb >> 1) * kHalfBytes;
 #pragma unroll
           for (int d = 0; d < 3; ++d) {
-            const int od4 = o + 4 * d;
-            *reinterpret_cast<uint32_t*>(chunk + (od4 >> 4) * 512 + j * 16 + (od4 & 15)) = q[d];
+            const int t = 12 * h + 4 * d;
+            int off;
+            if ((qb & 1) == 0)
+              off = t < 16 ? kPlaneA + j * 16 + t : kPlaneL + j * 8 + (t - 16);
+            else
+              off = t < 8 ? kPlaneH + j * 8 + t : kPlaneB + j * 16 + (t - 8);
+            *reinterpret_cast<uint32_t*>(half + off) = q[d];
           }
           if (h == 0)
             g.out_scales[((int64_t)stage * g.gx + gm) * kChunkScales + j * 4 + qb] = (uint8_t)sbyte;

@@ -22,6 +22,14 @@ constexpr int kTileStageK = 128;
 constexpr int kTileGroupRows = 32;
 constexpr int kChunkCodes = 3072;
 constexpr int kChunkScales = 128;
+// Planes of one half (blocks 2h and 2h+1 of a stage, 32 rows) of a tiled chunk:
+// A = bytes 0..15 of block 2h (16 per row), L = its bytes 16..23 (8 per row),
+// H = bytes 0..7 of block 2h+1 (8 per row), B = its bytes 8..23 (16 per row).
+constexpr int kHalfBytes = 1536;
+constexpr int kPlaneA = 0;
+constexpr int kPlaneL = 512;
+constexpr int kPlaneH = 768;
+constexpr int kPlaneB = 1024;
 
 constexpr int kEpiNone = 0;
 constexpr int kEpiGeluTanh = 1;

@@ -134,10 +134,10 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint8_t* __re
 // ---- tiled layout: one wave per (stage, 32-row group) chunk of 32 rows x 128
 // elements.  Loads: 256 (bf16) or 512 (fp32) contiguous bytes per row, 16 per
 // lane, consecutive lanes on consecutive bytes.  Each lane then converts two
-// blocks of one row (blocks 2h, 2h+1 for lane half h), whose 48 code bytes are
-// exactly pieces 3h .. 3h+2 of that row in the chunk: the 32 lanes of a half
-// write 3 runs of 512 contiguous bytes.  Rows >= rows and blocks >= K/32 are
-// written as padding (codes 0, scale 127).
+// blocks of one row (blocks 2h, 2h+1 for lane half h), whose 48 code bytes
+// fill that row's entries of the four planes of half h: the 32 lanes of a half
+// write runs of 512, 256, 256 and 512 contiguous bytes.  Rows >= rows and
+// blocks >= K/32 are written as padding (codes 0, scale 127).
 constexpr int kTWaves = 4;
 
 template <bool F32>
@@ -237,11 +237,12 @@ __global__ __launch_bounds__(kTWaves * 64) void quantize_tiled_kernel(const uint
     q[t] = r;
     sb[t] = byte;
   }
-  // 48 code bytes = pieces 3h, 3h+1, 3h+2 of row j
-  uint8_t* out = codes + (int64_t)chunk * kChunkCodes + 3 * h * 512 + j * 16;
-  *reinterpret_cast<u32x4*>(out) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
-  *reinterpret_cast<u32x4*>(out + 512) = u32x4{q[0][4], q[0][5], q[1][0], q[1][1]};
-  *reinterpret_cast<u32x4*>(out + 1024) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
+  // the 48 code bytes of row j in the planes of half h
+  uint8_t* half = codes + (int64_t)chunk * kChunkCodes + h * kHalfBytes;
+  *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
+  *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
+  *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
+  *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
   *reinterpret_cast<uint16_t*>(scales + (int64_t)chunk * kChunkScales + j * 4 + 2 * h) =
       (uint16_t)(sb[0] | (sb[1] << 8));
 }

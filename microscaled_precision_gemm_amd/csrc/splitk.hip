@@ -9,8 +9,9 @@
 //
 //  * Both operands are in the tiled MX layout.  A wave owns one 32-feature
 //    group of the weights and one K-chunk; per 128-element stage each lane
-//    loads 3 x 16 bytes of its row (pieces 3h .. 3h+2), so every load
-//    instruction reads two runs of 512 contiguous bytes.
+//    loads its row's entries of the four planes of half h (16 + 8 + 8 + 16
+//    bytes), so every load instruction reads two contiguous runs of 512 or
+//    256 bytes.
 //  * V_MFMA_SCALE_F32_32X32X64_F8F6F4 with the weights as the A operand and
 //    the tokens as the B operand; token rows 16..31 are layout padding (zero
 //    codes), so M = 8 or 16 costs no extra weight bytes and no branches.
@@ -36,9 +37,29 @@ struct StageOps {
   int ws, xs;          // scale pairs (bytes 2h, 2h+1 of the lane's row)
 };
 
-__device__ __forceinline__ void split_pieces(const u32x4 d0, const u32x4 d1, const u32x4 d2, v8i& s0, v8i& s1) {
-  s0 = v8i{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], 0, 0};
-  s1 = v8i{(int)d1[2], (int)d1[3], (int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3], 0, 0};
+// The two sub-step operands of lane (h, j) from the planes of half h of a
+// chunk: block 2h = plane A + plane L, block 2h+1 = plane H + plane B.
+template <bool NT>
+__device__ __forceinline__ void load_ops(const uint8_t* half, int j, v8i& s0, v8i& s1) {
+  const u32x4* pa = reinterpret_cast<const u32x4*>(half + kPlaneA + j * 16);
+  const u32x2* pl = reinterpret_cast<const u32x2*>(half + kPlaneL + j * 8);
+  const u32x2* ph = reinterpret_cast<const u32x2*>(half + kPlaneH + j * 8);
+  const u32x4* pb = reinterpret_cast<const u32x4*>(half + kPlaneB + j * 16);
+  u32x4 a, b;
+  u32x2 l, hh;
+  if constexpr (NT) {
+    a = __builtin_nontemporal_load(pa);
+    l = __builtin_nontemporal_load(pl);
+    hh = __builtin_nontemporal_load(ph);
+    b = __builtin_nontemporal_load(pb);
+  } else {
+    a = *pa;
+    l = *pl;
+    hh = *ph;
+    b = *pb;
+  }
+  s0 = v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)l[0], (int)l[1], 0, 0};
+  s1 = v8i{(int)hh[0], (int)hh[1], (int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0};
 }
 
 // grid: (ceil(N / 128), splits).  Wave w: weight group blockIdx.x * 4 + w, K-chunk blockIdx.y.
@@ -51,7 +72,7 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
   const int split = blockIdx.y;
   const int sps = g.K / kTileStageK / g.splits;  // stages per split
   const int s0 = split * sps;
-  const int lane_off = 3 * h * 512 + j * 16;
+  const int lane_off = h * kHalfBytes;
   const int scale_off = j * 4 + 2 * h;
   const uint8_t* wc = g.w_codes + ((int64_t)s0 * g.gw + grp) * kChunkCodes + lane_off;
   const uint8_t* ws = g.w_scales + ((int64_t)s0 * g.gw + grp) * kChunkScales + scale_off;
@@ -61,11 +82,8 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
 
   auto load = [&](int i) {
     StageOps o;
-    const u32x4* wp = reinterpret_cast<const u32x4*>(wc + i * w_step);
-    const u32x4* xp = reinterpret_cast<const u32x4*>(xc + (int64_t)i * kChunkCodes);
-    split_pieces(__builtin_nontemporal_load(wp), __builtin_nontemporal_load(wp + 32), __builtin_nontemporal_load(wp + 64),
-                 o.w0, o.w1);
-    split_pieces(xp[0], xp[32], xp[64], o.x0, o.x1);
+    load_ops<true>(wc + i * w_step, j, o.w0, o.w1);
+    load_ops<false>(xc + (int64_t)i * kChunkCodes, j, o.x0, o.x1);
     o.ws = *reinterpret_cast<const uint16_t*>(ws + i * ws_step);
     o.xs = *reinterpret_cast<const uint16_t*>(xs + (int64_t)i * kChunkScales);
     return o;

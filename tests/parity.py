@@ -30,14 +30,35 @@ def oracle_mx(x64: np.ndarray, fmt: str):
     return codes, scales, O.dequantize(codes, scales, fmt)
 
 
+def tiled_chunk_offsets() -> np.ndarray:
+    """offsets[j, b]: where byte b (0..95) of row j's 96-byte packed slice of a
+    128-element stage sits inside its 3072-byte tiled chunk.  Half h (blocks 2h
+    and 2h+1) owns bytes [1536h, 1536h+1536): plane A (bytes 0..15 of block 2h,
+    16 per row), plane L (its bytes 16..23, 8 per row), plane H (bytes 0..7 of
+    block 2h+1, 8 per row), plane B (its bytes 8..23, 16 per row)."""
+    off = np.empty((32, 96), dtype=np.int64)
+    for j in range(32):
+        for b in range(96):
+            q, t = divmod(b, 24)
+            base = (q >> 1) * 1536
+            if q % 2 == 0:
+                off[j, b] = base + (j * 16 + t if t < 16 else 512 + j * 8 + (t - 16))
+            else:
+                off[j, b] = base + (768 + j * 8 + t if t < 8 else 1024 + j * 16 + (t - 8))
+    return off
+
+
+_CHUNK_OFFSETS = tiled_chunk_offsets()
+
+
 def tiled_to_rows(codes_t: np.ndarray, scales_t: np.ndarray, rows: int, k: int):
     """Rearrange the tiled MX layout (128-element stages x 32-row groups, as the
     library's header defines it) into row-major packed codes [rows, 3k/4] and
     scales [rows, k/32].  Also returns the padding (codes and scale bytes of
     rows >= rows or blocks >= k/32), which must be 0 and 127."""
     stages, groups = -(-k // 128), -(-rows // 32)
-    c = np.asarray(codes_t).reshape(stages, groups, 6, 32, 16)   # [stage, group, piece, row, byte]
-    c = c.transpose(1, 3, 0, 2, 4).reshape(groups * 32, stages * 96)
+    c = np.asarray(codes_t).reshape(stages, groups, 3072)[:, :, _CHUNK_OFFSETS]  # [stage, group, row, byte]
+    c = c.transpose(1, 2, 0, 3).reshape(groups * 32, stages * 96)
     s = np.asarray(scales_t).reshape(stages, groups, 32, 4)       # [stage, group, row, block]
     s = s.transpose(1, 2, 0, 3).reshape(groups * 32, stages * 4)
     pad_c = np.concatenate([c[rows:].ravel(), c[:rows, 3 * k // 4:].ravel()])
