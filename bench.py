@@ -49,6 +49,20 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
+SETTLE_S = 0.5
+
+
+def settle(fn, seconds: float = SETTLE_S):
+    """Run `fn` untimed for about `seconds` before the warm-up steps: from idle
+    the GPU takes tens of milliseconds of sustained load to reach its steady
+    clocks, so the first GEMMs after setup run up to ~20 % slower."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def bench_mlp(steps: int, warmup: int):
     fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
     m, d, hdim = fc1.m, fc1.k, fc1.n
@@ -74,6 +88,7 @@ def bench_mlp(steps: int, warmup: int):
         if ev is not None:
             ev[3].record()
 
+    settle(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -112,9 +127,13 @@ def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
     del wb
     out = torch.empty((m, w.n), dtype=torch.bfloat16, device=dev)
     work = torch.empty(mx.mx_gemm_workspace_size(m, w.n, w.k, True, splits), dtype=torch.uint8, device=dev)
-    for i in range(5):
-        mx.mx_gemm_splitk(a, ws[i % copies], splits, out=out, workspace=work)
-    torch.cuda.synchronize()
+    it = [0]
+
+    def call():
+        mx.mx_gemm_splitk(a, ws[it[0] % copies], splits, out=out, workspace=work)
+        it[0] += 1
+
+    settle(call, 0.2)
     e0, e1 = _events(2)
     e0.record()
     for i in range(iters):

@@ -257,71 +257,108 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     MXG_MFMA(2, 0, S); MXG_MFMA(2, 1, S); MXG_MFMA(2, 2, S); MXG_MFMA(2, 3, S);
     MXG_MFMA(3, 0, S); MXG_MFMA(3, 1, S); MXG_MFMA(3, 2, S); MXG_MFMA(3, 3, S);
   };
-  // Steady-state phase 1 written in issue order (the LDS reads and the copies
-  // into LDS keep their program order): per MFMA one operand (or two scale)
-  // reads of the next stage and one copy of stage ks2 into slot slot2.
+  // The steady-state phases, written in issue order (the LDS reads and the
+  // copies into LDS keep their program order).  Each stage's 14 copies are
+  // split: copies 0..6 of stage ks+3 go out in phase 1 of stage ks (into the
+  // slot stage ks has just been read from), copies 7..13 in phase 0 of stage
+  // ks+1, so the vector-memory path sees 7 copies per 16 MFMAs throughout.
+  // Phase 1: sub-step 1 MFMAs, reads of the next stage's sub-step 0 operands
+  // and scales, first half of stage ks2's copies into slot slot2.
   auto phase1 = [&](const Half& r, const Scales& c, int ks2, int slot2, int nsl, Half& nr, Scales& ns) {
     const int so = nsl * kSlotBytes;
 #define MXG_RD(DST, B16, B8, F) nr.DST = op0(so + B16 + (F) * kChunkCodes, so + B8 + (F) * kChunkCodes)
     MXG_MFMA(0, 0, 1); MXG_RD(w0, w16, w8, 0); issue_one(0, ks2, slot2);
-    MXG_MFMA(0, 1, 1); MXG_RD(x0, x16, x8, 0); issue_one(1, ks2, slot2);
-    MXG_MFMA(0, 2, 1); MXG_RD(w1, w16, w8, 1); issue_one(2, ks2, slot2);
-    MXG_MFMA(0, 3, 1); MXG_RD(x1, x16, x8, 1); issue_one(3, ks2, slot2);
-    MXG_MFMA(1, 0, 1); MXG_RD(w2, w16, w8, 2); issue_one(4, ks2, slot2);
-    MXG_MFMA(1, 1, 1); MXG_RD(x2, x16, x8, 2); issue_one(5, ks2, slot2);
-    MXG_MFMA(1, 2, 1); MXG_RD(w3, w16, w8, 3); issue_one(6, ks2, slot2);
-    MXG_MFMA(1, 3, 1); MXG_RD(x3, x16, x8, 3); issue_one(7, ks2, slot2);
-    MXG_MFMA(2, 0, 1); ns.w0 = scale_at(so, wsc, 0); ns.w1 = scale_at(so, wsc, 1); issue_one(8, ks2, slot2);
-    MXG_MFMA(2, 1, 1); ns.w2 = scale_at(so, wsc, 2); ns.w3 = scale_at(so, wsc, 3); issue_one(9, ks2, slot2);
-    MXG_MFMA(2, 2, 1); ns.x0 = scale_at(so, xsc, 0); ns.x1 = scale_at(so, xsc, 1); issue_one(10, ks2, slot2);
-    MXG_MFMA(2, 3, 1); ns.x2 = scale_at(so, xsc, 2); ns.x3 = scale_at(so, xsc, 3); issue_one(11, ks2, slot2);
-    MXG_MFMA(3, 0, 1); issue_one(12, ks2, slot2);
-    MXG_MFMA(3, 1, 1); issue_one(13, ks2, slot2);
+    MXG_MFMA(0, 1, 1); MXG_RD(x0, x16, x8, 0);
+    MXG_MFMA(0, 2, 1); MXG_RD(w1, w16, w8, 1); issue_one(1, ks2, slot2);
+    MXG_MFMA(0, 3, 1); MXG_RD(x1, x16, x8, 1);
+    MXG_MFMA(1, 0, 1); MXG_RD(w2, w16, w8, 2); issue_one(2, ks2, slot2);
+    MXG_MFMA(1, 1, 1); MXG_RD(x2, x16, x8, 2);
+    MXG_MFMA(1, 2, 1); MXG_RD(w3, w16, w8, 3); issue_one(3, ks2, slot2);
+    MXG_MFMA(1, 3, 1); MXG_RD(x3, x16, x8, 3);
+    MXG_MFMA(2, 0, 1); ns.w0 = scale_at(so, wsc, 0); ns.w1 = scale_at(so, wsc, 1); issue_one(4, ks2, slot2);
+    MXG_MFMA(2, 1, 1); ns.w2 = scale_at(so, wsc, 2); ns.w3 = scale_at(so, wsc, 3);
+    MXG_MFMA(2, 2, 1); ns.x0 = scale_at(so, xsc, 0); ns.x1 = scale_at(so, xsc, 1); issue_one(5, ks2, slot2);
+    MXG_MFMA(2, 3, 1); ns.x2 = scale_at(so, xsc, 2); ns.x3 = scale_at(so, xsc, 3);
+    MXG_MFMA(3, 0, 1); issue_one(6, ks2, slot2);
+    MXG_MFMA(3, 1, 1);
     MXG_MFMA(3, 2, 1);
     MXG_MFMA(3, 3, 1);
-#undef MXG_RD
-    // pin that order for the scheduler: {MFMA, 2 LDS reads, copy} x 12,
-    // {MFMA, copy} x 2, then 2 MFMAs
+    // pin that order for the scheduler
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+#undef MXG_RD
+  };
+  // phase 0 with the second half (copies 7..13) of stage ks2 interleaved
+  auto phase0 = [&](const Half& r, const Scales& c, int sl, Half& nr, int ks2, int slot2) {
+    const int so = sl * kSlotBytes;
+#define MXG_RD1(DST, B16, B8, F) nr.DST = op1(so + B16 + (F) * kChunkCodes, so + B8 + (F) * kChunkCodes)
+    MXG_MFMA(0, 0, 0); MXG_RD1(w0, w16, w8, 0);
+    MXG_MFMA(0, 1, 0); MXG_RD1(x0, x16, x8, 0); issue_one(7, ks2, slot2);
+    MXG_MFMA(0, 2, 0); MXG_RD1(w1, w16, w8, 1);
+    MXG_MFMA(0, 3, 0); MXG_RD1(x1, x16, x8, 1); issue_one(8, ks2, slot2);
+    MXG_MFMA(1, 0, 0); MXG_RD1(w2, w16, w8, 2);
+    MXG_MFMA(1, 1, 0); MXG_RD1(x2, x16, x8, 2); issue_one(9, ks2, slot2);
+    MXG_MFMA(1, 2, 0); MXG_RD1(w3, w16, w8, 3);
+    MXG_MFMA(1, 3, 0); MXG_RD1(x3, x16, x8, 3); issue_one(10, ks2, slot2);
+    MXG_MFMA(2, 0, 0);
+    MXG_MFMA(2, 1, 0); issue_one(11, ks2, slot2);
+    MXG_MFMA(2, 2, 0);
+    MXG_MFMA(2, 3, 0); issue_one(12, ks2, slot2);
+    MXG_MFMA(3, 0, 0);
+    MXG_MFMA(3, 1, 0); issue_one(13, ks2, slot2);
+    MXG_MFMA(3, 2, 0);
+    MXG_MFMA(3, 3, 0);
+#undef MXG_RD1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 #undef MXG_MFMA
-  static_assert(kCopiesPerStage == 14, "phase 1 interleaves exactly 14 copies");
-  // phase 0 order: {MFMA, LDS read} x 16
-  auto pattern0 = []() {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
+  static_assert(kCopiesPerStage == 14, "the phases interleave 7 + 7 copies");
   auto next_slot = [](int sl) { return sl == 2 ? 0 : sl + 1; };
   using sub0 = std::integral_constant<int, 0>;
   using sub1 = std::integral_constant<int, 1>;
 
   // ---- main loop over the 3-slot ring, with the operand registers double
   // buffered at half-stage granularity.  At the top of stage ks the lane holds
-  // stage ks's sub-step 0 operands (ra) and scales (sc); copies of stages ks+1
-  // and ks+2 are in flight.  Phase 0: sub-step 0 MFMAs while reading stage
-  // ks's sub-step 1 operands (rb).  Then wait until at most one stage's copies
-  // are outstanding (they complete in order: stage ks+1 has landed), and
-  // barrier: every wave's part of stage ks+1 is visible and every wave is done
-  // reading slot ks.  Phase 1: sub-step 1 MFMAs while reading stage ks+1's
-  // sub-step 0 operands and scales, and copying stage ks+3 into slot ks.
+  // stage ks's sub-step 0 operands (ra) and scales (sc); all copies of stage
+  // ks+1 and the first half of stage ks+2's are in flight.  Phase 0: sub-step
+  // 0 MFMAs while reading stage ks's sub-step 1 operands (rb) and issuing the
+  // second half of stage ks+2's copies.  Then wait until at most one stage's
+  // copies are outstanding (they complete in order: stage ks+1 has landed),
+  // and barrier: every wave's part of stage ks+1 is visible and every wave is
+  // done reading slot ks.  Phase 1: sub-step 1 MFMAs while reading stage
+  // ks+1's sub-step 0 operands and scales and issuing the first half of stage
+  // ks+3's copies into slot ks.
+  auto issue_half = [&](int ks2, int sl2, int first) {
+#pragma unroll
+    for (int i = 0; i < 7; ++i) issue_one(first + i, ks2, sl2);
+  };
   if (nk > 0) issue(0, 0);
   if (nk > 1) issue(1, 1);
-  if (nk > 2) issue(2, 2);
+  if (nk > 2) issue_half(2, 2, 0);
   if (nk > 2)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kCopiesPerStage));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage + 7));
   else if (nk > 1)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
   else
@@ -331,25 +368,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   Scales sc = read_scales(0);
   int ks = 0, slot = 0;
   for (; ks + 3 < nk; ++ks) {
-    const Half rb = read_half(slot, sub1{});
-    mfmas(ra, sc, sub0{});
-    pattern0();
+    const int nsl = next_slot(slot);
+    Half rb;
+    phase0(ra, sc, slot, rb, ks + 2, next_slot(nsl));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
     __builtin_amdgcn_s_barrier();
-    const int nsl = next_slot(slot);
     Scales sn;
     phase1(rb, sc, ks + 3, slot, nsl, ra, sn);
     __builtin_amdgcn_sched_barrier(0);
     sc = sn;
     slot = nsl;
   }
-  // the last (up to) three stages: no more copies
   for (; ks < nk; ++ks) {
+    const int nsl = next_slot(slot);
+    if (ks + 2 < nk) issue_half(ks + 2, next_slot(nsl), 7);
     const Half rb = read_half(slot, sub1{});
     mfmas(ra, sc, sub0{});
     Scales sn = sc;
-    const int nsl = next_slot(slot);
     if (ks + 1 < nk) {
       if (ks + 2 < nk)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
