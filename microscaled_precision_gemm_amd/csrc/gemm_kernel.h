@@ -101,6 +101,28 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   tn = in / gsize;
 }
 
+// Eight v_permlane32_swap_b32: after it, a[i] holds a[i] of lanes 0..31 in
+// lanes 0..31 and b[i] of lanes 0..31 in lanes 32..63, b[i] holds a[i] of lanes
+// 32..63 in lanes 0..31 and b[i] of lanes 32..63 in lanes 32..63.  On gfx950 a
+// swap issued right after a VALU write of one of its operands reads stale
+// lanes, and the compiler does not put wait states in between, so the swaps
+// are written out with s_nop 4 ahead of them (the same wait is not needed
+// before a VALU reads their results).
+__device__ __forceinline__ void swap_halves8(uint32_t (&a)[8], uint32_t (&b)[8]) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_permlane32_swap_b32 %0, %8\n\t"
+      "v_permlane32_swap_b32 %1, %9\n\t"
+      "v_permlane32_swap_b32 %2, %10\n\t"
+      "v_permlane32_swap_b32 %3, %11\n\t"
+      "v_permlane32_swap_b32 %4, %12\n\t"
+      "v_permlane32_swap_b32 %5, %13\n\t"
+      "v_permlane32_swap_b32 %6, %14\n\t"
+      "v_permlane32_swap_b32 %7, %15"
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]),
+        "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7]));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
   uint16_t ua, ub;
@@ -402,6 +424,86 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 
   // ---- epilogue
   const int mw0 = m0 + wm * 128, nw0 = n0 + wn * 128;
+  if constexpr (OUT == kOutMx) {
+    // MX output along N.  Fragments 2p and 2p+1 are consecutive 32-feature
+    // blocks of one 128-feature stage (nw0 is a multiple of 128).  Each lane
+    // holds 16 features of each; one permlane32 swap per register gathers
+    // block 2p in lanes 0..31 and block 2p+1 in lanes 32..63, so every lane
+    // owns one whole block of token j: its amax is lane-local, one 32-value
+    // conversion covers it, and its 24 code bytes are one 16-byte and one
+    // 8-byte run of the tiled layout.
+    const int stage = nw0 / kTileStageK;
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      const int m = mw0 + fm * 32 + j;
+      const int gm = (mw0 + fm * 32) / kTileGroupRows;
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        v16f va = acc[2 * pr][fm], vb = acc[2 * pr + 1][fm];
+        if constexpr (GELU) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            va[r] = gelu_tanh_f32(va[r]);
+            vb[r] = gelu_tanh_f32(vb[r]);
+          }
+        }
+        // lo: features 0..15 of this lane's block (even ones in 0..7, odd in
+        // 8..15), hi: features 16..31 in the same order
+        v16f lo, hi;
+#pragma unroll
+        for (int half8 = 0; half8 < 2; ++half8) {
+          uint32_t x[8], y[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            x[i] = __float_as_uint(va[8 * half8 + i]);
+            y[i] = __float_as_uint(vb[8 * half8 + i]);
+          }
+          swap_halves8(x, y);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            lo[8 * half8 + i] = __uint_as_float(x[i]);
+            hi[8 * half8 + i] = __uint_as_float(y[i]);
+          }
+        }
+        uint32_t amax = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t x = __float_as_uint(lo[r]) & 0x7fffffffu, y = __float_as_uint(hi[r]) & 0x7fffffffu;
+          const uint32_t xy = x > y ? x : y;
+          amax = xy > amax ? xy : amax;
+        }
+        const BlockScale sc = scale_from_f32_bits<OFMT>(amax);
+        v16f ev, od;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ev[i] = lo[i];
+          ev[8 + i] = hi[i];
+          od[i] = lo[8 + i];
+          od[8 + i] = hi[8 + i];
+        }
+        v6u q = cvt_f32x2x16<OFMT>(ev, od, sc.scale);
+        uint32_t sbyte = sc.byte;
+        if (sc.nonfinite) q = v6u{0, 0, 0, 0, 0, 0};
+        const int qb = 2 * pr + h;           // this lane's block within the stage
+        const int nb = stage * 4 + qb;
+        if (gm < g.gx && stage < (g.N + kTileStageK - 1) / kTileStageK) {
+          if (m >= g.M || nb >= g.N / 32) {  // layout padding
+            q = v6u{0, 0, 0, 0, 0, 0};
+            sbyte = 127u;
+          }
+          // even block: plane A (bytes 0..15) + plane L (16..23);
+          // odd block: plane H (bytes 0..7) + plane B (8..23)
+          uint8_t* half = static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes + pr * kHalfBytes;
+          const u32x4 d16 = h == 0 ? u32x4{q[0], q[1], q[2], q[3]} : u32x4{q[2], q[3], q[4], q[5]};
+          const u32x2 d8 = h == 0 ? u32x2{q[4], q[5]} : u32x2{q[0], q[1]};
+          *reinterpret_cast<u32x4*>(half + (h == 0 ? kPlaneA : kPlaneB) + j * 16) = d16;
+          *reinterpret_cast<u32x2*>(half + (h == 0 ? kPlaneL : kPlaneH) + j * 8) = d8;
+          g.out_scales[((int64_t)stage * g.gx + gm) * kChunkScales + j * 4 + qb] = (uint8_t)sbyte;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int fn = 0; fn < 4; ++fn) {
 #pragma unroll
@@ -412,51 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] = gelu_tanh_f32(v[r]);
       }
-      if constexpr (OUT == kOutMx) {
-        const int nb = (nw0 + fn * 32) / 32;  // 32-feature block of this fragment
-        uint32_t amax = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t a = __float_as_uint(v[r]) & 0x7fffffffu;
-          amax = a > amax ? a : amax;
-        }
-        const uint32_t other = (uint32_t)__shfl_xor((int)amax, 32);
-        amax = other > amax ? other : amax;
-        const BlockScale sc = scale_from_f32_bits<OFMT>(amax);
-        v16f ev, od;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          ev[i] = i < 8 ? v[i] : 0.0f;
-          od[i] = i < 8 ? v[8 + i] : 0.0f;
-        }
-        v6u q = cvt_f32x2x16<OFMT>(ev, od, sc.scale);
-        uint32_t sbyte = sc.byte;
-        if (sc.nonfinite) q = v6u{0, 0, 0, 0, 0, 0};
-        const int gm = (mw0 + fm * 32) / kTileGroupRows;
-        const int stage = nb >> 2, qb = nb & 3;
-        if (gm < g.gx && stage < (g.N + kTileStageK - 1) / kTileStageK) {
-          if (m >= g.M || nb >= g.N / 32) {  // layout padding
-            q = v6u{0, 0, 0, 0, 0, 0};
-            sbyte = 127u;
-          }
-          // this lane's 12 code bytes are bytes [12h, 12h+12) of block qb of
-          // row j; each dword lies in one plane of half qb/2 of the chunk
-          uint8_t* half = static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes +
-                          (qb >> 1) * kHalfBytes;
-#pragma unroll
-          for (int d = 0; d < 3; ++d) {
-            const int t = 12 * h + 4 * d;
-            int off;
-            if ((qb & 1) == 0)
-              off = t < 16 ? kPlaneA + j * 16 + t : kPlaneL + j * 8 + (t - 16);
-            else
-              off = t < 8 ? kPlaneH + j * 8 + t : kPlaneB + j * 16 + (t - 8);
-            *reinterpret_cast<uint32_t*>(half + off) = q[d];
-          }
-          if (h == 0)
-            g.out_scales[((int64_t)stage * g.gx + gm) * kChunkScales + j * 4 + qb] = (uint8_t)sbyte;
-        }
-      } else {
+      {
         const int n = nw0 + fn * 32 + 16 * h;
         if (m < g.M) {
           if constexpr (OUT == kOutBf16) {

@@ -78,23 +78,35 @@ __device__ __forceinline__ BlockScale scale_from_bf16_bits(uint32_t amax_bits) {
   return scale_from_f32_bits<FMT>(amax_bits << 16);
 }
 
+// The scaled FP6 conversions below are written as inline asm with an
+// early-clobber result.  They produce their 6 result dwords over several
+// passes and read the scale operand again after the first one: if the
+// destination tuple starts on the scale's register, every element after the
+// first pass is converted with a clobbered scale.  The compiler's register
+// allocator does not know this and can assign such an overlap, so the result
+// is kept apart from all inputs.
+
 // 32 bf16 values -> 32 FP6 codes packed as 6 dwords (element i at bits [6i, 6i+6)).
 template <int FMT>
 __device__ __forceinline__ v6u cvt_bf16x32(v32bf x, float scale) {
+  v6u r;
   if constexpr (FMT == kFmtE2M3)
-    return __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, scale);
+    asm("v_cvt_scalef32_pk32_fp6_bf16 %0, %1, %2" : "=&v"(r) : "v"(x), "v"(scale));
   else
-    return __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(x, scale);
+    asm("v_cvt_scalef32_pk32_bf6_bf16 %0, %1, %2" : "=&v"(r) : "v"(x), "v"(scale));
+  return r;
 }
 
 // Two 16-float vectors -> 32 FP6 codes; output element 2i comes from a[i] and
 // element 2i+1 from b[i] (the instruction interleaves its two sources).
 template <int FMT>
 __device__ __forceinline__ v6u cvt_f32x2x16(v16f a, v16f b, float scale) {
+  v6u r;
   if constexpr (FMT == kFmtE2M3)
-    return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, scale);
+    asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(a), "v"(b), "v"(scale));
   else
-    return __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, scale);
+    asm("v_cvt_scalef32_2xpk16_bf6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(a), "v"(b), "v"(scale));
+  return r;
 }
 
 // GELU, tanh form, in fp32: 0.5 x (1 + tanh(u)) = x / (1 + e^{-2u}) with
@@ -103,9 +115,10 @@ __device__ __forceinline__ v6u cvt_f32x2x16(v16f a, v16f b, float scale) {
 // reciprocal; for very negative x, 2^{...} overflows to +inf and the result is
 // x * 0 = -0.
 __device__ __forceinline__ float gelu_tanh_f32(float x) {
-  constexpr float kNeg2SqrtTwoOverPiLog2e = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
-  const float p = __builtin_fmaf(0.044715f * x, x, 1.0f);
-  const float t = __builtin_amdgcn_exp2f(kNeg2SqrtTwoOverPiLog2e * x * p);
+  // -2u log2 e = x (c0 + c1 x^2) with c0 = -2 sqrt(2/pi) log2 e, c1 = 0.044715 c0
+  constexpr float kC0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float kC1 = kC0 * 0.044715f;
+  const float t = __builtin_amdgcn_exp2f(x * __builtin_fmaf(kC1, x * x, kC0));
   return x * __builtin_amdgcn_rcpf(1.0f + t);
 }
 
