@@ -181,11 +181,13 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
  * fixed order 0, 1, ..., splits-1 (deterministic) before the output rounding.
  *
  * Arguments as mx_gemm (operands in MX_LAYOUT_TILED), with:
- *   splits    >= 1; k % (128 * splits) == 0, i.e. each chunk is whole 128-element
- *             stages (else MX_ERR_UNSUPPORTED); m <= 16 (else MX_ERR_SHAPE).
+ *   splits    1 .. 16 and k % (128 * splits) == 0, i.e. each chunk is whole
+ *             128-element stages (else MX_ERR_UNSUPPORTED); m <= 16 (else
+ *             MX_ERR_SHAPE).
  *   epilogue  MX_EPI_NONE only; out_kind MX_OUT_F32 or MX_OUT_BF16.
  *   workspace at least mx_gemm_workspace_size(m, n, k, a_src != NULL, splits)
- *             bytes (quantized activations plus fp32 partials).
+ *             bytes, used for the activations quantized inside the call (the
+ *             partial sums stay on chip); may be NULL when that size is 0.
  */
 int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
                    const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,

@@ -272,10 +272,10 @@ def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kin
     if out is None:
         out = torch.empty((m, n), dtype=dtype, device=dev)
     need = mx_gemm_workspace_size(m, n, k, a_src is not None, splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib().mx_gemm_splitk(_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af, _ptr(w.codes),
                               _ptr(w.scales), _fmt(w.fmt), m, n, k, splits, kind, _ptr(out), out.stride(0),
-                              _ptr(workspace), workspace.numel(), _stream(dev))
+                              _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(dev))
     _check(st, "mx_gemm_splitk")
     return out

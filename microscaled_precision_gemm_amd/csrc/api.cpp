@@ -120,9 +120,8 @@ size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which) {
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t a_is_src, int32_t splits) {
   if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || splits < 0) return 0;
   if (splits == 0) return a_is_src ? tiled_ws(m, k).end : 0;
-  if (m > 16) return 0;
-  const size_t q = a_is_src ? tiled_ws(m, k).end : 0;
-  return q + round_up((size_t)splits * 16 * (size_t)n * 4, kWsAlign);
+  if (m > 16 || splits > kMaxSplits) return 0;
+  return a_is_src ? tiled_ws(m, k).end : 0;
 }
 
 int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
@@ -207,16 +206,15 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
   if (!out) return MX_ERR_NULL;
   if (ldo < n) return MX_ERR_SHAPE;
   if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
-  if (k % (kTileStageK * (int64_t)splits) != 0) return MX_ERR_UNSUPPORTED;
+  if (splits > kMaxSplits || k % (kTileStageK * (int64_t)splits) != 0) return MX_ERR_UNSUPPORTED;
   const size_t need = mx_gemm_workspace_size(m, n, k, a_src != nullptr, splits);
-  if (!workspace || workspace_bytes < need) return MX_ERR_WORKSPACE;
-  if (!aligned(workspace, kWsAlign)) return MX_ERR_ALIGN;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MX_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, kWsAlign)) return MX_ERR_ALIGN;
   if (m == 0 || n == 0) return MX_OK;
 
   uint8_t* base = static_cast<uint8_t*>(workspace);
   const uint8_t* xc = static_cast<const uint8_t*>(a_codes);
   const uint8_t* xs = a_scales;
-  size_t part_off = 0;
   if (a_src && k > 0) {
     const TiledWs w = tiled_ws(m, k);
     const hipError_t e = launch_quantize_tiled(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off,
@@ -224,14 +222,12 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
     if (e != hipSuccess) return MX_ERR_HIP;
     xc = base + w.codes_off;
     xs = base + w.scales_off;
-    part_off = w.end;
   }
   SplitKArgs g;
   g.x_codes = xc;
   g.x_scales = xs;
   g.w_codes = static_cast<const uint8_t*>(w_codes);
   g.w_scales = w_scales;
-  g.partial = reinterpret_cast<float*>(base + part_off);
   g.out = out;
   g.ldo = ldo;
   g.M = (int32_t)m;

@@ -61,12 +61,13 @@ hipError_t launch_quantize_tiled(const void* src, int src_type, int64_t rows, in
 hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, int out_kind, int out_fmt,
                        hipStream_t stream);
 
+constexpr int kMaxSplits = 16;  // split-K chunks (their partials live in LDS)
+
 struct SplitKArgs {
   const uint8_t* x_codes;   // activations [M, K], M <= 16, tiled layout (one 32-row group)
   const uint8_t* x_scales;
   const uint8_t* w_codes;   // weights [N, K], tiled layout
   const uint8_t* w_scales;
-  float* partial;           // [splits, 16, N] fp32 workspace
   void* out;                // f32 / bf16 [M, ldo]
   int64_t ldo;
   int32_t M, N, K, splits;

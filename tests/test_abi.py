@@ -139,10 +139,13 @@ def test_splitk_validation(L):
     assert sk(splits=0) == B.MX_ERR_SHAPE
     assert sk(splits=3) == B.MX_ERR_UNSUPPORTED
     assert sk(splits=64) == B.MX_ERR_UNSUPPORTED  # 64-element chunks (not whole 128-element stages)
+    assert sk(splits=32) == B.MX_ERR_UNSUPPORTED  # at most 16 chunks
     assert sk(out_kind=2) == B.MX_ERR_FORMAT
-    assert sk(ws_bytes=10) == B.MX_ERR_WORKSPACE
-    assert sk(ws=NULL) == B.MX_ERR_WORKSPACE
-    assert sk(ws=FAKE + 16) == B.MX_ERR_ALIGN
+    # activations quantized inside the call need a workspace
+    src = dict(a_src=FAKE, lda=4096, a_codes=NULL, a_scales=NULL)
+    assert sk(ws_bytes=10, **src) == B.MX_ERR_WORKSPACE
+    assert sk(ws=NULL, **src) == B.MX_ERR_WORKSPACE
+    assert sk(ws=FAKE + 16, **src) == B.MX_ERR_ALIGN
     assert sk(a_fmt=3) == B.MX_ERR_UNSUPPORTED
     assert sk(m=0) == B.MX_OK
 
@@ -162,8 +165,12 @@ def test_workspace_sizes(L):
     assert mx.mx_gemm_workspace_size(64, 64, 128, False, 0) == 0
     assert mx.mx_gemm_workspace_size(64, 64, 100, True, 0) == 0  # invalid K
     assert mx.mx_gemm_workspace_size(17, 64, 128, True, 4) == 0  # splitk needs m <= 16
+    assert mx.mx_gemm_workspace_size(16, 64, 128, True, 17) == 0  # at most 16 chunks
+    # split-K keeps its partial sums on chip: the workspace only holds the
+    # activations quantized in the call (128 stages x one 32-row group)
     sz = mx.mx_gemm_workspace_size(16, 13312, 16384, True, 16)
-    assert sz >= 16 * 13312 * 4 * 16 + 16 * 12288 + 16 * 512
+    assert sz == mx.mx_gemm_workspace_size(16, 13312, 16384, True, 0) >= 128 * (3072 + 128)
+    assert mx.mx_gemm_workspace_size(16, 13312, 16384, False, 16) == 0
 
 
 def test_binding_refuses_cpu_tensors(L):

@@ -181,7 +181,7 @@ def test_edge_shapes():
 
 
 @pytest.mark.parametrize("m", [8, 16, 5, 1])
-@pytest.mark.parametrize("splits", [1, 4, 8, 32])
+@pytest.mark.parametrize("splits", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("w_fmt", ["e3m2", "e2m3"])
 def test_splitk_small(m, splits, w_fmt):
     n, k = 400, 4096  # ragged N (12.5 groups of 32), 32 stages of 128
@@ -195,6 +195,19 @@ def test_splitk_small(m, splits, w_fmt):
     assert torch.equal(o, o_again)
     assert_bf16_close(bf16_tensor_to_f64(o), c, s, "splitk bf16")
     assert_fp32_close(to_np(o32).astype(np.float64), c, s, "splitk f32")
+
+
+@pytest.mark.parametrize("splits", [6, 12])
+def test_splitk_uneven_chunks_per_wave(splits):
+    """24 stages in 6 or 12 chunks: the four waves of a workgroup get 2, 2, 2, 0
+    or 3, 3, 3, 3 chunks (one idle wave for S = 6)."""
+    m, n, k = 16, 96, 3072
+    a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", "e3m2", seed=43)
+    wq = _gpu_weights(w, "e3m2", qw)
+    say(f"splitk uneven m={m} n={n} k={k} S={splits}")
+    o32 = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="f32")
+    torch.cuda.synchronize()
+    assert_fp32_close(to_np(o32).astype(np.float64), c, s, f"splitk S={splits}")
 
 
 def test_splitk_matches_plain_gemm_property():
