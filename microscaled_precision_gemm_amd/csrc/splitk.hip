@@ -9,8 +9,8 @@
 //
 //  * One workgroup per 32-feature group of the weights, 4 waves.  Wave w
 //    streams the K-chunks w*spw .. w*spw+spw-1 (spw = ceil(S/4)), stage after
-//    stage, with a window of kWindow stages of loads in flight across chunk
-//    boundaries.  416 groups x 4 waves fit the GPU in one round.
+//    stage, with kWindow stages of loads in flight across chunk boundaries.
+//    416 groups x 4 waves fit the GPU in one round.
 //  * Both operands are in the tiled MX layout.  Per 128-element stage each
 //    lane loads its row's entries of the four planes of half h (16 + 8 + 8 +
 //    16 bytes), so every load instruction reads contiguous runs of 512 or 256
@@ -90,21 +90,48 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
   const int c0 = wave * spw;
   const int c1 = min(g.splits, c0 + spw);
   const int nst = c1 > c0 ? (c1 - c0) * sps : 0;      // stages this wave streams
-  const int st0 = c0 * sps;                           // its first stage
+  const int nc = c1 > c0 ? c1 - c0 : 0;               // chunks of this wave
+  // Every workgroup walks its chunks in a rotated order and each chunk's
+  // stages from a rotated start, so that the workgroups, which all read the
+  // same activations, spread their requests over many lines instead of
+  // hammering the same few at the same time.  The order is fixed per group
+  // (deterministic); the chunks' partials still meet in order 0 .. S-1.
+  const int r0 = sps > 0 ? grp % sps : 0;
+  const int q0 = nc > 0 ? (grp / max(sps, 1)) % nc : 0;
   const int lane_off = h * kHalfBytes;
   const int scale_off = j * 4 + 2 * h;
-  const uint8_t* wc = g.w_codes + ((int64_t)st0 * g.gw + grp) * kChunkCodes + lane_off;
-  const uint8_t* ws = g.w_scales + ((int64_t)st0 * g.gw + grp) * kChunkScales + scale_off;
-  const uint8_t* xc = g.x_codes + (int64_t)st0 * kChunkCodes + lane_off;  // activations: one 32-row group
-  const uint8_t* xs = g.x_scales + (int64_t)st0 * kChunkScales + scale_off;
+  const uint8_t* wc = g.w_codes + (int64_t)grp * kChunkCodes + lane_off;
+  const uint8_t* ws = g.w_scales + (int64_t)grp * kChunkScales + scale_off;
+  const uint8_t* xc = g.x_codes + lane_off;  // activations: one 32-row group
+  const uint8_t* xs = g.x_scales + scale_off;
   const int64_t w_step = (int64_t)g.gw * kChunkCodes, ws_step = (int64_t)g.gw * kChunkScales;
+  const bool token = j < 16;  // rows 16..31 of the activation group are zero padding
 
-  auto load = [&](int i) {
+  // load cursor: chunk position cl (0 .. nc-1) and stage position tl (0 .. sps-1)
+  int cl = 0, tl = 0;
+  auto next_stage = [&]() {
+    int c = cl + q0;
+    c = c >= nc ? c - nc : c;
+    int t = tl + r0;
+    t = t >= sps ? t - sps : t;
+    if (++tl == sps) {
+      tl = 0;
+      ++cl;
+    }
+    return (c0 + c) * sps + t;
+  };
+  auto load = [&](int st) {
     StageOps o;
-    o.w = load_pieces<true>(wc + i * w_step, j);
-    o.x = load_pieces<false>(xc + (int64_t)i * kChunkCodes, j);
-    o.ws = *reinterpret_cast<const uint16_t*>(ws + i * ws_step);
-    o.xs = *reinterpret_cast<const uint16_t*>(xs + (int64_t)i * kChunkScales);
+    o.w = load_pieces<true>(wc + st * w_step, j);
+    o.ws = *reinterpret_cast<const uint16_t*>(ws + st * ws_step);
+    if (token) {
+      o.x = load_pieces<false>(xc + (int64_t)st * kChunkCodes, j);
+      o.xs = *reinterpret_cast<const uint16_t*>(xs + (int64_t)st * kChunkScales);
+    } else {
+      o.x.a = o.x.b = u32x4{0u, 0u, 0u, 0u};
+      o.x.l = o.x.hh = u32x2{0u, 0u};
+      o.xs = 0x7f7f;
+    }
     return o;
   };
 
@@ -114,19 +141,21 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
   StageOps win[kWindow];
 #pragma unroll
   for (int i = 0; i < kWindow; ++i)
-    if (i < nst) win[i] = load(i);
-  int chunk = c0, left = sps;  // chunk being accumulated, its stages still to come
+    if (i < nst) win[i] = load(next_stage());
+  int cc = 0, left = sps;  // chunk position being accumulated, its stages still to come
   for (int i = 0; i < nst; i += kWindow) {
 #pragma unroll
     for (int k = 0; k < kWindow; ++k) {
       if (i + k < nst) {
         const StageOps o = win[k];
-        if (i + k + kWindow < nst) win[k] = load(i + k + kWindow);
+        if (i + k + kWindow < nst) win[k] = load(next_stage());
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op0(o.w), op0(o.x), acc, WF, XF, 0, o.ws, 0, o.xs);
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op1(o.w), op1(o.x), acc, WF, XF, 1, o.ws, 1, o.xs);
         if (--left == 0) {
+          int chunk = cc + q0;
+          chunk = c0 + (chunk >= nc ? chunk - nc : chunk);
           // lane (h, j) holds, for token j, features 8a + 4h + b in register 4a + b
-          if (j < 16) {
+          if (token) {
 #pragma unroll
             for (int a = 0; a < 4; ++a)
               *reinterpret_cast<v4f*>(&part[chunk][j][8 * a + 4 * h]) =
@@ -134,7 +163,7 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-          ++chunk;
+          ++cc;
           left = sps;
         }
       }
