@@ -22,6 +22,13 @@ computes, in float64 with numpy:
   quantization, with blocks of 32 consecutive output columns.  The Hedra post
   (section "Fusion cut intermediate memory traffic") has the down projection
   read the quantized intermediate directly; this is that intermediate.
+* The SwiGLU variant of that epilogue (the MLP activation the same section
+  names for Krea 3): the gate and up projections are one GEMM over stacked
+  weights, and each output is silu(gate) * up (Shazeer, "GLU Variants Improve
+  Transformer", 2020; silu(x) = x * sigmoid(x)), MX-quantized the same way.
+  The stacking order is the library's own: in each run of 128 stacked rows,
+  the first 64 are gate rows of 64 consecutive features, the next 64 the up
+  rows of the same features.
 
 Readings where the pages are silent (also listed in the design doc):
 
@@ -255,6 +262,49 @@ def ulp_fp32(x: np.ndarray) -> np.ndarray:
     x = np.abs(np.asarray(x, dtype=np.float64))
     e = np.where(x > 0, floor_log2(np.where(x > 0, x, 1.0)), -126)
     return np.ldexp(1.0, np.maximum(e, -126) - 23)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU (swish with beta 1): x * sigmoid(x) = x / (1 + exp(-x))."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+SWIGLU_RUN = 64  # gate rows, then as many up rows, per 128 stacked rows
+
+
+def swiglu_rows(h: int) -> tuple[np.ndarray, np.ndarray]:
+    """Stacked-weight row indices of the gate and of the up projection of
+    features 0 .. h-1 (h a multiple of 64): feature f's gate row is
+    128 * (f // 64) + f % 64 and its up row 64 rows later."""
+    if h % SWIGLU_RUN:
+        raise ValueError("the SwiGLU hidden size must be a multiple of 64")
+    f = np.arange(h)
+    gate = 2 * SWIGLU_RUN * (f // SWIGLU_RUN) + f % SWIGLU_RUN
+    return gate, gate + SWIGLU_RUN
+
+
+def swiglu_ref(a_deq: np.ndarray, w_stacked_deq: np.ndarray):
+    """SwiGLU projection on dequantized operands: C = A @ Ws.T over the 2h
+    stacked rows, then out[:, f] = silu(C[:, gate f]) * C[:, up f].
+
+    Returns (out, gate, up, s_gate, s_up) in float64, where s_* are the
+    |A| @ |W|.T scales of the gate and up columns (for the tolerance)."""
+    c, s = gemm_ref(a_deq, w_stacked_deq)
+    gi, ui = swiglu_rows(c.shape[1] // 2)
+    gate, up = c[:, gi], c[:, ui]
+    return silu(gate) * up, gate, up, s[:, gi], s[:, ui]
+
+
+def fc1_swiglu_mx_ref(a_deq: np.ndarray, w_stacked_deq: np.ndarray, out_fmt: str = "e2m3"):
+    """Stacked gate/up projection with the fused SwiGLU epilogue,
+    re-quantized along the h output features from the fp32 rounding of the
+    float64 result (the precision the device quantizes in).  Returns
+    (codes [M, h], scales [M, h/32], out64, gate, up, s_gate, s_up)."""
+    out, gate, up, sg, su = swiglu_ref(a_deq, w_stacked_deq)
+    codes, scales = quantize(out.astype(np.float32).astype(np.float64), out_fmt)
+    return codes, scales, out, gate, up, sg, su
 
 
 # ---------------------------------------------------------------------------

@@ -334,3 +334,53 @@ def test_fc1_reference_is_quantized_gelu():
     spacing = np.ldexp(1.0, np.maximum(O.floor_log2(np.where(r > 0, r, 1.0)), 0) - 3)
     allowed = np.where(r > 7.5, r - 7.5, 0.5 * spacing) * unit
     assert np.all(np.abs(deq - g32) <= allowed * (1 + 1e-12))
+
+
+# ---------------------------------------------------------------- SwiGLU
+
+def test_silu_matches_torch():
+    x = np.concatenate([np.linspace(-60, 60, 6001), np.random.default_rng(5).standard_normal(5000) * 6])
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(O.silu(x), ref, rtol=1e-14, atol=1e-300)
+
+
+def test_silu_identities():
+    x = np.linspace(-30, 30, 6001)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, atol=1e-12)  # x sigma(x) - (-x) sigma(-x) = x
+    assert O.silu(np.array([800.0]))[0] == 800.0
+    assert O.silu(np.array([-800.0]))[0] == 0.0  # -800 / (1 + e^800) underflows to -0
+    # minimum of x sigma(x) is about -0.27846 near x = -1.27846
+    assert abs(O.silu(np.linspace(-3, 0, 300001)).min() + 0.2784645) < 1e-6
+
+
+def test_swiglu_stacking_and_product():
+    """A stacked weight built by interleaving blocks of 64 gate rows and 64 up
+    rows gives silu(A Wg^T) * (A Wu^T), computed here with torch."""
+    rng = np.random.default_rng(11)
+    m, k, h = 5, 64, 192
+    a = O.dequantize(*O.quantize(rng.standard_normal((m, k)), "e2m3"), "e2m3")
+    wg = O.dequantize(*O.quantize(rng.standard_normal((h, k)) * 0.2, "e2m3"), "e2m3")
+    wu = O.dequantize(*O.quantize(rng.standard_normal((h, k)) * 0.2, "e2m3"), "e2m3")
+    ws = np.stack([wg.reshape(h // 64, 64, k), wu.reshape(h // 64, 64, k)], axis=1).reshape(2 * h, k)
+    out, gate, up, sg, su = O.swiglu_ref(a, ws)
+    ta, tg, tu = (torch.from_numpy(v) for v in (a, wg, wu))
+    want = (torch.nn.functional.silu(ta @ tg.T) * (ta @ tu.T)).numpy()
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(sg, np.abs(a) @ np.abs(wg).T, rtol=1e-14)
+    np.testing.assert_allclose(su, np.abs(a) @ np.abs(wu).T, rtol=1e-14)
+
+
+def test_fc1_swiglu_reference_is_quantized_product():
+    rng = np.random.default_rng(12)
+    a = O.dequantize(*O.quantize(rng.standard_normal((8, 64)), "e2m3"), "e2m3")
+    ws = O.dequantize(*O.quantize(rng.standard_normal((128, 64)) * 0.1, "e2m3"), "e2m3")
+    codes, scales, out, gate, up, sg, su = O.fc1_swiglu_mx_ref(a, ws)
+    assert codes.shape == (8, 64) and scales.shape == (8, 2)
+    o32 = out.astype(np.float32).astype(np.float64)
+    deq = O.dequantize(codes, scales, "e2m3")
+    unit = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+    r = np.abs(o32) / unit
+    spacing = np.ldexp(1.0, np.maximum(O.floor_log2(np.where(r > 0, r, 1.0)), 0) - 3)
+    allowed = np.where(r > 7.5, r - 7.5, 0.5 * spacing) * unit
+    assert np.all(np.abs(deq - o32) <= allowed * (1 + 1e-12))

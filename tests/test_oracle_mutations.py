@@ -49,6 +49,22 @@ def _gelu_wrong_constant(x):
     return x / (1.0 + np.exp(-2.0 * u))
 
 
+def _silu_doubled(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-2.0 * x))
+
+
+def _swiglu_rows_swapped(h):
+    f = np.arange(h)
+    gate = 128 * (f // 64) + f % 64
+    return gate + 64, gate
+
+
+def _swiglu_rows_contiguous(h):
+    f = np.arange(h)
+    return f, f + h
+
+
 def _bias_off(fmt):
     e, m, b = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3)}[fmt]
     return (e, m, b + 1)
@@ -63,6 +79,9 @@ MUTANTS = [
     ("gemm_ref", _gemm_swapped_scale, [pins.test_gemm_one_hot_selects_columns]),
     ("gelu_tanh", _gelu_wrong_constant, [pins.test_gelu_matches_torch_tanh_gelu]),
     ("_fmt", _bias_off, [pins.test_magnitudes_match_literal_table]),
+    ("silu", _silu_doubled, [pins.test_silu_matches_torch]),
+    ("swiglu_rows", _swiglu_rows_swapped, [pins.test_swiglu_stacking_and_product]),
+    ("swiglu_rows", _swiglu_rows_contiguous, [pins.test_swiglu_stacking_and_product]),
 ]
 
 
