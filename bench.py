@@ -37,8 +37,9 @@ METRIC = "MXFP6 GEMM TFLOPS + % of 10.1 PF MFMA peak (DiT MLP 20480x3072x12288)"
 PEAK_MXFP6_TFLOPS = 10100.0
 PEAK_HBM_GBS = 8000.0
 
-# rocprofv3 names of the two GEMM instantiations (E2M3 x E2M3; fc1: MX out + GELU, fc2: bf16 out)
-KERNEL_NAMES = {"fc1": "gemm_kernel<2, 2, 2, true, 2>", "fc2": "gemm_kernel<2, 2, 1, false, 2>"}
+# rocprofv3 names of the two GEMM instantiations <W fmt, A fmt, out kind, epilogue, out fmt>
+# (E2M3 x E2M3; fc1: MX out + GELU, fc2: bf16 out, no epilogue)
+KERNEL_NAMES = {"fc1": "gemm_kernel<2, 2, 2, 1, 2>", "fc2": "gemm_kernel<2, 2, 1, 0, 2>"}
 # the sources the GEMM kernel is built from: measured HBM traffic is only reported
 # while they are unchanged since the counters were taken
 GEMM_SOURCES = ["gemm_kernel.h", "internal.h", "mx_device.h", "gemm_we2m3_e2m3.hip"]
@@ -116,6 +117,54 @@ def bench_mlp(steps: int, warmup: int):
         "fc1_bytes": m * d * 3 // 4 + m * d // 32 + hdim * d * 3 // 4 + hdim * d // 32 + m * hdim * 3 // 4 + m * hdim // 32,
         "fc2_bytes": m * hdim * 3 // 4 + m * hdim // 32 + d * hdim * 3 // 4 + d * hdim // 32 + m * d * 2,
     }
+
+
+def bench_swiglu_mlp(steps: int, warmup: int):
+    """The SwiGLU variant of the MLP step (the activation the Krea 3 post names):
+    quantize x, stacked gate/up GEMM 20480 x 3072 x 16384 with SwiGLU -> E2M3
+    (8192 features), down projection 20480 x 8192 x 3072 to bf16."""
+    w1w, w2w = syn.WORKLOADS["sw_fc1"], syn.WORKLOADS["sw_fc2"]
+    m, d, n1 = w1w.m, w1w.k, w1w.n
+    hdim = n1 // 2
+    dev = torch.device("cuda:0")
+    x = syn.make_a(w1w).to(dev)
+    w1 = mx.mx_quantize(syn.make_w(w1w).to(dev), "e2m3")
+    w2 = mx.mx_quantize(syn.make_w(w2w).to(dev), "e2m3")
+    xq = mx.MXTensor.empty(m, d, "e2m3", "tiled", dev)
+    h = mx.MXTensor.empty(m, hdim, "e2m3", "tiled", dev)
+    y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mx.mx_quantize(x, "e2m3", "tiled", out=xq)
+        if ev is not None:
+            ev[1].record()
+        mx.mx_gemm(xq, w1, out_kind="mx", epilogue="swiglu", out=h)
+        if ev is not None:
+            ev[2].record()
+        mx.mx_gemm(h, w2, out_kind="bf16", out=y)
+        if ev is not None:
+            ev[3].record()
+
+    settle(step, 0.3)
+    for _ in range(warmup):
+        step()
+    evs = [_events(4) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    f1 = np.array([e[1].elapsed_time(e[2]) for e in evs]).mean()
+    f2 = np.array([e[2].elapsed_time(e[3]) for e in evs]).mean()
+    fl1, fl2 = 2.0 * m * d * n1, 2.0 * m * hdim * d
+    return {"workload": "SwiGLU MLP forward: quantize x, gate/up 20480x3072x16384 (SwiGLU -> E2M3, 8192 "
+                        "features), down 20480x8192x3072 (bf16 out)",
+            "ms_per_step": round(wall * 1e3 / steps, 4), "tflops": round((fl1 + fl2) / (wall / steps) / 1e12, 1),
+            "fc1_ms": round(float(f1), 4), "fc1_tflops": round(fl1 / f1 / 1e9, 1),
+            "fc2_ms": round(float(f2), 4), "fc2_tflops": round(fl2 / f2 / 1e9, 1)}
 
 
 def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
@@ -241,6 +290,7 @@ def main():
     dom_ms = r[f"{dom}_ms"]
     achieved = r["flops_per_gemm"] / dom_ms / 1e9
     skinny = [bench_skinny(16, 16, args.skinny_iters), bench_skinny(8, 16, args.skinny_iters)]
+    swiglu = bench_swiglu_mlp(args.steps, args.warmup)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -266,6 +316,7 @@ def main():
                        "fc2_tflops": round(r["flops_per_gemm"] / r["fc2_ms"] / 1e9, 1),
                        "quantize_gb_s": round(r["quantize_bytes"] / r["quantize_ms"] / 1e6, 1)},
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
+        "swiglu_mlp": swiglu,
     }
     if args.copy_calibration:
         line["copy_calibration"] = copy_calibration()

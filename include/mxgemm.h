@@ -114,6 +114,14 @@ extern "C" {
 /* GEMM epilogues. */
 #define MX_EPI_NONE 0
 #define MX_EPI_GELU_TANH 1 /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+/* SwiGLU over stacked gate/up weights (the MLP activation of the Hedra post,
+ * section "Fusion cut intermediate memory traffic"; silu(x) = x / (1 + e^-x)):
+ * W holds n = 2h rows in runs of 128, the first 64 rows of each run are the
+ * gate rows of 64 consecutive features and the next 64 the up rows of the
+ * same features, i.e. feature f's gate row is 128 * (f / 64) + f % 64 and its
+ * up row is 64 rows later.  The output has h = n / 2 features:
+ * out[:, f] = silu(C[:, gate row f]) * C[:, up row f]. */
+#define MX_EPI_SWIGLU 2
 
 /*
  * mx_quantize - MX-quantize a [rows, k] matrix along its rows.
@@ -158,12 +166,15 @@ size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which);
  *   fp32 accuracy for that pair).
  * m, n, k: >= 0, k % 32 == 0.  m == 0 or n == 0 is a no-op; k == 0 writes
  *   C = 0 (epilogue applied).
- * epilogue: MX_EPI_NONE or MX_EPI_GELU_TANH (applied to the fp32 accumulator).
+ * epilogue: MX_EPI_NONE, MX_EPI_GELU_TANH or MX_EPI_SWIGLU, applied to the
+ *   fp32 accumulator.  MX_EPI_SWIGLU needs n % 128 == 0 and produces
+ *   n_out = n / 2 output features; the other epilogues keep n_out = n.
  * out_kind:
- *   MX_OUT_F32 / MX_OUT_BF16: out is [m, ldo] elements (ldo >= n), C is
- *     written to its first n columns; out_scales, out_fmt are ignored.
+ *   MX_OUT_F32 / MX_OUT_BF16: out is [m, ldo] elements (ldo >= n_out), the
+ *     result is written to its first n_out columns; out_scales, out_fmt are
+ *     ignored.
  *   MX_OUT_MX: the epilogue result is MX-quantized along N in blocks of 32
- *     (n % 32 == 0) into out / out_scales as an [m, n] matrix in
+ *     (n_out % 32 == 0) into out / out_scales as an [m, n_out] matrix in
  *     MX_LAYOUT_TILED (padding written too), element format out_fmt; ldo is
  *     ignored.  This output is directly the a_codes / a_scales of a
  *     following GEMM (the down projection reads the quantized intermediate).

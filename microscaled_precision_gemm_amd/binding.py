@@ -36,12 +36,13 @@ MX_OUT_BF16 = 1
 MX_OUT_MX = 2
 MX_EPI_NONE = 0
 MX_EPI_GELU_TANH = 1
+MX_EPI_SWIGLU = 2
 MX_LAYOUT_ROWS = 0
 MX_LAYOUT_TILED = 1
 
 FMT_CODES = {"e2m3": MX_FMT_E2M3, "e3m2": MX_FMT_E3M2}
 OUT_KINDS = {"f32": MX_OUT_F32, "bf16": MX_OUT_BF16, "mx": MX_OUT_MX}
-EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH}
+EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH, "swiglu": MX_EPI_SWIGLU}
 LAYOUTS = {"rows": MX_LAYOUT_ROWS, "tiled": MX_LAYOUT_TILED}
 
 EXPORTED = ("mx_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_splitk", "mx_gemm_workspace_size",
@@ -210,9 +211,12 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
             out_fmt: str = "e2m3", a_fmt: str = "e2m3", out: torch.Tensor | MXTensor | None = None,
             workspace: torch.Tensor | None = None):
     """C = A W^T.  ``a`` is a bf16/fp32 tensor (quantized to ``a_fmt`` inside the
-    call) or an MXTensor.  Returns a [m, n] tensor, or an MXTensor for out_kind="mx"."""
+    call) or an MXTensor.  Returns a [m, n_out] tensor, or an MXTensor for
+    out_kind="mx"; n_out = n, or n / 2 for epilogue="swiglu" (``w`` then holds
+    stacked gate/up rows, see include/mxgemm.h)."""
     _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
+    n_out = n // 2 if epilogue == "swiglu" else n
     if isinstance(a, MXTensor):
         _check_mx(a, "a", "tiled")
         a_src, a_codes, a_scales, af, lda, m = None, a.codes, a.scales, _fmt(a.fmt), 0, a.rows
@@ -228,17 +232,17 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
     kind = OUT_KINDS[out_kind]
     if kind == MX_OUT_MX:
         if out is None:
-            out = MXTensor.empty(m, n, out_fmt, "tiled", dev)
+            out = MXTensor.empty(m, n_out, out_fmt, "tiled", dev)
         _check_mx(out, "out", "tiled")
-        if out.rows != m or out.k != n:
-            raise ValueError("out must be an [m, n] MX matrix")
+        if out.rows != m or out.k != n_out:
+            raise ValueError("out must be an [m, n_out] MX matrix")
         out_data, out_scales, ldo = out.codes, out.scales, 0
     else:
         dtype = torch.float32 if kind == MX_OUT_F32 else torch.bfloat16
         if out is None:
-            out = torch.empty((m, n), dtype=dtype, device=dev)
-        if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (m, n):
-            raise ValueError("out must be [m, n] of the output dtype with unit stride")
+            out = torch.empty((m, n_out), dtype=dtype, device=dev)
+        if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (m, n_out):
+            raise ValueError("out must be [m, n_out] of the output dtype with unit stride")
         out_data, out_scales, ldo = out, None, out.stride(0)
     need = mx_gemm_workspace_size(m, n, k, a_src is not None, 0)
     if workspace is None and need > 0:

@@ -142,16 +142,19 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_gemm_common(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k);
   if (st != MX_OK) return st;
-  if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH) return MX_ERR_FORMAT;
+  if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH && epilogue != MX_EPI_SWIGLU) return MX_ERR_FORMAT;
   if (out_kind != MX_OUT_F32 && out_kind != MX_OUT_BF16 && out_kind != MX_OUT_MX) return MX_ERR_FORMAT;
+  // SwiGLU pairs the gate and up rows inside each run of 128 stacked rows
+  if (epilogue == MX_EPI_SWIGLU && n % 128 != 0) return MX_ERR_UNSUPPORTED;
+  const int64_t n_out = epilogue == MX_EPI_SWIGLU ? n / 2 : n;
   if (!out) return MX_ERR_NULL;
   if (out_kind == MX_OUT_MX) {
     if (!valid_fmt(out_fmt)) return MX_ERR_FORMAT;
     if (!out_scales) return MX_ERR_NULL;
-    if (n % 32 != 0) return MX_ERR_UNSUPPORTED;
+    if (n_out % 32 != 0) return MX_ERR_UNSUPPORTED;
     if (!aligned(out, 16) || !aligned(out_scales, 4)) return MX_ERR_ALIGN;
   } else {
-    if (ldo < n) return MX_ERR_SHAPE;
+    if (ldo < n_out) return MX_ERR_SHAPE;
     if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
   }
   const size_t need = mx_gemm_workspace_size(m, n, k, a_src != nullptr, 0);

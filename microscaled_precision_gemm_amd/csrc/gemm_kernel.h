@@ -131,7 +131,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
-template <int WF, int XF, int OUT, bool GELU, int OFMT>
+template <int WF, int XF, int OUT, int EPI, int OFMT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   constexpr int kLayout = OUT == kOutMx ? kLayoutMx : kLayoutContig;
@@ -424,102 +424,123 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 
   // ---- epilogue
   const int mw0 = m0 + wm * 128, nw0 = n0 + wn * 128;
+  // SwiGLU: this wave's 128 stacked rows are the gate rows (fragments 0, 1)
+  // and the up rows (fragments 2, 3) of output features nw0/2 .. nw0/2 + 63.
+  constexpr bool kSwiglu = EPI == kEpiSwiglu;
+  const int n_out = kSwiglu ? g.N / 2 : g.N;
+  auto act = [&](float x) { return EPI == kEpiGeluTanh ? gelu_tanh_f32(x) : x; };
   if constexpr (OUT == kOutMx) {
-    // MX output along N.  Fragments 2p and 2p+1 are consecutive 32-feature
-    // blocks of one 128-feature stage (nw0 is a multiple of 128).  Each lane
-    // holds 16 features of each; one permlane32 swap per register gathers
-    // block 2p in lanes 0..31 and block 2p+1 in lanes 32..63, so every lane
-    // owns one whole block of token j: its amax is lane-local, one 32-value
-    // conversion covers it, and its 24 code bytes are one 16-byte and one
-    // 8-byte run of the tiled layout.
-    const int stage = nw0 / kTileStageK;
+    // MX output along N.  A pair of fragment values (va, vb) holds two
+    // consecutive 32-feature blocks of one 128-feature output stage; each
+    // lane has 16 features of each, and one permlane32 swap per register
+    // gathers the first block in lanes 0..31 and the second in lanes 32..63,
+    // so every lane owns one whole block of token j: its amax is lane-local,
+    // one 32-value conversion covers it, and its 24 code bytes are one
+    // 16-byte and one 8-byte run of the tiled layout.
+    const int n_stages = (n_out + kTileStageK - 1) / kTileStageK;
+    auto emit_pair = [&](const v16f& va, const v16f& vb, int m, int gm, int stage, int pr) {
+      // lo: features 0..15 of this lane's block (even ones in 0..7, odd in
+      // 8..15), hi: features 16..31 in the same order
+      v16f lo, hi;
+#pragma unroll
+      for (int half8 = 0; half8 < 2; ++half8) {
+        uint32_t x[8], y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          x[i] = __float_as_uint(va[8 * half8 + i]);
+          y[i] = __float_as_uint(vb[8 * half8 + i]);
+        }
+        swap_halves8(x, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo[8 * half8 + i] = __uint_as_float(x[i]);
+          hi[8 * half8 + i] = __uint_as_float(y[i]);
+        }
+      }
+      uint32_t amax = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t x = __float_as_uint(lo[r]) & 0x7fffffffu, y = __float_as_uint(hi[r]) & 0x7fffffffu;
+        const uint32_t xy = x > y ? x : y;
+        amax = xy > amax ? xy : amax;
+      }
+      const BlockScale sc = scale_from_f32_bits<OFMT>(amax);
+      v16f ev, od;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ev[i] = lo[i];
+        ev[8 + i] = hi[i];
+        od[i] = lo[8 + i];
+        od[8 + i] = hi[8 + i];
+      }
+      v6u q = cvt_f32x2x16<OFMT>(ev, od, sc.scale);
+      uint32_t sbyte = sc.byte;
+      if (sc.nonfinite) q = v6u{0, 0, 0, 0, 0, 0};
+      const int qb = 2 * pr + h;  // this lane's block within the stage
+      const int nb = stage * 4 + qb;
+      if (gm < g.gx && stage < n_stages) {
+        if (m >= g.M || nb >= n_out / 32) {  // layout padding
+          q = v6u{0, 0, 0, 0, 0, 0};
+          sbyte = 127u;
+        }
+        // even block: plane A (bytes 0..15) + plane L (16..23);
+        // odd block: plane H (bytes 0..7) + plane B (8..23)
+        uint8_t* half = static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes + pr * kHalfBytes;
+        const u32x4 d16 = h == 0 ? u32x4{q[0], q[1], q[2], q[3]} : u32x4{q[2], q[3], q[4], q[5]};
+        const u32x2 d8 = h == 0 ? u32x2{q[4], q[5]} : u32x2{q[0], q[1]};
+        *reinterpret_cast<u32x4*>(half + (h == 0 ? kPlaneA : kPlaneB) + j * 16) = d16;
+        *reinterpret_cast<u32x2*>(half + (h == 0 ? kPlaneL : kPlaneH) + j * 8) = d8;
+        g.out_scales[((int64_t)stage * g.gx + gm) * kChunkScales + j * 4 + qb] = (uint8_t)sbyte;
+      }
+    };
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
       const int m = mw0 + fm * 32 + j;
       const int gm = (mw0 + fm * 32) / kTileGroupRows;
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        v16f va = acc[2 * pr][fm], vb = acc[2 * pr + 1][fm];
-        if constexpr (GELU) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            va[r] = gelu_tanh_f32(va[r]);
-            vb[r] = gelu_tanh_f32(vb[r]);
-          }
-        }
-        // lo: features 0..15 of this lane's block (even ones in 0..7, odd in
-        // 8..15), hi: features 16..31 in the same order
-        v16f lo, hi;
-#pragma unroll
-        for (int half8 = 0; half8 < 2; ++half8) {
-          uint32_t x[8], y[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            x[i] = __float_as_uint(va[8 * half8 + i]);
-            y[i] = __float_as_uint(vb[8 * half8 + i]);
-          }
-          swap_halves8(x, y);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            lo[8 * half8 + i] = __uint_as_float(x[i]);
-            hi[8 * half8 + i] = __uint_as_float(y[i]);
-          }
-        }
-        uint32_t amax = 0;
+      if constexpr (kSwiglu) {
+        // output features nw0/2 .. +63: blocks 2p, 2p+1 of stage nw0/256, p = (nw0/128) % 2
+        v16f va, vb;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t x = __float_as_uint(lo[r]) & 0x7fffffffu, y = __float_as_uint(hi[r]) & 0x7fffffffu;
-          const uint32_t xy = x > y ? x : y;
-          amax = xy > amax ? xy : amax;
+          va[r] = silu_f32(acc[0][fm][r]) * acc[2][fm][r];
+          vb[r] = silu_f32(acc[1][fm][r]) * acc[3][fm][r];
         }
-        const BlockScale sc = scale_from_f32_bits<OFMT>(amax);
-        v16f ev, od;
+        emit_pair(va, vb, m, gm, nw0 / (2 * kTileStageK), (nw0 / kTileStageK) & 1);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ev[i] = lo[i];
-          ev[8 + i] = hi[i];
-          od[i] = lo[8 + i];
-          od[8 + i] = hi[8 + i];
-        }
-        v6u q = cvt_f32x2x16<OFMT>(ev, od, sc.scale);
-        uint32_t sbyte = sc.byte;
-        if (sc.nonfinite) q = v6u{0, 0, 0, 0, 0, 0};
-        const int qb = 2 * pr + h;           // this lane's block within the stage
-        const int nb = stage * 4 + qb;
-        if (gm < g.gx && stage < (g.N + kTileStageK - 1) / kTileStageK) {
-          if (m >= g.M || nb >= g.N / 32) {  // layout padding
-            q = v6u{0, 0, 0, 0, 0, 0};
-            sbyte = 127u;
+        for (int pr = 0; pr < 2; ++pr) {
+          v16f va = acc[2 * pr][fm], vb = acc[2 * pr + 1][fm];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            va[r] = act(va[r]);
+            vb[r] = act(vb[r]);
           }
-          // even block: plane A (bytes 0..15) + plane L (16..23);
-          // odd block: plane H (bytes 0..7) + plane B (8..23)
-          uint8_t* half = static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes + pr * kHalfBytes;
-          const u32x4 d16 = h == 0 ? u32x4{q[0], q[1], q[2], q[3]} : u32x4{q[2], q[3], q[4], q[5]};
-          const u32x2 d8 = h == 0 ? u32x2{q[4], q[5]} : u32x2{q[0], q[1]};
-          *reinterpret_cast<u32x4*>(half + (h == 0 ? kPlaneA : kPlaneB) + j * 16) = d16;
-          *reinterpret_cast<u32x2*>(half + (h == 0 ? kPlaneL : kPlaneH) + j * 8) = d8;
-          g.out_scales[((int64_t)stage * g.gx + gm) * kChunkScales + j * 4 + qb] = (uint8_t)sbyte;
+          emit_pair(va, vb, m, gm, nw0 / kTileStageK, pr);
         }
       }
     }
     return;
   }
+  constexpr int kOutFrags = kSwiglu ? 2 : 4;
 #pragma unroll
-  for (int fn = 0; fn < 4; ++fn) {
+  for (int fn = 0; fn < kOutFrags; ++fn) {
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
       const int m = mw0 + fm * 32 + j;
-      v16f v = acc[fn][fm];
-      if constexpr (GELU) {
+      v16f v;
+      if constexpr (kSwiglu) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = gelu_tanh_f32(v[r]);
+        for (int r = 0; r < 16; ++r) v[r] = silu_f32(acc[fn][fm][r]) * acc[fn + 2][fm][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = act(acc[fn][fm][r]);
       }
       {
-        const int n = nw0 + fn * 32 + 16 * h;
+        const int n = (kSwiglu ? nw0 / 2 : nw0) + fn * 32 + 16 * h;
         if (m < g.M) {
           if constexpr (OUT == kOutBf16) {
             uint16_t* out = static_cast<uint16_t*>(g.out) + (int64_t)m * g.ldo;
-            if (g.vec_store && n + 16 <= g.N) {
+            if (g.vec_store && n + 16 <= n_out) {
               u32x4* o = reinterpret_cast<u32x4*>(out + n);
               o[0] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                            pack_bf16x2(v[6], v[7])};
@@ -528,14 +549,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
             } else {
 #pragma unroll
               for (int r = 0; r < 16; ++r)
-                if (n + r < g.N) {
+                if (n + r < n_out) {
                   const __bf16 b = (__bf16)v[r];
                   __builtin_memcpy(out + n + r, &b, 2);
                 }
             }
           } else {
             float* out = static_cast<float*>(g.out) + (int64_t)m * g.ldo;
-            if (g.vec_store && n + 16 <= g.N) {
+            if (g.vec_store && n + 16 <= n_out) {
               u32x4* o = reinterpret_cast<u32x4*>(out + n);
 #pragma unroll
               for (int q4 = 0; q4 < 4; ++q4)
@@ -544,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
             } else {
 #pragma unroll
               for (int r = 0; r < 16; ++r)
-                if (n + r < g.N) out[n + r] = v[r];
+                if (n + r < n_out) out[n + r] = v[r];
             }
           }
         }
@@ -553,31 +574,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   }
 }
 
+template <int WF, int XF, int EPI>
+void launch_epi(const GemmArgs& a, int out_kind, int out_fmt, dim3 grid, dim3 block, hipStream_t stream) {
+  if (out_kind == kOutF32)
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, EPI, kFmtE2M3>), grid, block, 0, stream, a);
+  else if (out_kind == kOutBf16)
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, EPI, kFmtE2M3>), grid, block, 0, stream, a);
+  else if (out_fmt == kFmtE2M3)
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE2M3>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE3M2>), grid, block, 0, stream, a);
+}
+
 template <int WF, int XF>
 hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream) {
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
-  const bool gelu = epilogue == kEpiGeluTanh;
-  if (out_kind == kOutF32) {
-    if (gelu)
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, true, kFmtE2M3>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, false, kFmtE2M3>), grid, block, 0, stream, a);
-  } else if (out_kind == kOutBf16) {
-    if (gelu)
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, true, kFmtE2M3>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, false, kFmtE2M3>), grid, block, 0, stream, a);
-  } else if (out_fmt == kFmtE2M3) {
-    if (gelu)
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, true, kFmtE2M3>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, false, kFmtE2M3>), grid, block, 0, stream, a);
-  } else {
-    if (gelu)
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, true, kFmtE3M2>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, false, kFmtE3M2>), grid, block, 0, stream, a);
-  }
+  if (epilogue == kEpiGeluTanh)
+    launch_epi<WF, XF, kEpiGeluTanh>(a, out_kind, out_fmt, grid, block, stream);
+  else if (epilogue == kEpiSwiglu)
+    launch_epi<WF, XF, kEpiSwiglu>(a, out_kind, out_fmt, grid, block, stream);
+  else
+    launch_epi<WF, XF, kEpiNone>(a, out_kind, out_fmt, grid, block, stream);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ constexpr int kPlaneB = 1024;
 
 constexpr int kEpiNone = 0;
 constexpr int kEpiGeluTanh = 1;
+constexpr int kEpiSwiglu = 2;   // stacked gate/up rows (runs of 64 + 64), out[:, f] = silu(gate f) * up f
 
 // Main GEMM tile: 256 tokens x 256 output features, K staged 128 at a time.
 constexpr int kTileM = 256;

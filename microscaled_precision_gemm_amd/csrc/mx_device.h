@@ -122,4 +122,13 @@ __device__ __forceinline__ float gelu_tanh_f32(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + t);
 }
 
+// SiLU in fp32: x * sigmoid(x) = x / (1 + e^{-x}), with e^{-x} taken as
+// 2^{-x log2 e} by the hardware exp2 and the quotient by the hardware
+// reciprocal; for very negative x the power overflows to +inf and the result
+// is x * 0 = -0.
+__device__ __forceinline__ float silu_f32(float x) {
+  constexpr float kNegLog2e = -1.4426950408889634f;
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * kNegLog2e));
+}
+
 }  // namespace mxg

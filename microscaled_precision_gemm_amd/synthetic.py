@@ -18,7 +18,13 @@ proj       4096 x 3072 x 3072          A ~ N(0, 1), W ~ N(0, 0.02), bf16 out
 fc1        20480 x 3072 x 12288        A ~ N(0, 1), W ~ N(0, 0.02), GELU -> E2M3
 fc2        20480 x 12288 x 3072        A ~ Student-t(3), 0.1 % of K channels x50
 skinny     {8, 16} x 16384 x 13312     A ~ N(0, 1), W ~ N(0, 0.02) as E3M2
+sw_fc1     20480 x 3072 x 16384        SwiGLU MLP: stacked gate/up rows (2 x 8192),
+                                       A ~ N(0, 1), W ~ N(0, 0.02), SwiGLU -> E2M3
+sw_fc2     20480 x 8192 x 3072         A ~ Student-t(3), 0.1 % of K channels x50
 =========  ==========================  ===========================================
+
+The SwiGLU MLP uses 8192 = 2/3 * 4 * 3072 hidden features, so its three weight
+matrices hold as many parameters as the GELU MLP's two.
 
 Recipe: numpy ``default_rng([workload_index, stream])`` with stream 0 = A,
 1 = W, 2 = the outlier-channel choice; draws are float32, then rounded to
@@ -54,6 +60,8 @@ WORKLOADS = {
     "fc1": Workload("fc1", 3, 20480, 3072, 12288, "normal", 1.0, 0.02, "e2m3", "mx"),
     "fc2": Workload("fc2", 4, 20480, 12288, 3072, "student_t_outliers", 1.0, 0.02, "e2m3", "bf16"),
     "skinny": Workload("skinny", 5, 16, 16384, 13312, "normal", 1.0, 0.02, "e3m2", "bf16", 16),
+    "sw_fc1": Workload("sw_fc1", 6, 20480, 3072, 16384, "normal", 1.0, 0.02, "e2m3", "mx"),
+    "sw_fc2": Workload("sw_fc2", 7, 20480, 8192, 3072, "student_t_outliers", 1.0, 0.02, "e2m3", "bf16"),
 }
 
 T_NU = 3.0

@@ -126,6 +126,19 @@ def gelu_eval_slack(c: np.ndarray, g: np.ndarray) -> np.ndarray:
     return (8.0 + 1.2 * arg) * O.ulp_fp32(g) + 1e-44
 
 
+SILU_DERIV_MAX = 1.1  # max |d/dx silu(x)| is about 1.0998
+
+
+def swiglu_bound(gate: np.ndarray, up: np.ndarray, s_gate: np.ndarray, s_up: np.ndarray,
+                 out: np.ndarray) -> np.ndarray:
+    """Distance the device's fp32 silu(gate) * up may lie from the exact value:
+    the gate / up accumulation errors (<= 1e-5 S each) through the product's
+    partial derivatives (|silu'| <= 1.1 times |up|, and |silu(gate)|), plus the
+    fp32 evaluation of silu (its exp2 argument's rounding grows with |gate|)."""
+    acc = O.GEMM_RTOL * (SILU_DERIV_MAX * np.abs(up) * s_gate + np.abs(O.silu(gate)) * s_up)
+    return acc + (8.0 + 1.2 * np.abs(gate)) * O.ulp_fp32(out) + 1e-44
+
+
 def check_mx_epilogue(gpu_codes: np.ndarray, gpu_scales: np.ndarray, c: np.ndarray, s: np.ndarray, gelu: bool,
                       fmt: str = "e2m3") -> dict:
     """Compare a fused-epilogue MX output (GELU or identity, then MX along N)
@@ -139,14 +152,22 @@ def check_mx_epilogue(gpu_codes: np.ndarray, gpu_scales: np.ndarray, c: np.ndarr
     of a power of two, the scale byte may differ by one.  Everything else must
     match exactly.  Returns counts of exact and tolerated differences.
     """
-    n = c.shape[1]
     g64 = O.gelu_tanh(c) if gelu else c
     g32 = g64.astype(np.float32).astype(np.float64)
+    delta = O.GEMM_RTOL * s * (GELU_DERIV_MAX if gelu else 1.0) + (gelu_eval_slack(c, g32) if gelu else 0.0)
+    return check_mx_values(gpu_codes, gpu_scales, g32, delta, fmt)
+
+
+def check_mx_values(gpu_codes: np.ndarray, gpu_scales: np.ndarray, g32: np.ndarray, delta: np.ndarray,
+                    fmt: str = "e2m3") -> dict:
+    """The boundary-aware comparison of a fused MX output with the oracle's
+    quantization of its fp32 values g32, given the distance delta by which the
+    device's fp32 values may differ from them (see check_mx_epilogue)."""
+    n = g32.shape[1]
     codes_o, scales_o = O.quantize(g32, fmt)
     codes_g = O.unpack(gpu_codes, n)
     deq_o = O.dequantize(codes_o, scales_o, fmt)
     deq_g = O.dequantize(codes_g, gpu_scales, fmt)
-    delta = O.GEMM_RTOL * s * (GELU_DERIV_MAX if gelu else 1.0) + (gelu_eval_slack(c, g32) if gelu else 0.0)
     delta = delta + O.ulp_fp32(g32)  # the oracle's own fp32 rounding of g
     rows, nb = scales_o.shape
     su_o = scales_o.astype(np.int64)

@@ -123,6 +123,11 @@ def test_gemm_validation(L):
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=120, ws=FAKE, ws_bytes=need) == B.MX_ERR_SHAPE
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=130, ws=FAKE, ws_bytes=need) == B.MX_ERR_ALIGN
     assert g(m=0) == B.MX_OK and g(n=0) == B.MX_OK  # empty is a no-op
+    # SwiGLU: stacked gate/up rows come in runs of 128; the output has n / 2 columns
+    assert g(epi=2, n=192, ldo=96) == B.MX_ERR_UNSUPPORTED
+    assert g(epi=2, n=128, ldo=63) == B.MX_ERR_SHAPE
+    assert g(epi=2, n=128, ldo=64, m=0) == B.MX_OK
+    assert g(epi=2, n=128, out_kind=2, out_scales=FAKE, m=0) == B.MX_OK
 
 
 def sk(**kw):

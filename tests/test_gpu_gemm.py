@@ -225,3 +225,63 @@ def test_splitk_matches_plain_gemm_property():
     torch.cuda.synchronize()
     for o in outs + [plain]:
         assert_fp32_close(to_np(o).astype(np.float64), c, s, "split count")
+
+
+# ---------------------------------------------------------------- SwiGLU epilogue
+
+def _swiglu_operands(m, h, k, a_fmt="e2m3", w_fmt="e2m3", seed=0):
+    a, w = syn.random_like_workload(seed, m, k, 2 * h, a_std=1.0, w_std=0.05)
+    qa = O.quantize(a.to(torch.float64).numpy(), a_fmt)
+    qw = O.quantize(w.to(torch.float64).numpy(), w_fmt)
+    out, gate, up, sg, su = O.swiglu_ref(O.dequantize(*qa, a_fmt), O.dequantize(*qw, w_fmt))
+    return a, w, qa, qw, out, gate, up, sg, su
+
+
+@pytest.mark.parametrize("a_fmt,w_fmt", FORMAT_PAIRS)
+@pytest.mark.parametrize("m,h,k", [(300, 320, 416), (37, 192, 160), (256, 128, 256)])
+def test_swiglu_f32_and_bf16(a_fmt, w_fmt, m, h, k):
+    """Stacked gate/up GEMM with the SwiGLU epilogue, fp32 and bf16 outputs,
+    over several tiles, ragged M and a ragged last N tile (n = 2h = 640, 384)."""
+    from tests.parity import swiglu_bound
+    a, w, qa, qw, out, gate, up, sg, su = _swiglu_operands(m, h, k, a_fmt, w_fmt, seed=m + h)
+    say(f"gemm swiglu f32/bf16 {m}x{2 * h}x{k} a={a_fmt} w={w_fmt}")
+    wq = _gpu_weights(w, w_fmt, qw)
+    o32 = mx.mx_gemm(a.cuda(), wq, out_kind="f32", epilogue="swiglu", a_fmt=a_fmt)
+    o16 = mx.mx_gemm(a.cuda(), wq, out_kind="bf16", epilogue="swiglu", a_fmt=a_fmt)
+    torch.cuda.synchronize()
+    assert tuple(o32.shape) == (m, h)
+    bound = swiglu_bound(gate, up, sg, su, out)
+    got = to_np(o32).astype(np.float64)
+    bad = np.argwhere(np.abs(got - out) > bound)
+    assert bad.size == 0, f"{len(bad)} SwiGLU outputs off; first {bad[0].tolist()}"
+    g16 = bf16_tensor_to_f64(o16)
+    # bf16: the device rounds its own fp32 value once
+    bad = np.argwhere(np.abs(g16 - out) > bound + O.ulp_bf16(out))
+    assert bad.size == 0, f"{len(bad)} bf16 SwiGLU outputs off; first {bad[0].tolist()}"
+
+
+@pytest.mark.parametrize("out_fmt", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("m,h,k", [(300, 320, 416), (64, 64, 128)])
+def test_swiglu_mx_out(out_fmt, m, h, k):
+    """SwiGLU -> MX re-quantization along the h output features, under the
+    boundary-aware rule; the padding of the tiled output is checked too."""
+    from tests.parity import check_mx_values, swiglu_bound
+    a, w, qa, qw, out, gate, up, sg, su = _swiglu_operands(m, h, k, seed=3 * m + h)
+    say(f"gemm swiglu mx-out {m}x{2 * h}x{k} out={out_fmt}")
+    wq = _gpu_weights(w, "e2m3", qw)
+    o = mx.mx_gemm(a.cuda(), wq, out_kind="mx", epilogue="swiglu", out_fmt=out_fmt)
+    torch.cuda.synchronize()
+    assert o.rows == m and o.k == h
+    oc, os_ = mx_rows_view(o)
+    o32 = out.astype(np.float32).astype(np.float64)
+    stats = check_mx_values(oc, os_, o32, swiglu_bound(gate, up, sg, su, o32), out_fmt)
+    print("swiglu mx", stats)
+    assert stats["exact"] >= 0.999 * stats["elements"], stats
+
+
+def test_swiglu_rejects_unpaired_rows():
+    w = torch.randn(192, 128).to(torch.bfloat16).cuda()
+    wq = mx.mx_quantize(w, "e2m3")
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_gemm(torch.randn(8, 128).to(torch.bfloat16).cuda(), wq, out_kind="f32", epilogue="swiglu")
+    assert e.value.status == mx.binding.MX_ERR_UNSUPPORTED

@@ -166,3 +166,70 @@ def test_skinny_full_size_splitk(m):
     assert_bf16_close(bf16_tensor_to_f64(out[:, ci]), c, s, "skinny bf16")
     assert_fp32_close(to_np(o32[:, ci]).astype(np.float64), c, s, "skinny f32")
     assert_fp32_close(to_np(o32_one[:, ci]).astype(np.float64), c, s, "skinny f32 one split")
+
+
+def _swiglu_sample_ref(x, w, rows, feats, h):
+    """Oracle SwiGLU of sampled tokens x sampled output features: the gate and
+    up rows of those features (stacked order from the oracle), their GEMMs on
+    the sampled token rows, silu(gate) * up."""
+    gate_rows, up_rows = O.swiglu_rows(h)
+    da = _deq_rows(x, rows, "e2m3")
+    g, sg = O.gemm_ref(da, _deq_rows(w, gate_rows[feats], "e2m3"))
+    u, su = O.gemm_ref(da, _deq_rows(w, up_rows[feats], "e2m3"))
+    return O.silu(g) * u, g, u, sg, su
+
+
+def test_swiglu_fc1_full_size_mx():
+    """SwiGLU fc1 20480 x 3072 x 16384 (stacked gate/up, 8192 features) with the
+    E2M3 re-quantization: sampled tokens x sampled whole 32-feature blocks under
+    the boundary-aware rule."""
+    from tests.parity import check_mx_values, swiglu_bound
+    w = syn.WORKLOADS["sw_fc1"]
+    h = w.n // 2
+    x, wt = syn.make_a(w), syn.make_w(w)
+    rng = np.random.default_rng([80, w.index])
+    rows = _pick(w.m, ROW_SAMPLE, rng)
+    blocks = _pick(h // 32, BLOCK_SAMPLE, rng)
+    feats = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    say(f"workload sw_fc1 {w.m}x{w.k}x{w.n} swiglu->e2m3")
+    dev = torch.device("cuda:0")
+    xq = mx.mx_quantize(x.to(dev), "e2m3")
+    wq = mx.mx_quantize(wt.to(dev), "e2m3")
+    hq = mx.MXTensor.empty(w.m, h, "e2m3", "tiled", dev)
+    mx.mx_gemm(xq, wq, out_kind="mx", epilogue="swiglu", out=hq)
+    torch.cuda.synchronize()
+    gc, gs = mx_rows_view(hq)
+    codes_g = O.unpack(gc[rows], h)[:, feats]
+    out, g, u, sg, su = _swiglu_sample_ref(x, wt, rows, feats, h)
+    o32 = out.astype(np.float32).astype(np.float64)
+    stats = check_mx_values(O.pack(codes_g), gs[rows][:, blocks], o32, swiglu_bound(g, u, sg, su, o32), "e2m3")
+    assert stats["exact"] >= 0.999 * stats["elements"], stats
+
+
+def test_swiglu_mlp_chain_full_size():
+    """The SwiGLU MLP step: quantize x, stacked gate/up GEMM with SwiGLU -> E2M3
+    (8192 features), down projection to bf16, at full size; sampled tokens of the
+    output against the oracle's own chain (as for the GELU chain)."""
+    w1w, w2w = syn.WORKLOADS["sw_fc1"], syn.WORKLOADS["sw_fc2"]
+    h = w1w.n // 2
+    x, w1, w2 = syn.make_a(w1w), syn.make_w(w1w), syn.make_w(w2w)
+    rng = np.random.default_rng([81, w1w.index])
+    rows = _pick(w1w.m, 8, rng)
+    cols = _pick(w2w.n, COL_SAMPLE, rng)
+    say("workload SwiGLU MLP chain 20480 tokens")
+    dev = torch.device("cuda:0")
+    xq = mx.mx_quantize(x.to(dev), "e2m3")
+    w1q, w2q = mx.mx_quantize(w1.to(dev), "e2m3"), mx.mx_quantize(w2.to(dev), "e2m3")
+    hq = mx.mx_gemm(xq, w1q, out_kind="mx", epilogue="swiglu")
+    y = mx.mx_gemm(hq, w2q, out_kind="bf16")
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)])
+    codes_o, scales_o, *_ = O.fc1_swiglu_mx_ref(_deq_rows(x, rows, "e2m3"), _deq_rows(w1, np.arange(w1w.n), "e2m3"))
+    dh = O.dequantize(codes_o, scales_o, "e2m3")
+    dw2 = _deq_rows(w2, cols, "e2m3")
+    c2, s2 = O.gemm_ref(dh, dw2)
+    step = np.ldexp(1.0, scales_o.astype(np.int64) - 127 - 2)
+    flip_bound = np.repeat(step, 32, axis=1) @ np.abs(dw2).T
+    ok, _ = O.check_bf16(got, c2, s2)
+    assert ok.mean() > 0.99, ok.mean()
+    assert np.all(np.abs(got - c2) <= flip_bound + O.GEMM_RTOL * s2 + O.ulp_bf16(c2))
