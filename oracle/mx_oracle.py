@@ -29,6 +29,16 @@ computes, in float64 with numpy:
   The stacking order is the library's own: in each run of 128 stacked rows,
   the first 64 are gate rows of 64 consecutive features, the next 64 the up
   rows of the same features.
+* The quantize-once producer of the projection and MLP inputs (same section:
+  modulation and RMSNorm fused, activations quantized once): RMSNorm (Zhang
+  and Sennrich, "Root Mean Square Layer Normalization", 2019, with the usual
+  eps inside the root) with a per-feature gain, then the adaptive-norm
+  modulation of diffusion transformers (Peebles and Xie, "Scalable Diffusion
+  Models with Transformers", 2023): y = norm(x) * (1 + scale) + shift, with
+  one (shift, scale) pair of vectors per conditioning (sample), then MX
+  quantization of y along the row.  The fused RMSNorm kernel of "Creating
+  Custom Kernels for the AMD MI300" (section "Fused RMS Norm Kernel") is the
+  MI300X counterpart.
 
 Readings where the pages are silent (also listed in the design doc):
 
@@ -305,6 +315,36 @@ def fc1_swiglu_mx_ref(a_deq: np.ndarray, w_stacked_deq: np.ndarray, out_fmt: str
     out, gate, up, sg, su = swiglu_ref(a_deq, w_stacked_deq)
     codes, scales = quantize(out.astype(np.float32).astype(np.float64), out_fmt)
     return codes, scales, out, gate, up, sg, su
+
+
+def rmsnorm_modulate(x: np.ndarray, gamma=None, shift=None, scale=None, rows_per_cond: int | None = None,
+                     eps: float = 1e-6) -> np.ndarray:
+    """y[r] = x[r] / sqrt(mean(x[r]**2) + eps) * gamma * (1 + scale[c]) + shift[c],
+    c = r // rows_per_cond, in float64.  gamma [d] (None = ones); shift and
+    scale [n_cond, d] (None = zeros)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, d = x.shape
+    inv = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    y = x * inv
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)[None, :]
+    if scale is not None or shift is not None:
+        per = rows if rows_per_cond is None else rows_per_cond
+        c = np.arange(rows) // per
+        if scale is not None:
+            y = y * (1.0 + np.asarray(scale, dtype=np.float64)[c])
+        if shift is not None:
+            y = y + np.asarray(shift, dtype=np.float64)[c]
+    return y
+
+
+def rmsnorm_quantize_ref(x: np.ndarray, gamma=None, shift=None, scale=None, rows_per_cond=None, eps: float = 1e-6,
+                         fmt: str = "e2m3"):
+    """The producer's output: MX quantization of fp32(rmsnorm_modulate(x)).
+    Returns (codes, scales, y64)."""
+    y = rmsnorm_modulate(x, gamma, shift, scale, rows_per_cond, eps)
+    codes, scales = quantize(y.astype(np.float32).astype(np.float64), fmt)
+    return codes, scales, y
 
 
 # ---------------------------------------------------------------------------

@@ -384,3 +384,49 @@ def test_fc1_swiglu_reference_is_quantized_product():
     spacing = np.ldexp(1.0, np.maximum(O.floor_log2(np.where(r > 0, r, 1.0)), 0) - 3)
     allowed = np.where(r > 7.5, r - 7.5, 0.5 * spacing) * unit
     assert np.all(np.abs(deq - o32) <= allowed * (1 + 1e-12))
+
+
+# ---------------------------------------------------------------- RMSNorm + modulation producer
+
+def test_rmsnorm_matches_torch():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((7, 96)) * np.exp2(rng.integers(-6, 6, (7, 1)))
+    g = rng.standard_normal(96)
+    for eps in (1e-6, 1e-2):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), eps).numpy()
+        np.testing.assert_allclose(O.rmsnorm_modulate(x, g, eps=eps), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_rmsnorm_invariants():
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((5, 128))
+    y = O.rmsnorm_modulate(x, eps=0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-13)  # unit root mean square
+    np.testing.assert_allclose(O.rmsnorm_modulate(3.5 * x, eps=0.0), y, rtol=1e-13)  # scale invariant
+    np.testing.assert_allclose(O.rmsnorm_modulate(-x, eps=0.0), -y, rtol=1e-13)
+
+
+def test_modulation_per_condition():
+    """y = norm(x) * (1 + scale[c]) + shift[c] with c = row // rows_per_cond,
+    checked row by row against torch's rms_norm."""
+    rng = np.random.default_rng(23)
+    rows, d, per = 6, 64, 2
+    x = rng.standard_normal((rows, d))
+    g = rng.standard_normal(d)
+    sh = rng.standard_normal((rows // per, d))
+    sc = rng.standard_normal((rows // per, d))
+    y = O.rmsnorm_modulate(x, g, sh, sc, per, eps=1e-5)
+    for r in range(rows):
+        n = torch.nn.functional.rms_norm(torch.from_numpy(x[r:r + 1]), (d,), torch.from_numpy(g), 1e-5).numpy()[0]
+        np.testing.assert_allclose(y[r], n * (1 + sc[r // per]) + sh[r // per], rtol=1e-13, atol=1e-14)
+    # zero modulation is the plain norm
+    np.testing.assert_allclose(O.rmsnorm_modulate(x, g, np.zeros((3, d)), np.zeros((3, d)), per),
+                               O.rmsnorm_modulate(x, g), rtol=0, atol=0)
+
+
+def test_rmsnorm_quantize_reference():
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((4, 64))
+    codes, scales, y = O.rmsnorm_quantize_ref(x)
+    ref_codes, ref_scales = O.quantize(y.astype(np.float32).astype(np.float64), "e2m3")
+    assert np.array_equal(codes, ref_codes) and np.array_equal(scales, ref_scales)

@@ -65,6 +65,26 @@ def _swiglu_rows_contiguous(h):
     return f, f + h
 
 
+def _rms_eps_outside(x, gamma=None, shift=None, scale=None, rows_per_cond=None, eps=1e-6):
+    x = np.asarray(x, dtype=np.float64)
+    y = x / (np.sqrt(np.mean(x * x, axis=1, keepdims=True)) + eps)
+    return y * (1.0 if gamma is None else np.asarray(gamma)[None, :])
+
+
+def _rms_scale_not_plus_one(x, gamma=None, shift=None, scale=None, rows_per_cond=None, eps=1e-6):
+    x = np.asarray(x, dtype=np.float64)
+    y = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma)[None, :]
+    rows = x.shape[0]
+    c = np.arange(rows) // (rows if rows_per_cond is None else rows_per_cond)
+    if scale is not None:
+        y = y * np.asarray(scale)[c]
+    if shift is not None:
+        y = y + np.asarray(shift)[c]
+    return y
+
+
 def _bias_off(fmt):
     e, m, b = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3)}[fmt]
     return (e, m, b + 1)
@@ -82,6 +102,8 @@ MUTANTS = [
     ("silu", _silu_doubled, [pins.test_silu_matches_torch]),
     ("swiglu_rows", _swiglu_rows_swapped, [pins.test_swiglu_stacking_and_product]),
     ("swiglu_rows", _swiglu_rows_contiguous, [pins.test_swiglu_stacking_and_product]),
+    ("rmsnorm_modulate", _rms_eps_outside, [pins.test_rmsnorm_matches_torch]),
+    ("rmsnorm_modulate", _rms_scale_not_plus_one, [pins.test_modulation_per_condition]),
 ]
 
 
