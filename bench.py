@@ -167,6 +167,34 @@ def bench_swiglu_mlp(steps: int, warmup: int):
             "fc2_ms": round(float(f2), 4), "fc2_tflops": round(fl2 / f2 / 1e9, 1)}
 
 
+def bench_producer(iters: int = 50):
+    """The quantize-once producer on fc1's input: RMSNorm with a gain, two
+    conditionings of 10240 rows (modulation), MX E2M3 into the tiled layout.
+    HBM-bound: algorithmic bytes = the bf16 input once + the packed output."""
+    w = syn.WORKLOADS["fc1"]
+    dev = torch.device("cuda:0")
+    x = syn.make_a(w).to(dev)
+    g = torch.ones(w.k, dtype=torch.float32, device=dev)
+    sh = torch.zeros((2, w.k), dtype=torch.float32, device=dev)
+    sc = torch.zeros((2, w.k), dtype=torch.float32, device=dev)
+    out = mx.MXTensor.empty(w.m, w.k, "e2m3", "tiled", dev)
+
+    def call():
+        mx.mx_rmsnorm_quantize(x, g, sh, sc, 10240, 1e-6, "e2m3", out=out)
+
+    settle(call, 0.2)
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(iters):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    alg = w.m * w.k * 2 + w.m * w.k * 3 // 4 + w.m * w.k // 32
+    return {"workload": "RMSNorm + modulation + E2M3 of 20480x3072 bf16 (fc1 input)", "ms": round(ms, 4),
+            "algorithmic_bytes": alg, "gb_s": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
 def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
     w = syn.WORKLOADS["skinny"]
     dev = torch.device("cuda:0")
@@ -291,6 +319,7 @@ def main():
     achieved = r["flops_per_gemm"] / dom_ms / 1e9
     skinny = [bench_skinny(16, 16, args.skinny_iters), bench_skinny(8, 16, args.skinny_iters)]
     swiglu = bench_swiglu_mlp(args.steps, args.warmup)
+    producer = bench_producer()
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -317,6 +346,7 @@ def main():
                        "quantize_gb_s": round(r["quantize_bytes"] / r["quantize_ms"] / 1e6, 1)},
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
         "swiglu_mlp": swiglu,
+        "producer": producer,
     }
     if args.copy_calibration:
         line["copy_calibration"] = copy_calibration()

@@ -143,6 +143,41 @@ int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int6
                 int32_t layout, void* codes, uint8_t* scales, hipStream_t stream);
 
 /*
+ * mx_rmsnorm_quantize - the quantize-once producer of a GEMM's activations:
+ * RMSNorm, the adaptive-norm modulation, and MX quantization in one pass
+ * (the Hedra post, section "Fusion cut intermediate memory traffic": the
+ * modulation and RMSNorm producers are fused and the activations are
+ * quantized once).  For each row r of x:
+ *
+ *   inv    = 1 / sqrt(mean_k x[r,k]^2 + eps)
+ *   y[r,k] = x[r,k] * inv * gamma[k] * (1 + scale[c,k]) + shift[c,k],
+ *            c = r / rows_per_cond,
+ *
+ * evaluated in fp32, then y is MX-quantized along the row exactly as
+ * mx_quantize quantizes an fp32 source, into MX_LAYOUT_TILED.
+ *
+ *   x         device bf16 (src_type MX_SRC_BF16) or fp32 [rows, d], row r at
+ *             x + r * ld_x elements; 16-byte aligned, ld_x * element size a
+ *             multiple of 16.
+ *   rows, d   rows >= 0, d >= 0, d % 32 == 0; rows == 0 or d == 0 is a no-op.
+ *   gamma     device fp32 [d] gain, or NULL for ones.
+ *   shift, scale  device fp32 [ceil(rows / rows_per_cond), d] modulation
+ *             vectors, either may be NULL (zeros).  When either is given,
+ *             rows_per_cond must be a positive multiple of 32 (every 32-row
+ *             group of the output shares one conditioning row); otherwise it
+ *             is ignored.
+ *   eps       >= 0, finite.
+ *   fmt       MX_FMT_E2M3 or MX_FMT_E3M2.
+ *   codes, scales  outputs of mx_packed_bytes(rows, d, MX_LAYOUT_TILED, 0 / 1)
+ *             bytes (16- and 4-byte aligned), padding included.
+ * The result follows the fp32 evaluation above; it is not bit-identical to a
+ * float64 evaluation where y lies at a rounding boundary of its code.
+ */
+int mx_rmsnorm_quantize(const void* x, int32_t src_type, int64_t rows, int64_t d, int64_t ld_x, const float* gamma,
+                        const float* shift, const float* scale, int64_t rows_per_cond, float eps, int32_t fmt,
+                        void* codes, uint8_t* scales, hipStream_t stream);
+
+/*
  * mx_packed_bytes - size in bytes of the codes (which == 0) or scales
  * (which == 1) buffer of a [rows, k] MX matrix in the given layout; 0 for
  * invalid arguments.

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     mx_gemm_workspace_size,
     mx_packed_bytes,
     mx_quantize,
+    mx_rmsnorm_quantize,
     mx_status_string,
     mx_version,
 )

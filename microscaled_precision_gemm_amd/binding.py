@@ -45,8 +45,8 @@ OUT_KINDS = {"f32": MX_OUT_F32, "bf16": MX_OUT_BF16, "mx": MX_OUT_MX}
 EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH, "swiglu": MX_EPI_SWIGLU}
 LAYOUTS = {"rows": MX_LAYOUT_ROWS, "tiled": MX_LAYOUT_TILED}
 
-EXPORTED = ("mx_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_splitk", "mx_gemm_workspace_size",
-            "mx_status_string", "mx_version")
+EXPORTED = ("mx_quantize", "mx_rmsnorm_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_splitk",
+            "mx_gemm_workspace_size", "mx_status_string", "mx_version")
 
 
 class MXError(RuntimeError):
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
     c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     L.mx_quantize.argtypes = [c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32, c_p, c_p, c_p]
     L.mx_quantize.restype = ctypes.c_int
+    L.mx_rmsnorm_quantize.argtypes = [c_p, c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_i64, ctypes.c_float, c_i32,
+                                      c_p, c_p, c_p]
+    L.mx_rmsnorm_quantize.restype = ctypes.c_int
     L.mx_packed_bytes.argtypes = [c_i64, c_i64, c_i32, c_i32]
     L.mx_packed_bytes.restype = c_sz
     L.mx_gemm.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32,
@@ -204,6 +207,34 @@ def mx_quantize(src: torch.Tensor, fmt: str = "e2m3", layout: str = "tiled", out
     st = lib().mx_quantize(_ptr(src), _src_type(src), rows, k, src.stride(0), _fmt(fmt), LAYOUTS[layout],
                            _ptr(out.codes), _ptr(out.scales), _stream(dev))
     _check(st, "mx_quantize")
+    return out
+
+
+def mx_rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor | None = None, shift: torch.Tensor | None = None,
+                        scale: torch.Tensor | None = None, rows_per_cond: int = 0, eps: float = 1e-6,
+                        fmt: str = "e2m3", out: MXTensor | None = None) -> MXTensor:
+    """RMSNorm + modulation + MX quantization of x [rows, d] into the tiled
+    layout (the GEMM operand).  gamma: fp32 [d]; shift / scale: fp32
+    [n_cond, d] with rows_per_cond rows per conditioning row (a multiple of 32)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [rows, d] with unit stride along d")
+    dev = _require_cuda(x)
+    rows, d = x.shape
+    for name, v in (("gamma", gamma), ("shift", shift), ("scale", scale)):
+        if v is not None:
+            if v.dtype != torch.float32 or not v.is_contiguous() or v.device != dev:
+                raise ValueError(f"{name} must be a contiguous fp32 tensor on {dev}")
+            if v.shape[-1] != d:
+                raise ValueError(f"{name} must have d = {d} features")
+    if out is None:
+        out = MXTensor.empty(rows, d, fmt, "tiled", dev)
+    if out.rows != rows or out.k != d or out.layout != "tiled":
+        raise ValueError("out must be a tiled [rows, d] MX matrix")
+    _check_mx(out, "out")
+    st = lib().mx_rmsnorm_quantize(_ptr(x), _src_type(x), rows, d, x.stride(0), _ptr(gamma), _ptr(shift), _ptr(scale),
+                                   rows_per_cond, float(eps), _fmt(fmt), _ptr(out.codes), _ptr(out.scales),
+                                   _stream(dev))
+    _check(st, "mx_rmsnorm_quantize")
     return out
 
 

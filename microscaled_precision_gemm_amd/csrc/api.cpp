@@ -110,6 +110,33 @@ const char* mx_status_string(int status) {
   }
 }
 
+int mx_rmsnorm_quantize(const void* x, int32_t src_type, int64_t rows, int64_t d, int64_t ld_x, const float* gamma,
+                        const float* shift, const float* scale, int64_t rows_per_cond, float eps, int32_t fmt,
+                        void* codes, uint8_t* scales, hipStream_t stream) {
+  int st = check_quantize_args(x, src_type, rows, d, ld_x, fmt, MX_LAYOUT_TILED, codes, scales);
+  if (st != MX_OK) return st;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return MX_ERR_SHAPE;  // rejects NaN, negative and infinite eps
+  const bool modulated = shift != nullptr || scale != nullptr;
+  if (modulated && (rows_per_cond <= 0 || rows_per_cond % 32 != 0)) return MX_ERR_SHAPE;
+  if (rows == 0 || d == 0) return MX_OK;
+  if (!aligned(gamma, 4) || !aligned(shift, 4) || !aligned(scale, 4)) return MX_ERR_ALIGN;
+  if (tiled_codes_bytes(rows, d) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
+  ProducerArgs a;
+  a.x = x;
+  a.ld_bytes = ld_x * (src_type == MX_SRC_BF16 ? 2 : 4);
+  a.rows = (int32_t)rows;
+  a.d = (int32_t)d;
+  a.groups = (int32_t)ceil_div(rows, kTileGroupRows);
+  a.gamma = gamma;
+  a.shift = shift;
+  a.scale = scale;
+  a.rows_per_cond = modulated ? rows_per_cond : 0;
+  a.eps = eps;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.scales = scales;
+  return hip_status(launch_rmsnorm_quantize(a, src_type, fmt, stream));
+}
+
 size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which) {
   if (rows < 0 || k < 0 || k % 32 != 0 || rows > kMaxDim || k > kMaxDim || !valid_layout(layout)) return 0;
   if (which != 0 && which != 1) return 0;

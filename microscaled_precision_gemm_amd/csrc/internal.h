@@ -77,6 +77,22 @@ struct SplitKArgs {
 
 hipError_t launch_gemm_splitk(const SplitKArgs& a, int x_fmt, int w_fmt, int out_kind, hipStream_t stream);
 
+// RMSNorm + modulation + MX quantization into the tiled layout (one workgroup per 32-row group).
+struct ProducerArgs {
+  const void* x;            // bf16 / fp32 [rows, d], row r at x + r * ld_bytes
+  int64_t ld_bytes;
+  int32_t rows, d, groups;  // groups = ceil(rows / 32)
+  const float* gamma;       // [d] or null (ones)
+  const float* shift;       // [n_cond, d] or null (zeros)
+  const float* scale;       // [n_cond, d] or null (zeros)
+  int64_t rows_per_cond;    // a multiple of 32 (0 when shift and scale are null)
+  float eps;
+  uint8_t* codes;           // tiled layout of the [rows, d] output
+  uint8_t* scales;
+};
+
+hipError_t launch_rmsnorm_quantize(const ProducerArgs& a, int src_type, int fmt, hipStream_t stream);
+
 }  // namespace mxg
 
 namespace mxg {

@@ -1,0 +1,224 @@
+// Quantize-once producer for gfx950: RMSNorm + adaptive-norm modulation + MX
+// quantization into the tiled GEMM operand layout, in one kernel.
+//
+// The Krea 3 / MI355X post (section "Fusion cut intermediate memory traffic")
+// fuses the modulation and RMSNorm that produce the projection and MLP inputs
+// and quantizes the activations once.  Per row r of x [rows, d]:
+//
+//   inv = 1 / sqrt(mean_k x[r,k]^2 + eps)
+//   y[r,k] = x[r,k] * inv * gamma[k] * (1 + scale[c,k]) + shift[c,k],  c = r / rows_per_cond
+//
+// then y is MX-quantized along the row (the rule of mx_quantize), written as
+// the tiled operand layout.  The MI300X counterpart is the page "Creating
+// Custom Kernels for the AMD MI300", section "Fused RMS Norm Kernel" (128-bit
+// coalesced loads, one block per row, a block-wide reduction); here:
+//
+//  * one workgroup (4 waves) per 32-row group.  Pass 1: each wave reduces the
+//    sum of squares of 8 rows with 16-byte loads (consecutive lanes on
+//    consecutive bytes, four loads in flight) and a wave-wide shuffle
+//    reduction, and parks 1/rms in LDS.  Pass 2: the waves take the group's
+//    128-element stages in turn, exactly as the tiled quantizer does (the chunk
+//    of 32 rows x 128 is staged through LDS so each lane owns two whole
+//    blocks of one row), apply the norm and the modulation in fp32 and convert
+//    with v_cvt_scalef32_2xpk16 (round to nearest even, saturating).
+//  * the second read of the group's rows comes from the caches: a group is
+//    32 rows (192 KB for d = 3072) and was streamed just before.
+//  * all rows of a group share one conditioning row (rows_per_cond is a
+//    multiple of 32), so the stage's gain and modulation vectors are folded
+//    into one (a, b) pair per feature in LDS.
+#include "internal.h"
+#include "mx_device.h"
+
+namespace mxg {
+
+namespace {
+
+constexpr int kPWaves = 4;
+constexpr int kPThreads = 64 * kPWaves;
+
+template <bool F32>
+struct PLayout {
+  static constexpr int kRowSrc = F32 ? 512 : 256;  // source bytes of one row of a 128-element stage
+  static constexpr int kRow = kRowSrc + 16;        // padded LDS row
+  static constexpr int kPieces = kRowSrc / 16;
+  static constexpr int kCopies = 32 * kPieces / 64;
+  static constexpr int kEsize = F32 ? 4 : 2;
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// 8 consecutive source elements (one 16-byte piece of bf16, or two of fp32) as fp32
+template <bool F32>
+__device__ __forceinline__ void piece_to_f32(const u32x4& w, float (&f)[4 * (F32 ? 1 : 2)]) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(w[e] << 16);
+      f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+}
+
+template <int FMT, bool F32>
+__global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const ProducerArgs a) {
+  using L = PLayout<F32>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_chunk[kPWaves * 32 * L::kRow];
+  __shared__ __attribute__((aligned(16))) float lds_ab[kPWaves][2][128];
+  __shared__ float lds_inv[32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = blockIdx.x;
+  const uint8_t* src = static_cast<const uint8_t*>(a.x);
+  const int d = a.d, kblocks = d / 32, stages = (d + kTileStageK - 1) / kTileStageK;
+
+  // ---- pass 1: 1 / rms of the group's rows, 8 rows per wave
+  constexpr int kElemsPerLoad = 16 / L::kEsize;   // 8 bf16 or 4 fp32 per lane and load
+  constexpr int kSpan = 64 * kElemsPerLoad;       // elements one wave load covers
+  for (int i = 0; i < 8; ++i) {
+    const int jr = wave * 8 + i;
+    const int row = grp * 32 + jr;
+    float ss = 0.0f;
+    if (row < a.rows) {
+      const uint8_t* xr = src + (int64_t)row * a.ld_bytes;
+      for (int k0 = 0; k0 < d; k0 += 4 * kSpan) {
+        u32x4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int e = k0 + u * kSpan + lane * kElemsPerLoad;
+          // plain (cached) loads: pass 2 reads the same rows again
+          w[u] = e < d ? *reinterpret_cast<const u32x4*>(xr + (int64_t)e * L::kEsize) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float f[4 * (F32 ? 1 : 2)];
+          piece_to_f32<F32>(w[u], f);
+#pragma unroll
+          for (int e = 0; e < 4 * (F32 ? 1 : 2); ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) lds_inv[jr] = row < a.rows ? 1.0f / __builtin_sqrtf(ss / (float)d + a.eps) : 0.0f;
+  }
+  __syncthreads();
+
+  // ---- pass 2: stages of the group, one wave at a time per stage
+  uint8_t* in = lds_chunk + wave * 32 * L::kRow;
+  float* va = lds_ab[wave][0];
+  float* vb = lds_ab[wave][1];
+  const int64_t cond = a.rows_per_cond > 0 ? (int64_t)grp * 32 / a.rows_per_cond : 0;
+  const float* sh = a.shift ? a.shift + cond * d : nullptr;
+  const float* sc = a.scale ? a.scale + cond * d : nullptr;
+  const int j = lane & 31, h = lane >> 5;
+  const int row = grp * 32 + j;
+  const float inv = lds_inv[j];
+  for (int stage = wave; stage < stages; stage += kPWaves) {
+#pragma unroll
+    for (int i = 0; i < L::kCopies; ++i) {
+      const int c = 64 * i + lane;
+      const int jr = c / L::kPieces, piece = c % L::kPieces;
+      const int r = grp * 32 + jr;
+      const int e = stage * kTileStageK + piece * (16 / L::kEsize);
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (r < a.rows && e < d)
+        v = *reinterpret_cast<const u32x4*>(src + (int64_t)r * a.ld_bytes + (int64_t)e * L::kEsize);
+      *reinterpret_cast<u32x4*>(in + jr * L::kRow + piece * 16) = v;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int k = stage * kTileStageK + 2 * lane + t;
+      float fa = 0.0f, fb = 0.0f;
+      if (k < d) {
+        fa = a.gamma ? a.gamma[k] : 1.0f;
+        if (sc) fa *= 1.0f + sc[k];
+        fb = sh ? sh[k] : 0.0f;
+      }
+      va[2 * lane + t] = fa;
+      vb[2 * lane + t] = fb;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    v6u q[2];
+    uint32_t sbyte[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int qb = 2 * h + t;
+      const uint8_t* p = in + j * L::kRow + qb * 32 * L::kEsize;
+      float y[32];
+#pragma unroll
+      for (int i = 0; i < 32 / (16 / L::kEsize); ++i) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * i);
+        float f[4 * (F32 ? 1 : 2)];
+        piece_to_f32<F32>(w, f);
+#pragma unroll
+        for (int e = 0; e < 4 * (F32 ? 1 : 2); ++e) {
+          const int kk = qb * 32 + i * (16 / L::kEsize) + e;  // element within the stage
+          y[i * (16 / L::kEsize) + e] = __builtin_fmaf(f[e] * inv, va[kk], vb[kk]);
+        }
+      }
+      uint32_t amax = 0;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t m = __float_as_uint(y[e]) & 0x7fffffffu;
+        amax = m > amax ? m : amax;
+      }
+      const BlockScale s = scale_from_f32_bits<FMT>(amax);
+      v16f even, odd;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        even[i] = y[2 * i];
+        odd[i] = y[2 * i + 1];
+      }
+      v6u r = cvt_f32x2x16<FMT>(even, odd, s.scale);
+      uint32_t byte = s.byte;
+      if (s.nonfinite) r = v6u{0, 0, 0, 0, 0, 0};
+      if (row >= a.rows || stage * 4 + qb >= kblocks) {  // padding
+        r = v6u{0, 0, 0, 0, 0, 0};
+        byte = 127u;
+      }
+      q[t] = r;
+      sbyte[t] = byte;
+    }
+    // the 48 code bytes of row j in the planes of half h of chunk (stage, grp)
+    const int64_t chunk = (int64_t)stage * a.groups + grp;
+    uint8_t* half = a.codes + chunk * kChunkCodes + h * kHalfBytes;
+    *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
+    *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
+    *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
+    *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
+    *reinterpret_cast<uint16_t*>(a.scales + chunk * kChunkScales + j * 4 + 2 * h) =
+        (uint16_t)(sbyte[0] | (sbyte[1] << 8));
+    // the next stage reuses this wave's LDS rows
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+}
+
+template <int FMT>
+void launch_fmt(const ProducerArgs& a, bool f32, hipStream_t stream) {
+  const dim3 grid((unsigned)a.groups), block(kPThreads);
+  if (f32)
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<FMT, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((rmsnorm_quantize_kernel<FMT, false>), grid, block, 0, stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_quantize(const ProducerArgs& a, int src_type, int fmt, hipStream_t stream) {
+  if (a.groups == 0 || a.d == 0) return hipSuccess;
+  if (fmt == kFmtE2M3)
+    launch_fmt<kFmtE2M3>(a, src_type == kSrcF32, stream);
+  else
+    launch_fmt<kFmtE3M2>(a, src_type == kSrcF32, stream);
+  return hipGetLastError();
+}
+
+}  // namespace mxg

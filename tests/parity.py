@@ -139,6 +139,24 @@ def swiglu_bound(gate: np.ndarray, up: np.ndarray, s_gate: np.ndarray, s_up: np.
     return acc + (8.0 + 1.2 * np.abs(gate)) * O.ulp_fp32(out) + 1e-44
 
 
+def rmsnorm_bound(x: np.ndarray, gamma, scale, rows_per_cond, eps: float, y: np.ndarray) -> np.ndarray:
+    """Distance the device's fp32 RMSNorm + modulation may lie from the exact y:
+    the sum of squares is accumulated per lane over d/64 terms and then over a
+    64-lane tree (relative error <= (d/64 + 6) 2^-24), the root and the
+    reciprocal add an ulp each, and the products x * inv * gamma * (1 + scale)
+    three more roundings; the final fma rounds once (an ulp of y)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, d = x.shape
+    inv = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    a = np.ones(d) if gamma is None else np.abs(np.asarray(gamma, dtype=np.float64))
+    t = np.abs(x) * inv * a[None, :]
+    if scale is not None:
+        c = np.arange(rows) // rows_per_cond
+        t = t * np.abs(1.0 + np.asarray(scale, dtype=np.float64)[c])
+    rel = (d / 64 + 6 + 2 + 4) * 2.0 ** -24
+    return t * rel + O.ulp_fp32(y) + 1e-44
+
+
 def check_mx_epilogue(gpu_codes: np.ndarray, gpu_scales: np.ndarray, c: np.ndarray, s: np.ndarray, gelu: bool,
                       fmt: str = "e2m3") -> dict:
     """Compare a fused-epilogue MX output (GELU or identity, then MX along N)

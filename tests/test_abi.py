@@ -87,6 +87,36 @@ def test_quantize_validation(L):
     assert q(NULL, 0, 4, 0, 0, 2, 1, NULL, NULL, s) == B.MX_OK
 
 
+def rq(**kw):
+    a = dict(x=FAKE, src_type=0, rows=64, d=128, ld=128, gamma=NULL, shift=NULL, scale=NULL, per=0,
+             eps=ctypes.c_float(1e-6), fmt=2, codes=FAKE, scales=FAKE, stream=NULL)
+    a.update(kw)
+    return mx.lib().mx_rmsnorm_quantize(*a.values())
+
+
+@host_only
+def test_rmsnorm_quantize_validation(L):
+    assert rq(d=100) == B.MX_ERR_SHAPE
+    assert rq(rows=-1) == B.MX_ERR_SHAPE
+    assert rq(ld=96) == B.MX_ERR_SHAPE
+    assert rq(src_type=5) == B.MX_ERR_FORMAT
+    assert rq(fmt=4) == B.MX_ERR_FORMAT
+    assert rq(x=NULL) == B.MX_ERR_NULL
+    assert rq(codes=NULL) == B.MX_ERR_NULL
+    assert rq(x=FAKE + 8) == B.MX_ERR_ALIGN
+    assert rq(ld=132) == B.MX_ERR_ALIGN
+    assert rq(scales=FAKE + 2) == B.MX_ERR_ALIGN
+    assert rq(gamma=FAKE + 2) == B.MX_ERR_ALIGN
+    assert rq(eps=ctypes.c_float(-1.0)) == B.MX_ERR_SHAPE
+    assert rq(eps=ctypes.c_float(float("nan"))) == B.MX_ERR_SHAPE
+    assert rq(eps=ctypes.c_float(float("inf"))) == B.MX_ERR_SHAPE
+    # modulation needs a positive multiple of 32 rows per conditioning row
+    assert rq(shift=FAKE) == B.MX_ERR_SHAPE
+    assert rq(scale=FAKE, per=48) == B.MX_ERR_SHAPE
+    assert rq(rows=0) == B.MX_OK and rq(d=0) == B.MX_OK
+    assert rq(rows=0, shift=FAKE, per=64) == B.MX_OK
+
+
 def g(**kw):
     a = dict(a_src=NULL, a_src_type=0, lda=0, a_codes=FAKE, a_scales=FAKE, a_fmt=2, w_codes=FAKE, w_scales=FAKE,
              w_fmt=2, m=64, n=64, k=128, epi=0, out_kind=1, out=FAKE, ldo=64, out_scales=NULL, out_fmt=2,
