@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 import microscaled_precision_gemm_amd as mx  # noqa: E402
 from microscaled_precision_gemm_amd import synthetic as syn  # noqa: E402
+from microscaled_precision_gemm_amd import tuning  # noqa: E402
 
 METRIC = "MXFP6 GEMM TFLOPS + % of 10.1 PF MFMA peak (DiT MLP 20480x3072x12288)"
 PEAK_MXFP6_TFLOPS = 10100.0
@@ -64,7 +65,7 @@ def settle(fn, seconds: float = SETTLE_S):
         torch.cuda.synchronize()
 
 
-def bench_mlp(steps: int, warmup: int):
+def bench_mlp(steps: int, warmup: int, tune: bool = True):
     fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
     m, d, hdim = fc1.m, fc1.k, fc1.n
     dev = torch.device("cuda:0")
@@ -74,6 +75,17 @@ def bench_mlp(steps: int, warmup: int):
     xq = mx.MXTensor.empty(m, d, "e2m3", "tiled", dev)
     h = mx.MXTensor.empty(m, hdim, "e2m3", "tiled", dev)
     y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
+    # per-shape tile order from the tuning table (tuned here, untimed, on these operands)
+    table = tuning.TuningTable()
+    tuned = {}
+    if tune:
+        mx.mx_quantize(x, "e2m3", "tiled", out=xq)
+        tuned["fc1"] = tuning.tune_gemm(table, xq, w1, out_kind="mx", epilogue="gelu_tanh")
+        h_t = mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh")
+        tuned["fc2"] = tuning.tune_gemm(table, h_t, w2, out_kind="bf16")
+        del h_t
+    cfg1 = table.lookup(m, hdim, d, epilogue="gelu_tanh", out_kind="mx")
+    cfg2 = table.lookup(m, d, hdim, epilogue="none", out_kind="bf16")
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -82,10 +94,10 @@ def bench_mlp(steps: int, warmup: int):
         mx.mx_quantize(x, "e2m3", "tiled", out=xq)
         if ev is not None:
             ev[1].record()
-        mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh", out=h)
+        mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh", out=h, config=cfg1)
         if ev is not None:
             ev[2].record()
-        mx.mx_gemm(h, w2, out_kind="bf16", out=y)
+        mx.mx_gemm(h, w2, out_kind="bf16", out=y, config=cfg2)
         if ev is not None:
             ev[3].record()
 
@@ -116,6 +128,7 @@ def bench_mlp(steps: int, warmup: int):
         "quantize_bytes": m * d * 2 + m * d * 3 // 4 + m * d // 32,
         "fc1_bytes": m * d * 3 // 4 + m * d // 32 + hdim * d * 3 // 4 + hdim * d // 32 + m * hdim * 3 // 4 + m * hdim // 32,
         "fc2_bytes": m * hdim * 3 // 4 + m * hdim // 32 + d * hdim * 3 // 4 + d * hdim // 32 + m * d * 2,
+        "tuning": {k: {"config": v["config"], "us": v["us"], "default_us": v["default_us"]} for k, v in tuned.items()},
     }
 
 
@@ -300,6 +313,7 @@ def main():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skinny-iters", type=int, default=100)
+    p.add_argument("--no-tune", action="store_true", help="use the default tile order instead of tuning it")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = p.parse_args()
@@ -310,7 +324,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
 
-    r = bench_mlp(args.steps, args.warmup)
+    r = bench_mlp(args.steps, args.warmup, tune=not args.no_tune)
     ms_step = r["wall_ms_per_step"]
     value = r["flops_per_step"] / ms_step / 1e9  # TFLOP/s
     # dominant kernel: the slower of the two GEMMs, timed with events on its own stream
@@ -344,6 +358,7 @@ def main():
                        "fc1_tflops": round(r["flops_per_gemm"] / r["fc1_ms"] / 1e9, 1),
                        "fc2_tflops": round(r["flops_per_gemm"] / r["fc2_ms"] / 1e9, 1),
                        "quantize_gb_s": round(r["quantize_bytes"] / r["quantize_ms"] / 1e6, 1)},
+        "tuning": r["tuning"],
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
         "swiglu_mlp": swiglu,
         "producer": producer,

@@ -222,6 +222,35 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
             int32_t out_fmt, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Launch configuration of mx_gemm: the order in which the 256 x 256 output
+ * tiles are handed to workgroups.  It changes the speed (which operand stages
+ * the workgroups in flight share in each XCD's L2), never the result: every
+ * configuration computes each output with the same arithmetic.  The Hedra
+ * post (section "We tuned before writing custom kernels") keeps per-shape
+ * choices found by timing candidates on real data; a table of such choices
+ * (microscaled_precision_gemm_amd/tuning.py) passes them here.
+ */
+typedef struct {
+  int32_t group_m;   /* m-tiles per group of the tile walk, 1 .. 16 (default 4)             */
+  int32_t xcd_remap; /* 1: each XCD walks a contiguous range of the grouped order (default);
+                        0: tiles in plain grouped order, dealt round-robin to the XCDs        */
+} mx_gemm_config;
+
+/* mx_gemm_default_config - fill *config with the defaults mx_gemm uses. */
+void mx_gemm_default_config(mx_gemm_config* config);
+
+/*
+ * mx_gemm_with_config - mx_gemm with an explicit launch configuration
+ * (NULL = the defaults).  Same arguments, results and errors as mx_gemm,
+ * plus MX_ERR_FORMAT for a configuration outside the ranges above.
+ */
+int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+                        const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
+                        int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t epilogue, int32_t out_kind, void* out,
+                        int64_t ldo, uint8_t* out_scales, int32_t out_fmt, void* workspace, size_t workspace_bytes,
+                        const mx_gemm_config* config, hipStream_t stream);
+
+/*
  * mx_gemm_splitk - the same product for skinny m (0 <= m <= 16), split along
  * K into `splits` contiguous chunks whose fp32 partial sums are added in the
  * fixed order 0, 1, ..., splits-1 (deterministic) before the output rounding.

@@ -8,9 +8,11 @@ from .binding import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     MXError,
+    MXGemmConfig,
     MXTensor,
     lib,
     mx_gemm,
+    mx_gemm_default_config,
     mx_gemm_splitk,
     mx_gemm_workspace_size,
     mx_packed_bytes,

@@ -45,8 +45,17 @@ OUT_KINDS = {"f32": MX_OUT_F32, "bf16": MX_OUT_BF16, "mx": MX_OUT_MX}
 EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH, "swiglu": MX_EPI_SWIGLU}
 LAYOUTS = {"rows": MX_LAYOUT_ROWS, "tiled": MX_LAYOUT_TILED}
 
-EXPORTED = ("mx_quantize", "mx_rmsnorm_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_splitk",
-            "mx_gemm_workspace_size", "mx_status_string", "mx_version")
+EXPORTED = ("mx_quantize", "mx_rmsnorm_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_default_config",
+            "mx_gemm_with_config", "mx_gemm_splitk", "mx_gemm_workspace_size", "mx_status_string", "mx_version")
+
+
+class MXGemmConfig(ctypes.Structure):
+    """mx_gemm_config: the tile order of mx_gemm (speed only, never the result)."""
+
+    _fields_ = [("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32)]
+
+    def key(self) -> tuple[int, int]:
+        return (int(self.group_m), int(self.xcd_remap))
 
 
 class MXError(RuntimeError):
@@ -79,6 +88,10 @@ def lib() -> ctypes.CDLL:
     L.mx_gemm.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32,
                           c_p, c_i64, c_p, c_i32, c_p, c_sz, c_p]
     L.mx_gemm.restype = ctypes.c_int
+    L.mx_gemm_with_config.argtypes = L.mx_gemm.argtypes[:-1] + [ctypes.POINTER(MXGemmConfig), c_p]
+    L.mx_gemm_with_config.restype = ctypes.c_int
+    L.mx_gemm_default_config.argtypes = [ctypes.POINTER(MXGemmConfig)]
+    L.mx_gemm_default_config.restype = None
     L.mx_gemm_splitk.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32,
                                  c_i32, c_p, c_i64, c_p, c_sz, c_p]
     L.mx_gemm_splitk.restype = ctypes.c_int
@@ -238,13 +251,20 @@ def mx_rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor | None = None, shif
     return out
 
 
+def mx_gemm_default_config() -> MXGemmConfig:
+    c = MXGemmConfig()
+    lib().mx_gemm_default_config(ctypes.byref(c))
+    return c
+
+
 def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epilogue: str = "none",
             out_fmt: str = "e2m3", a_fmt: str = "e2m3", out: torch.Tensor | MXTensor | None = None,
-            workspace: torch.Tensor | None = None):
+            workspace: torch.Tensor | None = None, config: MXGemmConfig | tuple[int, int] | None = None):
     """C = A W^T.  ``a`` is a bf16/fp32 tensor (quantized to ``a_fmt`` inside the
     call) or an MXTensor.  Returns a [m, n_out] tensor, or an MXTensor for
     out_kind="mx"; n_out = n, or n / 2 for epilogue="swiglu" (``w`` then holds
-    stacked gate/up rows, see include/mxgemm.h)."""
+    stacked gate/up rows, see include/mxgemm.h).  ``config``: the tile order
+    (an MXGemmConfig or (group_m, xcd_remap)); None = the library default."""
     _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
     n_out = n // 2 if epilogue == "swiglu" else n
@@ -279,9 +299,15 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() if workspace is not None else 0
-    st = lib().mx_gemm(_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af, _ptr(w.codes),
-                       _ptr(w.scales), _fmt(w.fmt), m, n, k, EPILOGUES[epilogue], kind, _ptr(out_data), ldo,
-                       _ptr(out_scales), _fmt(out_fmt), _ptr(workspace), ws_bytes, _stream(dev))
+    args = (_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af, _ptr(w.codes), _ptr(w.scales),
+            _fmt(w.fmt), m, n, k, EPILOGUES[epilogue], kind, _ptr(out_data), ldo, _ptr(out_scales), _fmt(out_fmt),
+            _ptr(workspace), ws_bytes)
+    if config is None:
+        st = lib().mx_gemm(*args, _stream(dev))
+    else:
+        if not isinstance(config, MXGemmConfig):
+            config = MXGemmConfig(*config)
+        st = lib().mx_gemm_with_config(*args, ctypes.byref(config), _stream(dev))
     _check(st, "mx_gemm")
     return out
 

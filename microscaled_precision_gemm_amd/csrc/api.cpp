@@ -163,10 +163,33 @@ int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int6
   return hip_status(launch_quantize(src, src_type, rows, k, ld_src, fmt, static_cast<uint8_t*>(codes), scales, stream));
 }
 
+void mx_gemm_default_config(mx_gemm_config* config) {
+  if (!config) return;
+  config->group_m = 4;
+  config->xcd_remap = 1;
+}
+
 int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
             int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n, int64_t k,
             int32_t epilogue, int32_t out_kind, void* out, int64_t ldo, uint8_t* out_scales, int32_t out_fmt,
             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mx_gemm_with_config(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k,
+                             epilogue, out_kind, out, ldo, out_scales, out_fmt, workspace, workspace_bytes, nullptr,
+                             stream);
+}
+
+int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+                        const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
+                        int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t epilogue, int32_t out_kind, void* out,
+                        int64_t ldo, uint8_t* out_scales, int32_t out_fmt, void* workspace, size_t workspace_bytes,
+                        const mx_gemm_config* config, hipStream_t stream) {
+  mx_gemm_config cfg;
+  mx_gemm_default_config(&cfg);
+  if (config) {
+    if (config->group_m < 1 || config->group_m > 16 || (config->xcd_remap != 0 && config->xcd_remap != 1))
+      return MX_ERR_FORMAT;
+    cfg = *config;
+  }
   int st = check_gemm_common(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k);
   if (st != MX_OK) return st;
   if (epilogue != MX_EPI_NONE && epilogue != MX_EPI_GELU_TANH && epilogue != MX_EPI_SWIGLU) return MX_ERR_FORMAT;
@@ -217,6 +240,8 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
   g.gw = (int32_t)ceil_div(n, kTileGroupRows);
   const int64_t esize = out_kind == MX_OUT_F32 ? 4 : 2;
   g.vec_store = out_kind != MX_OUT_MX && aligned(out, 16) && (ldo * esize) % 16 == 0;
+  g.group_m = cfg.group_m;
+  g.xcd_remap = cfg.xcd_remap;
   if ((int64_t)g.tiles_m * g.tiles_n > INT32_MAX) return MX_ERR_SHAPE;
   // the kernel addresses one stage of an operand with 32-bit offsets
   if ((int64_t)g.gx * kChunkCodes >= ((int64_t)1 << 32) || (int64_t)g.gw * kChunkCodes >= ((int64_t)1 << 32))

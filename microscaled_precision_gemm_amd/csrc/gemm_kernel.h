@@ -83,20 +83,24 @@ __device__ __forceinline__ int feature_of_row(int j) {
     return 16 * h + (r < 8 ? 2 * r : 2 * (r - 8) + 1);
 }
 
-// XCD-aware tile order: contiguous ranges per XCD, grouped 4 m-tiles wide.
-__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+// Tile order.  With xcd_remap, workgroup b (dispatched round-robin to XCD
+// b % 8) takes position b / 8 of a contiguous range per XCD, so the tiles one
+// XCD has in flight are neighbours; positions then walk a grouped order,
+// group_m m-tiles wide, so that those neighbours share A and W stages in the
+// XCD's L2.
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int group_m, int xcd_remap, int& tm,
+                                            int& tn) {
   const int total = tiles_m * tiles_n;
   int s = b;
-  if (total >= 64) {
+  if (xcd_remap && total >= 64) {
     const int xcd = b & 7, idx = b >> 3;
     const int per = total >> 3, rem = total & 7;
     s = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
   }
-  constexpr int kGroupM = 4;
-  const int group = s / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in = s - group * kGroupM * tiles_n;
+  const int group = s / (group_m * tiles_n);
+  const int first_m = group * group_m;
+  const int gsize = min(tiles_m - first_m, group_m);
+  const int in = s - group * group_m * tiles_n;
   tm = first_m + in % gsize;
   tn = in / gsize;
 }
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
-  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, g.xcd_remap, tm, tn);
   const int m0 = tm * kTileM, n0 = tn * kTileN;
   const int nk = (g.K + kTileStageK - 1) / kTileStageK;
   const int gx0 = m0 / kTileGroupRows, gw0 = n0 / kTileGroupRows;

@@ -52,6 +52,8 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
   int32_t gx, gw;           // 32-row groups of the activations (ceil(M/32)) and weights (ceil(N/32))
   int32_t vec_store;        // 1 when 16-byte vector stores of a row segment are aligned
+  int32_t group_m;          // tile order: m-tiles per group (1 .. 16)
+  int32_t xcd_remap;        // tile order: 1 = contiguous tile ranges per XCD
 };
 
 hipError_t launch_quantize(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,

@@ -1,0 +1,145 @@
+"""Shape-keyed tuning table for mx_gemm's launch configuration, persisted as JSON.
+
+The Hedra post on Krea 3 (section "We tuned before writing custom kernels")
+found library kernels falling back to a generic configuration for shapes
+missing from their dispatch tables, and kept per-shape choices found by timing
+candidates on real data.  This module does that for the one knob of mx_gemm
+that is free to choose per shape: the order in which output tiles are handed
+to workgroups (``MXGemmConfig``: group width and XCD remapping), which decides
+which operand stages the tiles in flight share in each XCD's L2.
+
+* ``tune_gemm`` times every candidate on the caller's own operands (HIP events
+  on the current stream, after a warm-up), requires each candidate's output to
+  be bit-identical to the default configuration's (the tile order never
+  changes the arithmetic, and the check holds the library to that on the real
+  data), and records the fastest, keeping the default unless a candidate beats
+  it by more than ``margin``.
+* ``TuningTable.lookup`` returns the recorded configuration for a call, or
+  None (the library default) for shapes never tuned.
+* ``TuningTable.save`` / ``load`` persist the table as JSON; entries are keyed
+  by device name, so a table carried to other hardware is not applied there.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+import tempfile
+
+import torch
+
+from .binding import MXGemmConfig, MXTensor, mx_gemm, mx_gemm_default_config
+
+CANDIDATES = ((4, 1), (2, 1), (8, 1), (16, 1), (1, 1), (4, 0), (8, 0))
+FORMAT_VERSION = 1
+
+
+def device_name(device: torch.device | None = None) -> str:
+    return torch.cuda.get_device_name(device)
+
+
+def gemm_key(m: int, n: int, k: int, a_fmt: str, w_fmt: str, epilogue: str, out_kind: str, out_fmt: str,
+             device: str) -> str:
+    """Table key of one mx_gemm call shape (output format only matters for MX outputs)."""
+    of = out_fmt if out_kind == "mx" else "-"
+    return f"{device}|{m}x{n}x{k}|a={a_fmt}|w={w_fmt}|epi={epilogue}|out={out_kind}:{of}"
+
+
+class TuningTable:
+    """Per-shape launch configurations of mx_gemm."""
+
+    def __init__(self, path: str | None = None):
+        self.path = path
+        self.entries: dict[str, dict] = {}
+        if path is not None and os.path.exists(path):
+            self.load(path)
+
+    def lookup(self, m, n, k, a_fmt="e2m3", w_fmt="e2m3", epilogue="none", out_kind="bf16", out_fmt="e2m3",
+               device: str | None = None) -> MXGemmConfig | None:
+        e = self.entries.get(gemm_key(m, n, k, a_fmt, w_fmt, epilogue, out_kind, out_fmt, device or device_name()))
+        return None if e is None else MXGemmConfig(*e["config"])
+
+    def record(self, key: str, entry: dict) -> None:
+        self.entries[key] = entry
+
+    def save(self, path: str | None = None) -> str:
+        path = path or self.path
+        if path is None:
+            raise ValueError("no path to save the tuning table to")
+        d = os.path.dirname(os.path.abspath(path))
+        os.makedirs(d, exist_ok=True)
+        fd, tmp = tempfile.mkstemp(dir=d, prefix=".tuning-", suffix=".json")
+        with os.fdopen(fd, "w") as f:
+            json.dump({"format": FORMAT_VERSION, "entries": self.entries}, f, indent=1, sort_keys=True)
+        os.replace(tmp, path)
+        return path
+
+    def load(self, path: str) -> None:
+        with open(path) as f:
+            data = json.load(f)
+        if data.get("format") != FORMAT_VERSION:
+            raise ValueError(f"{path}: unknown tuning table format {data.get('format')!r}")
+        for key, e in data["entries"].items():
+            cfg = e.get("config")
+            if not (isinstance(cfg, list) and len(cfg) == 2 and 1 <= cfg[0] <= 16 and cfg[1] in (0, 1)):
+                raise ValueError(f"{path}: bad entry {key!r}")
+        self.entries.update(data["entries"])
+
+    def gemm(self, a, w: MXTensor, out_kind: str = "bf16", epilogue: str = "none", out_fmt: str = "e2m3",
+             a_fmt: str = "e2m3", **kw):
+        """mx_gemm with this table's configuration for the call's shape (the
+        library default when the shape was never tuned)."""
+        m = a.rows if isinstance(a, MXTensor) else a.shape[0]
+        af = a.fmt if isinstance(a, MXTensor) else a_fmt
+        cfg = self.lookup(m, w.rows, w.k, af, w.fmt, epilogue, out_kind, out_fmt)
+        return mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, a_fmt=a_fmt, config=cfg, **kw)
+
+
+def _same(x, y) -> bool:
+    if isinstance(x, MXTensor):
+        return torch.equal(x.codes, y.codes) and torch.equal(x.scales, y.scales)
+    return torch.equal(x, y)
+
+
+def _time_us(fn, iters: int) -> float:
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(iters):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e3 / iters
+
+
+def tune_gemm(table: TuningTable, a: MXTensor, w: MXTensor, out_kind: str = "bf16", epilogue: str = "none",
+              out_fmt: str = "e2m3", candidates=CANDIDATES, iters: int = 10, rounds: int = 3,
+              margin: float = 0.01) -> dict:
+    """Time the candidate tile orders for this call on these operands and
+    record the fastest in ``table`` (see the module docstring).  Returns the
+    recorded entry; raises if a candidate's output differs from the default's."""
+    default = mx_gemm_default_config().key()
+    cands = [default] + [c for c in candidates if c != default]
+    ref = mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, config=default)
+    outs = {c: mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, config=c) for c in cands}
+    torch.cuda.synchronize()
+    for c, o in outs.items():
+        if not _same(o, ref):
+            raise RuntimeError(f"tile order {c} changed the result of mx_gemm; not recorded")
+    for _ in range(3):  # warm-up, and let the clocks settle
+        for c in cands:
+            mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, out=outs[c], config=c)
+    torch.cuda.synchronize()
+    best = {c: float("inf") for c in cands}
+    for _ in range(rounds):  # interleaved rounds: drifting clocks hit every candidate alike
+        for c in cands:
+            t = _time_us(lambda: mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, out=outs[c],
+                                         config=c), iters)
+            best[c] = min(best[c], t)
+    pick = min(cands, key=lambda c: best[c])
+    if best[pick] > best[default] * (1.0 - margin):
+        pick = default
+    entry = {"config": list(pick), "us": round(best[pick], 2), "default_us": round(best[default], 2),
+             "candidates": {f"{c[0]},{c[1]}": round(t, 2) for c, t in best.items()}}
+    key = gemm_key(a.rows, w.rows, w.k, a.fmt, w.fmt, epilogue, out_kind, out_fmt, device_name())
+    table.record(key, entry)
+    return entry

@@ -160,6 +160,22 @@ def test_gemm_validation(L):
     assert g(epi=2, n=128, out_kind=2, out_scales=FAKE, m=0) == B.MX_OK
 
 
+@host_only
+def test_gemm_config_validation(L):
+    args = dict(a_src=NULL, a_src_type=0, lda=0, a_codes=FAKE, a_scales=FAKE, a_fmt=2, w_codes=FAKE,
+                w_scales=FAKE, w_fmt=2, m=64, n=64, k=128, epi=0, out_kind=1, out=FAKE, ldo=64, out_scales=NULL,
+                out_fmt=2, ws=NULL, ws_bytes=0)
+    d = B.MXGemmConfig()
+    L.mx_gemm_default_config(ctypes.byref(d))
+    assert d.key() == (4, 1)
+    for bad in ((0, 1), (17, 1), (4, 2), (4, -1)):
+        c = B.MXGemmConfig(*bad)
+        assert L.mx_gemm_with_config(*args.values(), ctypes.byref(c), NULL) == B.MX_ERR_FORMAT
+    ok = B.MXGemmConfig(8, 0)
+    assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(ok), NULL) == B.MX_OK
+    assert L.mx_gemm_with_config(*dict(args, k=100).values(), ctypes.byref(ok), NULL) == B.MX_ERR_SHAPE
+
+
 def sk(**kw):
     a = dict(a_src=NULL, a_src_type=0, lda=0, a_codes=FAKE, a_scales=FAKE, a_fmt=2, w_codes=FAKE, w_scales=FAKE,
              w_fmt=3, m=16, n=64, k=4096, splits=8, out_kind=1, out=FAKE, ldo=64, ws=FAKE, ws_bytes=1 << 30,

@@ -1,0 +1,66 @@
+"""The shape-keyed tuning table: host-side behaviour (no GPU) and, on a GPU,
+tuning a real call (every candidate bit-identical to the default; the
+recorded choice is applied and survives a save / load round trip)."""
+
+import json
+
+import pytest
+import torch
+
+import microscaled_precision_gemm_amd as mx
+from microscaled_precision_gemm_amd import tuning as T
+
+
+def test_key_names_every_dimension():
+    k = T.gemm_key(20480, 12288, 3072, "e2m3", "e2m3", "gelu_tanh", "mx", "e2m3", "dev0")
+    assert k == "dev0|20480x12288x3072|a=e2m3|w=e2m3|epi=gelu_tanh|out=mx:e2m3"
+    # the output element format only matters for MX outputs
+    assert T.gemm_key(1, 2, 32, "e2m3", "e3m2", "none", "bf16", "e3m2", "d") == \
+        T.gemm_key(1, 2, 32, "e2m3", "e3m2", "none", "bf16", "e2m3", "d")
+
+
+def test_save_load_round_trip(tmp_path):
+    t = T.TuningTable()
+    key = T.gemm_key(256, 512, 1024, "e2m3", "e2m3", "none", "bf16", "e2m3", "devX")
+    t.record(key, {"config": [8, 1], "us": 12.5, "default_us": 13.0, "candidates": {"4,1": 13.0, "8,1": 12.5}})
+    p = t.save(str(tmp_path / "sub" / "tuning.json"))
+    u = T.TuningTable(p)
+    assert u.lookup(256, 512, 1024, device="devX").key() == (8, 1)
+    assert u.lookup(256, 512, 1024, device="other") is None  # entries are per device
+    assert u.lookup(256, 512, 2048, device="devX") is None  # untuned shape: library default
+
+
+def test_load_rejects_bad_entries(tmp_path):
+    p = tmp_path / "bad.json"
+    p.write_text(json.dumps({"format": 1, "entries": {"k": {"config": [0, 1]}}}))
+    with pytest.raises(ValueError):
+        T.TuningTable(str(p))
+    p.write_text(json.dumps({"format": 99, "entries": {}}))
+    with pytest.raises(ValueError):
+        T.TuningTable(str(p))
+
+
+@pytest.mark.gpu
+def test_tune_real_call_and_apply(tmp_path):
+    from tests.parity import say
+    torch.manual_seed(0)
+    m, k, n = 2048, 512, 2048  # 8 x 8 tiles: the XCD remapping applies
+    a = mx.mx_quantize(torch.randn(m, k, device="cuda").to(torch.bfloat16), "e2m3")
+    w = mx.mx_quantize((torch.randn(n, k, device="cuda") * 0.05).to(torch.bfloat16), "e2m3")
+    say("tuning 2048x512x2048 gelu->mx")
+    table = T.TuningTable(str(tmp_path / "t.json"))
+    entry = T.tune_gemm(table, a, w, out_kind="mx", epilogue="gelu_tanh", iters=3, rounds=2)
+    assert set(entry["candidates"]) >= {"4,1", "8,1", "1,1", "4,0"}
+    cfg = table.lookup(m, n, k, epilogue="gelu_tanh", out_kind="mx")
+    assert cfg is not None and cfg.key() == tuple(entry["config"])
+    got = table.gemm(a, w, out_kind="mx", epilogue="gelu_tanh")
+    ref = mx.mx_gemm(a, w, out_kind="mx", epilogue="gelu_tanh")
+    torch.cuda.synchronize()
+    assert torch.equal(got.codes, ref.codes) and torch.equal(got.scales, ref.scales)
+    table.save()
+    assert T.TuningTable(str(tmp_path / "t.json")).lookup(m, n, k, epilogue="gelu_tanh", out_kind="mx").key() == cfg.key()
+    # a configuration outside the documented ranges is refused by the library
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm(a, w, out_kind="bf16", config=(0, 1))
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm(a, w, out_kind="bf16", config=(4, 2))
