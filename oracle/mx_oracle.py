@@ -40,14 +40,25 @@ computes, in float64 with numpy:
   Custom Kernels for the AMD MI300" (section "Fused RMS Norm Kernel") is the
   MI300X counterpart.
 
+* The format variants on the same scaled matrix instruction: the section
+  "Quality set the precision limit" weighs MXFP4 (which the chip runs at the
+  MXFP6 rate, rejected there on quality) and FP8 against MXFP6.  Their OCP MX
+  element types are E2M1 (4 bits, max 6), E4M3 (8 bits, bias 7, max 448, the
+  all-ones exponent and mantissa pattern is NaN, no infinity) and E5M2
+  (8 bits, bias 15, max 57344, the all-ones exponent field is infinity or
+  NaN).  The same scale rule and rounding apply; special codes are never
+  produced (finite magnitudes above the largest saturate to it).
+
 Readings where the pages are silent (also listed in the design doc):
 
 * all-zero block -> the scale exponent clamps to -127 (byte 0x00), codes +-0;
 * the sign bit of each code is the sign bit of the source value, so -0.0 and
   negative values that round to zero give code 0b100000;
 * a block holding a NaN or an infinity gets scale byte 0xFF (NaN) and codes 0;
-* packing: element i of a 32-element block occupies bits [6i, 6i+6) of a
-  little-endian 192-bit field (24 bytes); blocks follow each other along a row.
+* packing: element i of a 32-element block occupies bits [b*i, b*i+b) of a
+  little-endian field of 32*b bits, b the element width (24 bytes for the
+  6-bit types, 16 for E2M1 with element 2i in the low nibble of byte i, 32
+  for the 8-bit types); blocks follow each other along a row.
 """
 
 from __future__ import annotations
@@ -59,8 +70,11 @@ SCALE_NAN = 0xFF
 
 # Element formats: exponent bits, mantissa bits, exponent bias.
 FORMATS = {
-    "e2m3": (2, 3, 1),
-    "e3m2": (3, 2, 3),
+    "e2m3": (2, 3, 1),   # FP6
+    "e3m2": (3, 2, 3),   # FP6
+    "e2m1": (2, 1, 1),   # FP4
+    "e4m3": (4, 3, 7),   # FP8: exponent and mantissa all ones is NaN; no infinity
+    "e5m2": (5, 2, 15),  # FP8: exponent all ones is infinity (mantissa 0) or NaN
 }
 
 
@@ -71,20 +85,34 @@ def _fmt(fmt: str) -> tuple[int, int, int]:
         raise ValueError(f"unknown MX element format {fmt!r}") from None
 
 
-def element_values(fmt: str) -> np.ndarray:
-    """Value of each of the 64 six-bit codes, decoded from the bit fields.
+def element_bits(fmt: str) -> int:
+    """Width of one element code: sign + exponent + mantissa bits."""
+    ebits, mbits, _ = _fmt(fmt)
+    return 1 + ebits + mbits
 
-    Code bits: sign (bit 5), exponent field e (E bits), mantissa field m
+
+def element_values(fmt: str) -> np.ndarray:
+    """Value of each of the 2**b element codes, decoded from the bit fields.
+
+    Code bits: sign (top bit), exponent field e (E bits), mantissa field m
     (M bits).  e == 0 is subnormal: 2**(1-bias) * m / 2**M; otherwise
-    2**(e-bias) * (1 + m / 2**M).  No code is Inf or NaN.
+    2**(e-bias) * (1 + m / 2**M).  The 6-bit and 4-bit types have no special
+    codes.  E4M3 reserves e and m all ones for NaN; E5M2 reserves e all ones
+    for infinity (m == 0) and NaN.
     """
     ebits, mbits, bias = _fmt(fmt)
-    vals = np.empty(64, dtype=np.float64)
-    for c in range(64):
-        sign = -1.0 if (c >> 5) & 1 else 1.0
-        e = (c >> mbits) & ((1 << ebits) - 1)
-        m = c & ((1 << mbits) - 1)
-        if e == 0:
+    bits = 1 + ebits + mbits
+    vals = np.empty(1 << bits, dtype=np.float64)
+    emask, mmask = (1 << ebits) - 1, (1 << mbits) - 1
+    for c in range(1 << bits):
+        sign = -1.0 if (c >> (bits - 1)) & 1 else 1.0
+        e = (c >> mbits) & emask
+        m = c & mmask
+        if fmt == "e4m3" and e == emask and m == mmask:
+            mag = np.nan
+        elif fmt == "e5m2" and e == emask:
+            mag = np.inf if m == 0 else np.nan
+        elif e == 0:
             mag = 2.0 ** (1 - bias) * (m / 2.0 ** mbits)
         else:
             mag = 2.0 ** (e - bias) * (1.0 + m / 2.0 ** mbits)
@@ -93,8 +121,10 @@ def element_values(fmt: str) -> np.ndarray:
 
 
 def magnitudes(fmt: str) -> np.ndarray:
-    """The 32 non-negative magnitudes, indexed by the low 5 code bits."""
-    return element_values(fmt)[:32].copy()
+    """The finite non-negative magnitudes, indexed by code (codes 0 .. top):
+    32 for the 6-bit types, 8 for E2M1, 127 for E4M3, 124 for E5M2."""
+    pos = element_values(fmt)[: 1 << (element_bits(fmt) - 1)]
+    return pos[np.isfinite(pos)].copy()
 
 
 def floor_log2(x: np.ndarray) -> np.ndarray:
@@ -122,17 +152,19 @@ def e8m0_value(u) -> np.ndarray:
 def round_to_code(r: np.ndarray, fmt: str) -> np.ndarray:
     """Nearest element code for already-scaled values r (float64).
 
-    The magnitude goes to the nearest of the 32 representable magnitudes;
-    an exact tie goes to the even code (mantissa LSB 0), which is
+    The magnitude goes to the nearest of the format's finite magnitudes; an
+    exact tie goes to the even code (mantissa LSB 0), which is
     round-half-to-even because the codes increase with the magnitude.  A
-    magnitude above the largest one maps to the largest (saturation).  The
-    sign bit is copied from r, so -0.0 and negative underflow give code 32.
+    magnitude above the largest one maps to the largest (saturation), so the
+    special codes of the 8-bit types never appear.  The sign bit is copied
+    from r, so -0.0 and negative underflow give the negative-zero code.
     """
     mags = magnitudes(fmt)
+    top = len(mags) - 1
     r = np.asarray(r, dtype=np.float64)
     a = np.abs(r)
     hi = np.searchsorted(mags, a, side="left")  # first magnitude >= a
-    hi = np.minimum(hi, 31)
+    hi = np.minimum(hi, top)
     lo = np.maximum(hi - 1, 0)
     d_lo = a - mags[lo]
     d_hi = mags[hi] - a
@@ -140,9 +172,9 @@ def round_to_code(r: np.ndarray, fmt: str) -> np.ndarray:
     tie = d_lo == d_hi
     pick = np.where(tie, np.where(lo % 2 == 0, lo, hi), pick)
     # above the largest magnitude: nearest is the largest
-    pick = np.where(a >= mags[31], 31, pick)
+    pick = np.where(a >= mags[top], top, pick)
     sign = np.signbit(r).astype(np.int64)
-    return (pick + 32 * sign).astype(np.uint8)
+    return (pick + (sign << (element_bits(fmt) - 1))).astype(np.uint8)
 
 
 def quantize(x: np.ndarray, fmt: str = "e2m3") -> tuple[np.ndarray, np.ndarray]:
@@ -184,32 +216,46 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str = "e2m3") -> np.n
     return (vals.reshape(rows, k // BLOCK, BLOCK) * sc[:, :, None]).reshape(rows, k)
 
 
-def pack(codes: np.ndarray) -> np.ndarray:
-    """codes uint8 [rows, K] (values < 64) -> packed bytes uint8 [rows, 3K/4].
+def pack(codes: np.ndarray, fmt: str = "e2m3") -> np.ndarray:
+    """codes uint8 [rows, K] -> packed bytes uint8 [rows, K*b/8], b the
+    element width of fmt.
 
-    Element i of the row occupies bits [6i, 6i+6) of the row's little-endian
-    bit string; so four codes c0..c3 make the 24-bit word c0 | c1<<6 | c2<<12
-    | c3<<18 stored as three bytes, low byte first.  A 32-element block is
-    24 bytes.
+    Element i of the row occupies bits [b*i, b*i+b) of the row's
+    little-endian bit string.  6 bits: four codes c0..c3 make the 24-bit word
+    c0 | c1<<6 | c2<<12 | c3<<18 stored as three bytes, low byte first (a
+    32-element block is 24 bytes).  4 bits: byte i is c[2i] | c[2i+1]<<4.
+    8 bits: one byte per code.
     """
     codes = np.asarray(codes, dtype=np.uint32)
     rows, k = codes.shape
+    bits = element_bits(fmt)
     if k % 4:
         raise ValueError("K must be a multiple of 4")
-    if np.any(codes >= 64):
-        raise ValueError("codes must be 6-bit")
+    if np.any(codes >= (1 << bits)):
+        raise ValueError(f"codes must be {bits}-bit")
+    if bits == 8:
+        return codes.astype(np.uint8)
+    if bits == 4:
+        q = codes.reshape(rows, k // 2, 2)
+        return (q[..., 0] | (q[..., 1] << 4)).astype(np.uint8)
     q = codes.reshape(rows, k // 4, 4)
     w = q[..., 0] | (q[..., 1] << 6) | (q[..., 2] << 12) | (q[..., 3] << 18)
     out = np.stack([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], axis=-1)
     return out.reshape(rows, 3 * k // 4).astype(np.uint8)
 
 
-def unpack(packed: np.ndarray, k: int) -> np.ndarray:
-    """Inverse of ``pack``: bytes [rows, 3K/4] -> codes uint8 [rows, K]."""
+def unpack(packed: np.ndarray, k: int, fmt: str = "e2m3") -> np.ndarray:
+    """Inverse of ``pack``: bytes [rows, K*b/8] -> codes uint8 [rows, K]."""
     packed = np.asarray(packed, dtype=np.uint32)
     rows = packed.shape[0]
-    if packed.shape[1] != 3 * k // 4:
+    bits = element_bits(fmt)
+    if packed.shape[1] != bits * k // 8:
         raise ValueError("packed width does not match K")
+    if bits == 8:
+        return packed.astype(np.uint8)
+    if bits == 4:
+        q = np.stack([packed & 15, packed >> 4], axis=-1)
+        return q.reshape(rows, k).astype(np.uint8)
     b = packed.reshape(rows, k // 4, 3)
     w = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16)
     q = np.stack([(w >> (6 * i)) & 63 for i in range(4)], axis=-1)

@@ -44,29 +44,76 @@ def test_magnitudes_match_literal_table():
         assert math.copysign(1.0, full[32]) == -1.0  # code 32 is -0
 
 
-@pytest.mark.parametrize("fmt,emax,vmax,min_sub,min_norm", [
-    ("e2m3", 2, 7.5, 0.125, 1.0),
-    ("e3m2", 4, 28.0, 0.0625, 0.25),
+@pytest.mark.parametrize("fmt,bits,emax,vmax,min_sub,min_norm,nfinite", [
+    ("e2m3", 6, 2, 7.5, 0.125, 1.0, 32),
+    ("e3m2", 6, 4, 28.0, 0.0625, 0.25, 32),
+    ("e2m1", 4, 2, 6.0, 0.5, 1.0, 8),
+    ("e4m3", 8, 8, 448.0, 2.0 ** -9, 2.0 ** -6, 127),
+    ("e5m2", 8, 15, 57344.0, 2.0 ** -16, 2.0 ** -14, 124),
 ])
-def test_format_constants(fmt, emax, vmax, min_sub, min_norm):
+def test_format_constants(fmt, bits, emax, vmax, min_sub, min_norm, nfinite):
     mags = O.magnitudes(fmt)
+    assert O.element_bits(fmt) == bits
+    assert len(mags) == nfinite
     assert O.emax_elem(fmt) == emax
     assert mags.max() == vmax
     assert mags[1] == min_sub
-    assert np.all(np.diff(mags) > 0), "codes 0..31 must increase strictly"
+    assert np.all(np.diff(mags) > 0), "codes must increase strictly with the magnitude"
     # smallest normal: exponent field 1, mantissa 0
-    mbits = {"e2m3": 3, "e3m2": 2}[fmt]
+    mbits = {"e2m3": 3, "e3m2": 2, "e2m1": 1, "e4m3": 3, "e5m2": 2}[fmt]
     assert mags[1 << mbits] == min_norm
-    assert np.all(np.isfinite(O.element_values(fmt)))
+    assert np.all(np.isfinite(O.element_values(fmt))) == (bits < 8)
 
 
-@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp4_fp8_element_values_match_literal_table():
+    for line in _golden_lines("fp4_fp8_element_values.txt"):
+        fmt, code, val = line.split()
+        got = O.element_values(fmt)[int(code)]
+        want = float(val)
+        if math.isnan(want):
+            assert math.isnan(got), (fmt, code, got)
+        else:
+            assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), (fmt, code, got, want)
+
+
+@pytest.mark.parametrize("fmt,dtype", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_decode_matches_torch(fmt, dtype):
+    """All 256 FP8 codes decode as torch's float8 types decode them."""
+    ref = torch.arange(256, dtype=torch.uint8).view(dtype).to(torch.float64).numpy()
+    got = O.element_values(fmt)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[fin], ref[fin])
+    np.testing.assert_array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+@pytest.mark.parametrize("fmt,dtype", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_rounding_matches_torch_cast(fmt, dtype):
+    """Within the finite range, element rounding equals torch's fp32 -> float8
+    cast (round to nearest even), ties and subnormals included."""
+    rng = np.random.default_rng(31)
+    vmax = O.magnitudes(fmt).max()
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-20, 17, 200000))).astype(np.float32)
+    mids = (O.magnitudes(fmt)[:-1] + O.magnitudes(fmt)[1:]) / 2  # every exact tie
+    x = np.concatenate([x, mids.astype(np.float32), -mids.astype(np.float32), np.float32([0.0, -0.0])])
+    x = x[np.abs(x) <= vmax]
+    ref = torch.from_numpy(x).to(dtype).view(torch.uint8).numpy()
+    got = O.round_to_code(x.astype(np.float64), fmt)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, (fmt, x[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+ALL_FMTS = ["e2m3", "e3m2", "e2m1", "e4m3", "e5m2"]
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_exhaustive_round_trip(fmt):
-    """Every code decodes and re-encodes to itself, in a block whose scale is
-    fixed to 2**0 by a max-magnitude element (so the block scale byte is 127)."""
+    """Every finite code decodes and re-encodes to itself, in a block whose
+    scale is fixed to 2**0 by a max-magnitude element (so the block scale byte
+    is 127)."""
     vals = O.element_values(fmt)
     vmax = O.magnitudes(fmt).max()
-    for c in range(64):
+    for c in np.flatnonzero(np.isfinite(vals)):
         blk = np.zeros((1, 32))
         blk[0, 0] = vmax
         blk[0, 5] = vals[c]
@@ -78,16 +125,19 @@ def test_exhaustive_round_trip(fmt):
         assert math.copysign(1.0, back[0, 5]) == math.copysign(1.0, vals[c])
 
 
-@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
-@pytest.mark.parametrize("shift", [-130, -20, -1, 3, 60, 120])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+@pytest.mark.parametrize("shift", [-130, -20, -1, 3, 60, 100])
 def test_round_trip_under_any_scale(fmt, shift):
     """Scaling a block by 2**k changes only the scale byte (by k), never the codes."""
     vals = O.element_values(fmt)
-    vmax = O.magnitudes(fmt).max()
+    mags = O.magnitudes(fmt)
+    vmax = mags.max()
+    half = 1 << (O.element_bits(fmt) - 1)
+    pick = np.linspace(1, len(mags) - 1, 31).round().astype(int)  # 31 finite codes spread over the range
     base = np.zeros((2, 32))
     base[:, 0] = vmax
-    base[0, 1:] = vals[1:32]
-    base[1, 1:] = vals[33:64]
+    base[0, 1:] = vals[pick]
+    base[1, 1:] = vals[half + pick]
     c0, s0 = O.quantize(base, fmt)
     scaled = np.ldexp(base, shift)
     if not np.all(np.isfinite(scaled)) or shift < -120:
@@ -117,11 +167,11 @@ def test_block_cases():
         got_c, got_s = O.quantize(blk, fmt)
         assert int(got_s[0, 0]) == int(scale), (line, int(got_s[0, 0]))
         assert got_c[0, : len(c)].tolist() == c, (line, got_c[0, : len(c)].tolist())
-        assert not np.any(got_c[0, len(c):] % 32), line  # zero padding stays +-0
+        assert not np.any(got_c[0, len(c):] % (1 << (O.element_bits(fmt) - 1))), line  # zero padding stays +-0
 
 
 def _brute_code(r: Fraction, fmt: str, negative: bool) -> int:
-    """Exhaustive search over all 32 magnitudes with exact rationals."""
+    """Exhaustive search over all finite magnitudes with exact rationals."""
     mags = [Fraction(x) for x in O.magnitudes(fmt)]
     a = abs(r)
     best = None
@@ -129,7 +179,7 @@ def _brute_code(r: Fraction, fmt: str, negative: bool) -> int:
         d = abs(a - m)
         if best is None or d < best[0] or (d == best[0] and c % 2 == 0 and best[1] % 2 == 1):
             best = (d, c)
-    return best[1] + (32 if negative else 0)
+    return best[1] + ((1 << (O.element_bits(fmt) - 1)) if negative else 0)
 
 
 def _brute_shared(amax: Fraction, emax: int) -> int:
@@ -142,10 +192,10 @@ def _brute_shared(amax: Fraction, emax: int) -> int:
     return max(-127, min(127, s))
 
 
-@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_quantize_matches_exact_brute_force(fmt):
     rng = np.random.default_rng(7)
-    emax = {"e2m3": 2, "e3m2": 4}[fmt]
+    emax = {"e2m3": 2, "e3m2": 4, "e2m1": 2, "e4m3": 8, "e5m2": 15}[fmt]
     # bf16-valued inputs over a wide range of magnitudes, incl. ties and zeros
     x = rng.standard_normal((24, 32)).astype(np.float32)
     x *= np.exp2(rng.integers(-40, 40, size=(24, 1))).astype(np.float32)
@@ -165,7 +215,7 @@ def test_quantize_matches_exact_brute_force(fmt):
 
 def test_scale_invariant_on_random_blocks():
     rng = np.random.default_rng(11)
-    for fmt in ("e2m3", "e3m2"):
+    for fmt in ALL_FMTS:
         emax = O.emax_elem(fmt)
         x = rng.standard_t(3, size=(200, 64)) * np.exp2(rng.integers(-60, 60, size=(200, 1)))
         x = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
@@ -197,6 +247,26 @@ def test_pack_cases():
         np.testing.assert_array_equal(O.unpack(want, 32), c)
 
 
+def test_pack_cases_fp4_fp8():
+    for line in _golden_lines("pack_cases_fp4_fp8.txt"):
+        fmt, codes, hexbytes = (p.strip() for p in line.split("|"))
+        c = np.array([[int(x) for x in codes.split()]], dtype=np.uint8)
+        want = np.array([[int(h, 16) for h in hexbytes.split()]], dtype=np.uint8)
+        assert c.shape == (1, 32) and want.shape == (1, O.element_bits(fmt) * 4)
+        np.testing.assert_array_equal(O.pack(c, fmt), want)
+        np.testing.assert_array_equal(O.unpack(want, 32, fmt), c)
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3"])
+def test_pack_round_trip_random_fp4_fp8(fmt):
+    rng = np.random.default_rng(4)
+    bits = O.element_bits(fmt)
+    c = rng.integers(0, 1 << bits, size=(5, 96), dtype=np.uint8)
+    p = O.pack(c, fmt)
+    assert p.shape == (5, 96 * bits // 8)
+    np.testing.assert_array_equal(O.unpack(p, 96, fmt), c)
+
+
 def test_pack_round_trip_random():
     rng = np.random.default_rng(3)
     c = rng.integers(0, 64, size=(7, 96), dtype=np.uint8)
@@ -207,27 +277,43 @@ def test_pack_round_trip_random():
 
 # ---------------------------------------------------------------- GEMM
 
+# (exponent bits, mantissa bits, bias) written from the OCP MX element
+# definitions, independently of the oracle's table
+_BITFIELDS = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3), "e2m1": (2, 1, 1), "e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}
+
+
 def _int_decode(code: int, fmt: str) -> int:
-    """Integer n with value = n * 2**-3 (E2M3) or n * 2**-4 (E3M2), from the bits."""
-    s = -1 if code & 32 else 1
-    if fmt == "e2m3":
-        e, m = (code >> 3) & 3, code & 7
-        n = m if e == 0 else (8 + m) << (e - 1)
-    else:
-        e, m = (code >> 2) & 7, code & 3
-        n = m if e == 0 else (4 + m) << (e - 1)
+    """Integer n with value = n * 2**-F, F = bias + M - 1 (E2M3: 3, E3M2: 4,
+    E2M1: 1, E4M3: 9, E5M2: 16), from the bits."""
+    eb, mb, _ = _BITFIELDS[fmt]
+    s = -1 if (code >> (eb + mb)) & 1 else 1
+    e, m = (code >> mb) & ((1 << eb) - 1), code & ((1 << mb) - 1)
+    n = m if e == 0 else ((1 << mb) + m) << (e - 1)
     return s * n
 
 
-@pytest.mark.parametrize("fa,fw", [("e2m3", "e2m3"), ("e2m3", "e3m2"), ("e3m2", "e3m2")])
+def _finite_codes(fmt: str) -> np.ndarray:
+    """Codes that are neither Inf nor NaN, from the bit fields."""
+    eb, mb, _ = _BITFIELDS[fmt]
+    c = np.arange(1 << (1 + eb + mb))
+    e, m = (c >> mb) & ((1 << eb) - 1), c & ((1 << mb) - 1)
+    if fmt == "e4m3":
+        return c[~((e == 15) & (m == 7))]
+    if fmt == "e5m2":
+        return c[e != 31]
+    return c
+
+
+@pytest.mark.parametrize("fa,fw", [("e2m3", "e2m3"), ("e2m3", "e3m2"), ("e3m2", "e3m2"), ("e2m1", "e2m1"),
+                                   ("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e5m2", "e5m2"), ("e2m1", "e4m3")])
 @pytest.mark.parametrize("m,n,k", [(4, 4, 32), (3, 5, 64), (2, 3, 96)])
 def test_gemm_exact_integer_brute_force(fa, fw, m, n, k):
-    rng = np.random.default_rng([m, n, k, len(fa + fw)])
-    ca = rng.integers(0, 64, size=(m, k), dtype=np.uint8)
-    cw = rng.integers(0, 64, size=(n, k), dtype=np.uint8)
+    rng = np.random.default_rng([m, n, k, len(fa + fw), ord(fa[1]), ord(fw[1])])
+    ca = rng.choice(_finite_codes(fa), size=(m, k)).astype(np.uint8)
+    cw = rng.choice(_finite_codes(fw), size=(n, k)).astype(np.uint8)
     sa = rng.integers(110, 145, size=(m, k // 32), dtype=np.uint8)
     sw = rng.integers(110, 145, size=(n, k // 32), dtype=np.uint8)
-    frac = {"e2m3": 3, "e3m2": 4}
+    frac = {f: b + mb - 1 for f, (_, mb, b) in _BITFIELDS.items()}
     c_ref, s_ref = O.gemm_ref(O.dequantize(ca, sa, fa), O.dequantize(cw, sw, fw))
     for i in range(m):
         for j in range(n):

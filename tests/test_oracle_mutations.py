@@ -8,18 +8,41 @@ import tests.test_oracle as pins
 from oracle import mx_oracle as O
 
 
+_ORIG_EMAX = O.emax_elem
+_ORIG_FMT = O._fmt
+_ORIG_VALUES = O.element_values
+
+
 def _ties_away(r, fmt):
     mags = O.magnitudes(fmt)
+    top = len(mags) - 1
     a = np.abs(np.asarray(r, dtype=np.float64))
-    hi = np.minimum(np.searchsorted(mags, a, side="left"), 31)
+    hi = np.minimum(np.searchsorted(mags, a, side="left"), top)
     lo = np.maximum(hi - 1, 0)
     pick = np.where(a - mags[lo] < mags[hi] - a, lo, hi)
-    pick = np.where(a >= mags[31], 31, pick)
-    return (pick + 32 * np.signbit(r)).astype(np.uint8)
+    pick = np.where(a >= mags[top], top, pick)
+    return (pick + (np.signbit(r).astype(np.int64) << (O.element_bits(fmt) - 1))).astype(np.uint8)
 
 
 def _emax_plus_one(fmt):
-    return {"e2m3": 3, "e3m2": 5}[fmt]
+    return _ORIG_EMAX(fmt) + 1
+
+
+def _e4m3_nan_as_number(fmt):
+    """Decode E4M3's NaN code as if it were the finite 480."""
+    v = _ORIG_VALUES(fmt)
+    if fmt == "e4m3":
+        v = v.copy()
+        v[127], v[255] = 480.0, -480.0
+    return v
+
+
+def _fp4_nibbles_swapped(codes, fmt="e2m3"):
+    codes = np.asarray(codes, dtype=np.uint32)
+    if O.element_bits(fmt) != 4:
+        return _ORIG_PACK(codes, fmt)
+    q = codes.reshape(codes.shape[0], -1, 2)
+    return ((q[..., 0] << 4) | q[..., 1]).astype(np.uint8)
 
 
 def _pack_big_endian(codes):
@@ -86,8 +109,11 @@ def _rms_scale_not_plus_one(x, gamma=None, shift=None, scale=None, rows_per_cond
 
 
 def _bias_off(fmt):
-    e, m, b = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3)}[fmt]
+    e, m, b = _ORIG_FMT(fmt)
     return (e, m, b + 1)
+
+
+_ORIG_PACK = O.pack
 
 
 MUTANTS = [
@@ -104,6 +130,11 @@ MUTANTS = [
     ("swiglu_rows", _swiglu_rows_contiguous, [pins.test_swiglu_stacking_and_product]),
     ("rmsnorm_modulate", _rms_eps_outside, [pins.test_rmsnorm_matches_torch]),
     ("rmsnorm_modulate", _rms_scale_not_plus_one, [pins.test_modulation_per_condition]),
+    ("element_values", _e4m3_nan_as_number,
+     [lambda: pins.test_format_constants("e4m3", 8, 8, 448.0, 2.0 ** -9, 2.0 ** -6, 127),
+      lambda: pins.test_fp8_decode_matches_torch("e4m3", pins.torch.float8_e4m3fn)]),
+    ("pack", _fp4_nibbles_swapped, [pins.test_pack_cases_fp4_fp8]),
+    ("emax_elem", _emax_plus_one, [lambda: pins.test_quantize_matches_exact_brute_force("e5m2")]),
 ]
 
 
