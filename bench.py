@@ -180,6 +180,42 @@ def bench_swiglu_mlp(steps: int, warmup: int):
             "fc2_ms": round(float(f2), 4), "fc2_tflops": round(fl2 / f2 / 1e9, 1)}
 
 
+PEAK_BY_FMT = {"e2m3": 10100.0, "e2m1": 10100.0, "e4m3": 5000.0, "e5m2": 5000.0}
+
+
+def bench_formats(iters: int = 20):
+    """The operand formats of the same scaled matrix instruction on fc1's shape
+    (20480 x 3072 x 12288, both operands pre-quantized, bf16 out, no
+    epilogue): MXFP6 E2M3, MXFP4 E2M1 and MXFP8 E4M3, each against its own
+    dense peak (10.1 PF for FP6 and FP4, 5.0 PF for FP8)."""
+    w = syn.WORKLOADS["fc1"]
+    dev = torch.device("cuda:0")
+    a_src = syn.make_a(w).to(dev)
+    w_src = syn.make_w(w).to(dev)
+    out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * w.m * w.n * w.k
+    res = {}
+    for fmt in ("e2m3", "e2m1", "e4m3"):
+        aq, wq = mx.mx_quantize(a_src, fmt), mx.mx_quantize(w_src, fmt)
+
+        def call():
+            mx.mx_gemm(aq, wq, out_kind="bf16", out=out)
+
+        settle(call, 0.2)
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(iters):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        tf = flops / ms / 1e9
+        res[fmt] = {"ms": round(ms, 4), "tflops": round(tf, 1), "peak_tflops": PEAK_BY_FMT[fmt],
+                    "frac": round(tf / PEAK_BY_FMT[fmt], 4)}
+        del aq, wq
+    return {"workload": "fc1-shaped GEMM 20480x3072x12288, pre-quantized operands, bf16 out", **res}
+
+
 def bench_producer(iters: int = 50):
     """The quantize-once producer on fc1's input: RMSNorm with a gain, two
     conditionings of 10240 rows (modulation), MX E2M3 into the tiled layout.
@@ -334,6 +370,7 @@ def main():
     skinny = [bench_skinny(16, 16, args.skinny_iters), bench_skinny(8, 16, args.skinny_iters)]
     swiglu = bench_swiglu_mlp(args.steps, args.warmup)
     producer = bench_producer()
+    formats = bench_formats()
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -362,6 +399,7 @@ def main():
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
         "swiglu_mlp": swiglu,
         "producer": producer,
+        "operand_formats": formats,
     }
     if args.copy_calibration:
         line["copy_calibration"] = copy_calibration()

@@ -23,26 +23,37 @@
  *     saturate; the sign bit is the source's sign bit (so -0.0 -> 0b100000);
  *   - a block containing a NaN or an infinity gets u = 0xFF and codes 0.
  *
+ * The same section weighs MXFP4 (which the chip runs at the MXFP6 rate) and
+ * FP8 against MXFP6.  The library also takes the other element types of the
+ * gfx950 scaled matrix instruction, with the same block, scale and rounding
+ * rule: E2M1 (FP4: emax_elem 2, max 6), E4M3 (FP8: emax_elem 8, max 448) and
+ * E5M2 (FP8: emax_elem 15, max 57344).  Their special codes (E4M3's NaN,
+ * E5M2's infinities and NaNs) are never produced: larger finite magnitudes
+ * saturate to the maximum, and non-finite blocks get u = 0xFF and codes 0.
+ *
  * The skinny split-K GEMM follows the split-K technique of the page "Creating
  * Custom Kernels for the AMD MI300" (section "Skinny GEMM Kernel"): K is cut
  * into contiguous chunks computed concurrently and their fp32 partial sums are
  * reduced in a fixed order.
  *
- * Packing.  Element i of a row occupies bits [6i, 6i+6) of the row read as a
- * little-endian bit string, so a 32-element block is 24 bytes and four codes
- * c0..c3 form the 24-bit word c0 | c1<<6 | c2<<12 | c3<<18.  Code bits: sign
- * (bit 5), then the exponent field, then the mantissa field.  Weights use the
+ * Packing.  With b-bit codes (b = 6, 4 or 8), element i of a row occupies
+ * bits [b*i, b*i+b) of the row read as a little-endian bit string, so a
+ * 32-element block is 4b bytes (24, 16 or 32).  For b = 6 four codes c0..c3
+ * form the 24-bit word c0 | c1<<6 | c2<<12 | c3<<18; for b = 4 byte i holds
+ * element 2i in its low nibble and element 2i+1 in its high nibble.  Code
+ * bits: sign (the top bit), then the exponent field, then the mantissa field.  Weights use the
  * PyTorch Linear layout [N, K]; the GEMM computes C[M, N] = A[M, K] * W[N, K]^T
  * with exact block-scaled products and fp32 accumulation.  All buffers are
  * owned by the caller and live in device memory.  Two storage layouts:
  *
  * MX_LAYOUT_ROWS (interchange):
- *   codes   [rows, 3K/4] bytes, row-major (row r is the packed row above);
+ *   codes   [rows, bK/8] bytes, row-major (row r is the packed row above);
  *   scales  [rows, K/32] bytes, row-major.
  *
  * MX_LAYOUT_TILED (the operand layout of both GEMMs and of the MX output): the
  * matrix is cut into stages of 128 K-elements (S = ceil(K/128)) and groups of
- * 32 rows (G = ceil(rows/32)).  Each (stage s, group g) pair owns
+ * 32 rows (G = ceil(rows/32)).  Each (stage s, group g) pair owns, for the
+ * 6-bit types,
  *   codes   3072 bytes at offset (s*G + g) * 3072.  For each row j = 0..31 of
  *           the group, the row's 96-byte packed slice of K-elements
  *           [128s, 128s+128) is four 24-byte blocks q = 0..3.  Half h = 0, 1
@@ -55,10 +66,20 @@
  *           so each block of a row is one 16-byte and one 8-byte run;
  *   scales  128 bytes at offset (s*G + g) * 128: byte j*4 + q is the scale of
  *           block 4s+q of row 32g+j.
+ *   For the 8-bit types a chunk is 4096 bytes at offset (s*G + g) * 4096;
+ *   half h (bytes [2048h, 2048h+2048)) holds bytes 16h..16h+15 of every
+ *   block of the 32 rows in four planes of 16 bytes per row (row j at j*16):
+ *             +0     block 0,   +512   block 2,
+ *             +1024  block 1,   +1536  block 3
+ *   (the instruction takes each 8-bit block from both lane halves).
+ *   For E2M1 a chunk is 2048 bytes at offset (s*G + g) * 2048; half h
+ *   (bytes [1024h, 1024h+1024)) holds block 2h at +0 and block 2h+1 at +512,
+ *   16 bytes per row (row j at j*16).  The scales are the same for all types.
  *   Rows >= rows and blocks >= K/32 are padding: codes 0, scale byte 127.
- *   Total: codes S*G*3072 bytes, scales S*G*128 bytes (mx_packed_bytes).
- *   Each stage of 256 rows is one contiguous 24 KB run, which the GEMM copies
- *   straight into its LDS ring.
+ *   Total: codes S*G*512b bytes (3072 for the 6-bit types), scales S*G*128
+ *   bytes (mx_packed_bytes).  Each stage of 256 rows is one contiguous run
+ *   (24 KB for the 6-bit types), which the GEMM copies straight into its LDS
+ *   ring.
  *
  * Conventions:
  *   - every call is asynchronous on the given HIP stream; the library never
@@ -95,8 +116,11 @@ extern "C" {
 
 /* Element formats.  The values equal the format codes of the gfx950 scaled
  * f8f6f4 MFMA instructions. */
-#define MX_FMT_E2M3 2
-#define MX_FMT_E3M2 3
+#define MX_FMT_E4M3 0 /* FP8 */
+#define MX_FMT_E5M2 1 /* FP8 */
+#define MX_FMT_E2M3 2 /* FP6 */
+#define MX_FMT_E3M2 3 /* FP6 */
+#define MX_FMT_E2M1 4 /* FP4 */
 
 /* Storage layouts of packed MX matrices. */
 #define MX_LAYOUT_ROWS 0
@@ -131,12 +155,12 @@ extern "C" {
  *             elements; 16-byte aligned, ld_src * element size a multiple of 16.
  *   rows, k   rows >= 0, k >= 0, k % 32 == 0.  rows == 0 or k == 0 is a
  *             no-op that returns MX_OK.
- *   fmt       MX_FMT_E2M3 or MX_FMT_E3M2.
+ *   fmt       any MX_FMT_* element format.
  *   layout    MX_LAYOUT_ROWS or MX_LAYOUT_TILED (padding included).
- *   codes     device output of mx_packed_bytes(rows, k, layout, 0) bytes,
- *             16-byte aligned.
- *   scales    device output of mx_packed_bytes(rows, k, layout, 1) bytes,
- *             4-byte aligned.
+ *   codes     device output of mx_packed_bytes(rows, k, fmt, layout, 0)
+ *             bytes, 16-byte aligned.
+ *   scales    device output of mx_packed_bytes(rows, k, fmt, layout, 1)
+ *             bytes, 4-byte aligned.
  * The result is exactly the rule in the header comment (bit-exact).
  */
 int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
@@ -167,9 +191,9 @@ int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int6
  *             group of the output shares one conditioning row); otherwise it
  *             is ignored.
  *   eps       >= 0, finite.
- *   fmt       MX_FMT_E2M3 or MX_FMT_E3M2.
- *   codes, scales  outputs of mx_packed_bytes(rows, d, MX_LAYOUT_TILED, 0 / 1)
- *             bytes (16- and 4-byte aligned), padding included.
+ *   fmt       MX_FMT_E2M3 or MX_FMT_E3M2 (other formats: MX_ERR_UNSUPPORTED).
+ *   codes, scales  outputs of mx_packed_bytes(rows, d, fmt, MX_LAYOUT_TILED,
+ *             0 / 1) bytes (16- and 4-byte aligned), padding included.
  * The result follows the fp32 evaluation above; it is not bit-identical to a
  * float64 evaluation where y lies at a rounding boundary of its code.
  */
@@ -179,10 +203,10 @@ int mx_rmsnorm_quantize(const void* x, int32_t src_type, int64_t rows, int64_t d
 
 /*
  * mx_packed_bytes - size in bytes of the codes (which == 0) or scales
- * (which == 1) buffer of a [rows, k] MX matrix in the given layout; 0 for
- * invalid arguments.
+ * (which == 1) buffer of a [rows, k] MX matrix of element format fmt in the
+ * given layout; 0 for invalid arguments.
  */
-size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which);
+size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t fmt, int32_t layout, int32_t which);
 
 /*
  * mx_gemm - C = A * W^T on MX operands, fp32 accumulation, optional epilogue.
@@ -196,9 +220,11 @@ size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which);
  * Alignment: a_src and code pointers 16 bytes, scale pointers 4 bytes, the
  *   workspace 256 bytes, f32/bf16 outputs their element size (16 bytes and
  *   ldo * element size % 16 == 0 enable vector stores), MX outputs 4 bytes.
- * Formats: E2M3 x E2M3, E2M3 x E3M2 and E3M2 x E2M3; E3M2 activations with
- *   E3M2 weights return MX_ERR_UNSUPPORTED (the scaled MFMA does not keep
- *   fp32 accuracy for that pair).
+ * Formats (weights x activations): E2M3 x E2M3, E2M3 x E3M2 and E3M2 x
+ *   E2M3 with every epilogue and output; E2M1 x E2M1, and E4M3 / E5M2 x
+ *   E4M3 / E5M2, with MX_EPI_NONE and MX_OUT_F32 / MX_OUT_BF16.  Other pairs
+ *   (E3M2 x E3M2, where the scaled MFMA does not keep fp32 accuracy, and
+ *   pairs of different element widths) return MX_ERR_UNSUPPORTED.
  * m, n, k: >= 0, k % 32 == 0.  m == 0 or n == 0 is a no-op; k == 0 writes
  *   C = 0 (epilogue applied).
  * epilogue: MX_EPI_NONE, MX_EPI_GELU_TANH or MX_EPI_SWIGLU, applied to the
@@ -210,11 +236,12 @@ size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which);
  *     ignored.
  *   MX_OUT_MX: the epilogue result is MX-quantized along N in blocks of 32
  *     (n_out % 32 == 0) into out / out_scales as an [m, n_out] matrix in
- *     MX_LAYOUT_TILED (padding written too), element format out_fmt; ldo is
- *     ignored.  This output is directly the a_codes / a_scales of a
+ *     MX_LAYOUT_TILED (padding written too), element format out_fmt
+ *     (MX_FMT_E2M3 or MX_FMT_E3M2); ldo is ignored.  This output is directly the a_codes / a_scales of a
  *     following GEMM (the down projection reads the quantized intermediate).
  * workspace: device memory of at least mx_gemm_workspace_size(m, n, k, a_src
- *   != NULL, 0) bytes (may be NULL when that size is 0).
+ *   != NULL, 0) bytes (may be NULL when that size is 0).  That size holds the
+ *   quantized activations in any element format.
  */
 int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
             int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n,
@@ -259,6 +286,7 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
  *   splits    1 .. 16 and k % (128 * splits) == 0, i.e. each chunk is whole
  *             128-element stages (else MX_ERR_UNSUPPORTED); m <= 16 (else
  *             MX_ERR_SHAPE).
+ *   formats   the 6-bit pairs of mx_gemm only (else MX_ERR_UNSUPPORTED).
  *   epilogue  MX_EPI_NONE only; out_kind MX_OUT_F32 or MX_OUT_BF16.
  *   workspace at least mx_gemm_workspace_size(m, n, k, a_src != NULL, splits)
  *             bytes, used for the activations quantized inside the call (the

@@ -27,8 +27,11 @@ MX_ERR_WORKSPACE = -5
 MX_ERR_UNSUPPORTED = -6
 MX_ERR_HIP = -7
 
+MX_FMT_E4M3 = 0
+MX_FMT_E5M2 = 1
 MX_FMT_E2M3 = 2
 MX_FMT_E3M2 = 3
+MX_FMT_E2M1 = 4
 MX_SRC_BF16 = 0
 MX_SRC_F32 = 1
 MX_OUT_F32 = 0
@@ -40,7 +43,9 @@ MX_EPI_SWIGLU = 2
 MX_LAYOUT_ROWS = 0
 MX_LAYOUT_TILED = 1
 
-FMT_CODES = {"e2m3": MX_FMT_E2M3, "e3m2": MX_FMT_E3M2}
+FMT_CODES = {"e2m3": MX_FMT_E2M3, "e3m2": MX_FMT_E3M2, "e2m1": MX_FMT_E2M1, "e4m3": MX_FMT_E4M3,
+             "e5m2": MX_FMT_E5M2}
+FMT_BITS = {"e2m3": 6, "e3m2": 6, "e2m1": 4, "e4m3": 8, "e5m2": 8}
 OUT_KINDS = {"f32": MX_OUT_F32, "bf16": MX_OUT_BF16, "mx": MX_OUT_MX}
 EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH, "swiglu": MX_EPI_SWIGLU}
 LAYOUTS = {"rows": MX_LAYOUT_ROWS, "tiled": MX_LAYOUT_TILED}
@@ -83,7 +88,7 @@ def lib() -> ctypes.CDLL:
     L.mx_rmsnorm_quantize.argtypes = [c_p, c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p, c_i64, ctypes.c_float, c_i32,
                                       c_p, c_p, c_p]
     L.mx_rmsnorm_quantize.restype = ctypes.c_int
-    L.mx_packed_bytes.argtypes = [c_i64, c_i64, c_i32, c_i32]
+    L.mx_packed_bytes.argtypes = [c_i64, c_i64, c_i32, c_i32, c_i32]
     L.mx_packed_bytes.restype = c_sz
     L.mx_gemm.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i32,
                           c_p, c_i64, c_p, c_i32, c_p, c_sz, c_p]
@@ -117,16 +122,17 @@ def mx_gemm_workspace_size(m: int, n: int, k: int, a_is_src: bool, splits: int =
     return int(lib().mx_gemm_workspace_size(m, n, k, int(bool(a_is_src)), splits))
 
 
-def mx_packed_bytes(rows: int, k: int, layout: str = "tiled", which: int = 0) -> int:
+def mx_packed_bytes(rows: int, k: int, layout: str = "tiled", which: int = 0, fmt: str = "e2m3") -> int:
     """Bytes of the codes (which=0) or scales (which=1) buffer of a [rows, k] MX matrix."""
-    return int(lib().mx_packed_bytes(rows, k, LAYOUTS[layout], which))
+    return int(lib().mx_packed_bytes(rows, k, _fmt(fmt), LAYOUTS[layout], which))
 
 
 @dataclass
 class MXTensor:
     """Packed MX matrix of logical shape [rows, k].
 
-    layout "rows": codes [rows, 3k/4] and scales [rows, k/32] uint8 tensors.
+    layout "rows": codes [rows, b*k/8] (b = 6, 4 or 8 bits per element) and
+    scales [rows, k/32] uint8 tensors.
     layout "tiled": codes and scales are flat uint8 tensors in the tiled GEMM
     layout (128-element stages x 32-row groups, see include/mxgemm.h).
     """
@@ -141,11 +147,11 @@ class MXTensor:
     @staticmethod
     def empty(rows: int, k: int, fmt: str = "e2m3", layout: str = "tiled", device=None) -> "MXTensor":
         if layout == "rows":
-            codes = torch.empty((rows, 3 * k // 4), dtype=torch.uint8, device=device)
+            codes = torch.empty((rows, FMT_BITS[fmt] * k // 8), dtype=torch.uint8, device=device)
             scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=device)
         else:
-            codes = torch.empty(mx_packed_bytes(rows, k, layout, 0), dtype=torch.uint8, device=device)
-            scales = torch.empty(mx_packed_bytes(rows, k, layout, 1), dtype=torch.uint8, device=device)
+            codes = torch.empty(mx_packed_bytes(rows, k, layout, 0, fmt), dtype=torch.uint8, device=device)
+            scales = torch.empty(mx_packed_bytes(rows, k, layout, 1, fmt), dtype=torch.uint8, device=device)
         return MXTensor(codes, scales, fmt, rows, k, layout)
 
 
@@ -198,10 +204,11 @@ def _check_mx(x: MXTensor, name: str, layout: str | None = None) -> None:
     if not (x.codes.is_contiguous() and x.scales.is_contiguous()):
         raise ValueError(f"{name}: codes and scales must be contiguous")
     if x.layout == "rows":
-        ok = tuple(x.codes.shape) == (x.rows, 3 * x.k // 4) and tuple(x.scales.shape) == (x.rows, x.k // 32)
+        ok = (tuple(x.codes.shape) == (x.rows, FMT_BITS[x.fmt] * x.k // 8)
+              and tuple(x.scales.shape) == (x.rows, x.k // 32))
     else:
-        ok = (x.codes.numel() == mx_packed_bytes(x.rows, x.k, x.layout, 0)
-              and x.scales.numel() == mx_packed_bytes(x.rows, x.k, x.layout, 1))
+        ok = (x.codes.numel() == mx_packed_bytes(x.rows, x.k, x.layout, 0, x.fmt)
+              and x.scales.numel() == mx_packed_bytes(x.rows, x.k, x.layout, 1, x.fmt))
     if not ok:
         raise ValueError(f"{name}: buffer sizes do not match a [{x.rows}, {x.k}] {x.layout} MX matrix")
 

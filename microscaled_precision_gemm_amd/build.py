@@ -22,8 +22,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmxgemm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm_we2m3_e2m3.hip", "gemm_we3m2_e2m3.hip", "gemm_we2m3_e3m2.hip", "splitk.hip",
-           "producer.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm_we2m3_e2m3.hip", "gemm_we3m2_e2m3.hip", "gemm_we2m3_e3m2.hip",
+           "gemm_we2m1_e2m1.hip", "gemm_wfp8_fp8.hip", "splitk.hip", "producer.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -18,7 +18,11 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool valid_fmt(int32_t f) { return f == MX_FMT_E2M3 || f == MX_FMT_E3M2; }
+bool valid_fmt(int32_t f) {
+  return f == MX_FMT_E2M3 || f == MX_FMT_E3M2 || f == MX_FMT_E2M1 || f == MX_FMT_E4M3 || f == MX_FMT_E5M2;
+}
+
+bool fp6_fmt(int32_t f) { return f == MX_FMT_E2M3 || f == MX_FMT_E3M2; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
@@ -38,15 +42,17 @@ int check_quantize_args(const void* src, int32_t src_type, int64_t rows, int64_t
   return MX_OK;
 }
 
-// Workspace for activations quantized inside mx_gemm: tiled codes then scales.
+// Workspace for activations quantized inside mx_gemm: tiled codes then
+// scales.  Its advertised size is the one of 8-bit codes, which covers every
+// element format.
 struct TiledWs {
   size_t codes_off, scales_off, end;
 };
 
-TiledWs tiled_ws(int64_t rows, int64_t k) {
+TiledWs tiled_ws(int64_t rows, int64_t k, int bits) {
   TiledWs w;
   w.codes_off = 0;
-  w.scales_off = round_up((size_t)tiled_codes_bytes(rows, k), kWsAlign);
+  w.scales_off = round_up((size_t)tiled_codes_bytes(rows, k, bits), kWsAlign);
   w.end = w.scales_off + round_up((size_t)tiled_scales_bytes(rows, k), kWsAlign);
   return w;
 }
@@ -60,6 +66,9 @@ int check_gemm_common(const void* a_src, int32_t a_src_type, int64_t lda, const 
   // The scaled MFMA loses fp32 accuracy when both operands are E3M2 (measured on
   // gfx950: errors up to ~4e-5 of sum|a*b|), which breaks the GEMM tolerance.
   if (a_fmt == MX_FMT_E3M2 && w_fmt == MX_FMT_E3M2) return MX_ERR_UNSUPPORTED;
+  // kernel variants: the 6-bit pairs above, E2M1 x E2M1, and 8-bit x 8-bit
+  const int ba = fmt_bits(a_fmt), bw = fmt_bits(w_fmt);
+  if (ba != bw) return MX_ERR_UNSUPPORTED;
   if (k == 0) {
     // nothing is read: C = 0; empty operands may come with NULL pointers
     if (a_src && a_src_type != MX_SRC_BF16 && a_src_type != MX_SRC_F32) return MX_ERR_FORMAT;
@@ -88,13 +97,18 @@ hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, in
   if (w_fmt == kFmtE2M3 && x_fmt == kFmtE2M3) return launch_gemm_formats<kFmtE2M3, kFmtE2M3>(a, epilogue, out_kind, out_fmt, stream);
   if (w_fmt == kFmtE3M2 && x_fmt == kFmtE2M3) return launch_gemm_formats<kFmtE3M2, kFmtE2M3>(a, epilogue, out_kind, out_fmt, stream);
   if (w_fmt == kFmtE2M3 && x_fmt == kFmtE3M2) return launch_gemm_formats<kFmtE2M3, kFmtE3M2>(a, epilogue, out_kind, out_fmt, stream);
-  return hipErrorInvalidValue;  // E3M2 x E3M2 is rejected before this point
+  if (w_fmt == kFmtE2M1 && x_fmt == kFmtE2M1) return launch_gemm_formats<kFmtE2M1, kFmtE2M1>(a, epilogue, out_kind, out_fmt, stream);
+  if (w_fmt == kFmtE4M3 && x_fmt == kFmtE4M3) return launch_gemm_formats<kFmtE4M3, kFmtE4M3>(a, epilogue, out_kind, out_fmt, stream);
+  if (w_fmt == kFmtE5M2 && x_fmt == kFmtE5M2) return launch_gemm_formats<kFmtE5M2, kFmtE5M2>(a, epilogue, out_kind, out_fmt, stream);
+  if (w_fmt == kFmtE4M3 && x_fmt == kFmtE5M2) return launch_gemm_formats<kFmtE4M3, kFmtE5M2>(a, epilogue, out_kind, out_fmt, stream);
+  if (w_fmt == kFmtE5M2 && x_fmt == kFmtE4M3) return launch_gemm_formats<kFmtE5M2, kFmtE4M3>(a, epilogue, out_kind, out_fmt, stream);
+  return hipErrorInvalidValue;  // other pairs are rejected before this point
 }
 }  // namespace mxg
 
 extern "C" {
 
-int mx_version(void) { return 100; }
+int mx_version(void) { return 200; }
 
 const char* mx_status_string(int status) {
   switch (status) {
@@ -115,12 +129,13 @@ int mx_rmsnorm_quantize(const void* x, int32_t src_type, int64_t rows, int64_t d
                         void* codes, uint8_t* scales, hipStream_t stream) {
   int st = check_quantize_args(x, src_type, rows, d, ld_x, fmt, MX_LAYOUT_TILED, codes, scales);
   if (st != MX_OK) return st;
+  if (!fp6_fmt(fmt)) return MX_ERR_UNSUPPORTED;
   if (!(eps >= 0.0f) || eps > 3.0e38f) return MX_ERR_SHAPE;  // rejects NaN, negative and infinite eps
   const bool modulated = shift != nullptr || scale != nullptr;
   if (modulated && (rows_per_cond <= 0 || rows_per_cond % 32 != 0)) return MX_ERR_SHAPE;
   if (rows == 0 || d == 0) return MX_OK;
   if (!aligned(gamma, 4) || !aligned(shift, 4) || !aligned(scale, 4)) return MX_ERR_ALIGN;
-  if (tiled_codes_bytes(rows, d) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
+  if (tiled_codes_bytes(rows, d, 6) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
   ProducerArgs a;
   a.x = x;
   a.ld_bytes = ld_x * (src_type == MX_SRC_BF16 ? 2 : 4);
@@ -137,18 +152,19 @@ int mx_rmsnorm_quantize(const void* x, int32_t src_type, int64_t rows, int64_t d
   return hip_status(launch_rmsnorm_quantize(a, src_type, fmt, stream));
 }
 
-size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t layout, int32_t which) {
+size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t fmt, int32_t layout, int32_t which) {
   if (rows < 0 || k < 0 || k % 32 != 0 || rows > kMaxDim || k > kMaxDim || !valid_layout(layout)) return 0;
-  if (which != 0 && which != 1) return 0;
-  if (layout == MX_LAYOUT_ROWS) return (size_t)(which == 0 ? rows * (k / 32) * 24 : rows * (k / 32));
-  return (size_t)(which == 0 ? tiled_codes_bytes(rows, k) : tiled_scales_bytes(rows, k));
+  if (!valid_fmt(fmt) || (which != 0 && which != 1)) return 0;
+  const int bits = fmt_bits(fmt);
+  if (layout == MX_LAYOUT_ROWS) return (size_t)(which == 0 ? rows * (k / 32) * 4 * bits : rows * (k / 32));
+  return (size_t)(which == 0 ? tiled_codes_bytes(rows, k, bits) : tiled_scales_bytes(rows, k));
 }
 
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t a_is_src, int32_t splits) {
   if (m < 0 || n < 0 || k < 0 || k % 32 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || splits < 0) return 0;
-  if (splits == 0) return a_is_src ? tiled_ws(m, k).end : 0;
+  if (splits == 0) return a_is_src ? tiled_ws(m, k, 8).end : 0;
   if (m > 16 || splits > kMaxSplits) return 0;
-  return a_is_src ? tiled_ws(m, k).end : 0;
+  return a_is_src ? tiled_ws(m, k, 8).end : 0;
 }
 
 int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
@@ -156,7 +172,7 @@ int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int6
   const int st = check_quantize_args(src, src_type, rows, k, ld_src, fmt, layout, codes, scales);
   if (st != MX_OK || rows == 0 || k == 0) return st;
   if (layout == MX_LAYOUT_TILED) {
-    if (tiled_codes_bytes(rows, k) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
+    if (tiled_codes_bytes(rows, k, fmt_bits(fmt)) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
     return hip_status(
         launch_quantize_tiled(src, src_type, rows, k, ld_src, fmt, static_cast<uint8_t*>(codes), scales, stream));
   }
@@ -196,10 +212,13 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   if (out_kind != MX_OUT_F32 && out_kind != MX_OUT_BF16 && out_kind != MX_OUT_MX) return MX_ERR_FORMAT;
   // SwiGLU pairs the gate and up rows inside each run of 128 stacked rows
   if (epilogue == MX_EPI_SWIGLU && n % 128 != 0) return MX_ERR_UNSUPPORTED;
+  // the 4- and 8-bit operand formats have the plain product with fp32 / bf16 output
+  if (!fp6_fmt(w_fmt) && (epilogue != MX_EPI_NONE || out_kind == MX_OUT_MX)) return MX_ERR_UNSUPPORTED;
   const int64_t n_out = epilogue == MX_EPI_SWIGLU ? n / 2 : n;
   if (!out) return MX_ERR_NULL;
   if (out_kind == MX_OUT_MX) {
     if (!valid_fmt(out_fmt)) return MX_ERR_FORMAT;
+    if (!fp6_fmt(out_fmt)) return MX_ERR_UNSUPPORTED;
     if (!out_scales) return MX_ERR_NULL;
     if (n_out % 32 != 0) return MX_ERR_UNSUPPORTED;
     if (!aligned(out, 16) || !aligned(out_scales, 4)) return MX_ERR_ALIGN;
@@ -215,7 +234,7 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   const uint8_t* xc = static_cast<const uint8_t*>(a_codes);
   const uint8_t* xs = a_scales;
   if (a_src && k > 0) {
-    const TiledWs w = tiled_ws(m, k);
+    const TiledWs w = tiled_ws(m, k, fmt_bits(a_fmt));
     uint8_t* base = static_cast<uint8_t*>(workspace);
     const hipError_t e = launch_quantize_tiled(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off,
                                                base + w.scales_off, stream);
@@ -244,7 +263,8 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   g.xcd_remap = cfg.xcd_remap;
   if ((int64_t)g.tiles_m * g.tiles_n > INT32_MAX) return MX_ERR_SHAPE;
   // the kernel addresses one stage of an operand with 32-bit offsets
-  if ((int64_t)g.gx * kChunkCodes >= ((int64_t)1 << 32) || (int64_t)g.gw * kChunkCodes >= ((int64_t)1 << 32))
+  const int64_t chunk = chunk_codes(fmt_bits(w_fmt));
+  if ((int64_t)g.gx * chunk >= ((int64_t)1 << 32) || (int64_t)g.gw * chunk >= ((int64_t)1 << 32))
     return MX_ERR_UNSUPPORTED;
   return hip_status(launch_gemm(g, a_fmt, w_fmt, epilogue, out_kind, out_fmt, stream));
 }
@@ -257,6 +277,7 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
   if (st != MX_OK) return st;
   if (m > 16) return MX_ERR_SHAPE;
   if (splits < 1) return MX_ERR_SHAPE;
+  if (!fp6_fmt(a_fmt) || !fp6_fmt(w_fmt)) return MX_ERR_UNSUPPORTED;
   if (out_kind != MX_OUT_F32 && out_kind != MX_OUT_BF16) return MX_ERR_FORMAT;
   if (!out) return MX_ERR_NULL;
   if (ldo < n) return MX_ERR_SHAPE;
@@ -271,7 +292,7 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
   const uint8_t* xc = static_cast<const uint8_t*>(a_codes);
   const uint8_t* xs = a_scales;
   if (a_src && k > 0) {
-    const TiledWs w = tiled_ws(m, k);
+    const TiledWs w = tiled_ws(m, k, 6);
     const hipError_t e = launch_quantize_tiled(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off,
                                                base + w.scales_off, stream);
     if (e != hipSuccess) return MX_ERR_HIP;

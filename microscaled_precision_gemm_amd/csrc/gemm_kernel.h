@@ -8,7 +8,10 @@
 //  * Operands stay packed (24 bytes per 32-element block) from HBM to the
 //    matrix cores.  A workgroup computes a 256 x 256 tile of C with 4 waves of
 //    128 x 128 on V_MFMA_SCALE_F32_32X32X64_F8F6F4 (per lane 32 K-contiguous
-//    FP6 codes in 6 VGPRs and one E8M0 byte picked by op_sel).
+//    FP6 codes in 6 VGPRs and one E8M0 byte picked by op_sel).  The same
+//    kernel takes the instruction's other operand formats (FP4 E2M1 in 4
+//    VGPRs, FP8 E4M3 / E5M2 in 8), the layout's chunk size and the ring depth
+//    following the element width.
 //  * K advances in stages of 128.  In the tiled layout one stage of 256 rows
 //    is a contiguous 24 KB run, so each stage is brought in by
 //    global_load_lds_dwordx4 copies straight into LDS (no VGPR staging), into
@@ -49,21 +52,83 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kRing = 3;
 constexpr int kGroupsPerTile = kTileM / kTileGroupRows;            // 8
-constexpr int kStageCodes = kGroupsPerTile * kChunkCodes;           // 24 KB per operand
 constexpr int kStageScales = kGroupsPerTile * kChunkScales;         // 1 KB per operand
-constexpr int kOffX = 0;
-constexpr int kOffW = kStageCodes;
-constexpr int kOffXs = 2 * kStageCodes;
-constexpr int kOffWs = 2 * kStageCodes + kStageScales;
-constexpr int kSlotBytes = 2 * kStageCodes + 2 * kStageScales;      // 51200
-constexpr int kLdsBytes = kRing * kSlotBytes;                       // 153600
-constexpr int kCodeCopiesPerWave = kStageCodes / 1024 / 4;          // 6 x 1 KB per operand
-constexpr int kCopiesPerStage = 2 * kCodeCopiesPerWave + 2;         // per wave: codes + one scale copy each
 static_assert(kTileM == kTileN, "the loader assumes square tiles");
-static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS is 160 KB per workgroup");
 static_assert(kStageScales == 4 * 64 * 4, "one 4-byte copy per lane per wave covers a stage's scales");
+
+// LDS ring and copy schedule for weight format WF and activation format XF.
+// A slot holds one stage of both operands (256 rows x 128 K each, 4 KB per
+// element bit) and their scales; three slots when they fit in the 160 KB of
+// LDS, else two.  Each wave copies 1 KB per instruction (16 bytes per lane):
+// bits(XF) activation copies, bits(WF) weight copies and one scale copy per
+// operand per stage.  With three slots, stage ks+3's copies go out half in
+// phase 1 of stage ks and half in phase 0 of stage ks+1; with two, stage
+// ks+2's copies all go out in phase 1 of stage ks (the slot it refills is
+// free from the middle of stage ks on, and the copies have a whole stage of
+// matrix work to land).
+template <int WF, int XF>
+struct Ring {
+  static constexpr int kBW = fmt_bits(WF), kBX = fmt_bits(XF);
+  static constexpr int kChunkW = chunk_codes(kBW), kChunkX = chunk_codes(kBX);
+  static constexpr int kHalfW = half_codes(kBW), kHalfX = half_codes(kBX);
+  static constexpr int kStageW = kGroupsPerTile * kChunkW, kStageX = kGroupsPerTile * kChunkX;
+  static constexpr int kOffX = 0;
+  static constexpr int kOffW = kStageX;
+  static constexpr int kOffXs = kStageX + kStageW;
+  static constexpr int kOffWs = kOffXs + kStageScales;
+  static constexpr int kSlot = kStageX + kStageW + 2 * kStageScales;  // 51200 for two 6-bit operands
+  static constexpr int kSlots = 3 * kSlot <= 160 * 1024 ? 3 : 2;
+  static constexpr int kLds = kSlots * kSlot;
+  static constexpr int kCX = kStageX / 1024 / 4, kCW = kStageW / 1024 / 4;  // 1 KB code copies per wave
+  static constexpr int kCopies = kCX + kCW + 2;
+  static constexpr int kFirst = kSlots == 3 ? (kCopies + 1) / 2 : kCopies;  // issued in phase 1
+  static constexpr int kSecond = kCopies - kFirst;                           // issued in phase 0
+  static_assert(kLds <= 160 * 1024, "gfx950 LDS is 160 KB per workgroup");
+  static_assert(kCopies + kFirst <= 63, "vmcnt counts at most 63 outstanding copies");
+};
+
+// MFMA (0..15) of a phase after which copy c of n goes out: every other MFMA
+// when they fit (phase 1 from the first, phase 0 from the second), spread
+// evenly otherwise.
+constexpr int copy_slot(int c, int n, int phase) {
+  return n <= 8 ? 2 * c + (phase == 0 ? 1 : 0) : c * 16 / n;
+}
+constexpr int copies_after(int i, int n, int phase) {
+  int k = 0;
+  for (int c = 0; c < n; ++c) k += copy_slot(c, n, phase) == i;
+  return k;
+}
+constexpr int first_copy_after(int i, int n, int phase) {
+  for (int c = 0; c < n; ++c)
+    if (copy_slot(c, n, phase) == i) return c;
+  return n;
+}
+
+template <int... I>
+struct Seq {};
+template <int N, int... I>
+struct MakeSeq : MakeSeq<N - 1, N - 1, I...> {};
+template <int... I>
+struct MakeSeq<0, I...> {
+  using type = Seq<I...>;
+};
+template <class F, int... I>
+__device__ __forceinline__ void static_for(F&& f, Seq<I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+using Seq16 = MakeSeq<16>::type;
+
+// global -> LDS copies of 16 bytes (codes) and 4 bytes (scales) per lane.
+// Kept out of the kernel template: the host compilation cannot check the
+// target builtin once its arguments depend on template parameters, and then
+// drops the kernel's launch stub.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 4, 0, 0);
+}
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt == 0, expcnt not waited.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
@@ -137,7 +202,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 template <int WF, int XF, int OUT, int EPI, int OFMT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  using R = Ring<WF, XF>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[R::kLds];
   constexpr int kLayout = OUT == kOutMx ? kLayoutMx : kLayoutContig;
 
   const int tid = threadIdx.x;
@@ -149,17 +215,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   const int nk = (g.K + kTileStageK - 1) / kTileStageK;
   const int gx0 = m0 / kTileGroupRows, gw0 = n0 / kTileGroupRows;
 
-  // ---- DMA sources.  Each wave copies 6 KB of each operand's 24 KB stage run
-  // (1 KB per instruction, 16 bytes per lane) and 256 bytes of each 1 KB scale
-  // run (4 bytes per lane).  Groups past the operand's last one (ragged tiles)
-  // re-read its last group; those rows are never stored.
-  uint32_t xo[kCodeCopiesPerWave], wo[kCodeCopiesPerWave];
+  // ---- DMA sources.  Each wave copies a quarter of each operand's stage run
+  // (1 KB per instruction, 16 bytes per lane) and 256 bytes of each 1 KB
+  // scale run (4 bytes per lane).  Groups past the operand's last one (ragged
+  // tiles) re-read its last group; those rows are never stored.
+  uint32_t xo[R::kCX], wo[R::kCW];
 #pragma unroll
-  for (int i = 0; i < kCodeCopiesPerWave; ++i) {
-    const int off = (wave * kCodeCopiesPerWave + i) * 1024 + lane * 16;
-    const int grp = off / kChunkCodes, within = off - grp * kChunkCodes;
-    xo[i] = (uint32_t)min(gx0 + grp, g.gx - 1) * kChunkCodes + within;
-    wo[i] = (uint32_t)min(gw0 + grp, g.gw - 1) * kChunkCodes + within;
+  for (int i = 0; i < R::kCX; ++i) {
+    const int off = (wave * R::kCX + i) * 1024 + lane * 16;
+    const int grp = off / R::kChunkX, within = off - grp * R::kChunkX;
+    xo[i] = (uint32_t)min(gx0 + grp, g.gx - 1) * R::kChunkX + within;
+  }
+#pragma unroll
+  for (int i = 0; i < R::kCW; ++i) {
+    const int off = (wave * R::kCW + i) * 1024 + lane * 16;
+    const int grp = off / R::kChunkW, within = off - grp * R::kChunkW;
+    wo[i] = (uint32_t)min(gw0 + grp, g.gw - 1) * R::kChunkW + within;
   }
   uint32_t xso, wso;
   {
@@ -168,45 +239,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     xso = (uint32_t)min(gx0 + grp, g.gx - 1) * kChunkScales + within;
     wso = (uint32_t)min(gw0 + grp, g.gw - 1) * kChunkScales + within;
   }
-  const int64_t x_stage = (int64_t)g.gx * kChunkCodes, w_stage = (int64_t)g.gw * kChunkCodes;
+  const int64_t x_stage = (int64_t)g.gx * R::kChunkX, w_stage = (int64_t)g.gw * R::kChunkW;
   const int64_t xs_stage = (int64_t)g.gx * kChunkScales, ws_stage = (int64_t)g.gw * kChunkScales;
 
-  // copy number idx (0..13) of this wave's share of stage ks into ring slot `slot`
+  // copy number idx (0 .. kCopies-1) of this wave's share of stage ks into
+  // ring slot `slot`: activation codes, weight codes, activation scales,
+  // weight scales
   auto issue_one = [&](int idx, int ks, int slot) {
-    uint8_t* base = lds + slot * kSlotBytes;
-    if (idx < kCodeCopiesPerWave) {
-      __builtin_amdgcn_global_load_lds(g.x_codes + ks * x_stage + xo[idx],
-                                       (lds_void_t*)(base + kOffX + (wave * kCodeCopiesPerWave + idx) * 1024), 16, 0,
-                                       0);
-    } else if (idx < 2 * kCodeCopiesPerWave) {
-      const int i = idx - kCodeCopiesPerWave;
-      __builtin_amdgcn_global_load_lds(g.w_codes + ks * w_stage + wo[i],
-                                       (lds_void_t*)(base + kOffW + (wave * kCodeCopiesPerWave + i) * 1024), 16, 0, 0);
-    } else if (idx == 2 * kCodeCopiesPerWave) {
-      __builtin_amdgcn_global_load_lds(g.x_scales + ks * xs_stage + xso, (lds_void_t*)(base + kOffXs + wave * 256), 4,
-                                       0, 0);
+    uint8_t* base = lds + slot * R::kSlot;
+    if (idx < R::kCX) {
+      copy16_to_lds(g.x_codes + ks * x_stage + xo[idx], base + R::kOffX + (wave * R::kCX + idx) * 1024);
+    } else if (idx < R::kCX + R::kCW) {
+      const int i = idx - R::kCX;
+      copy16_to_lds(g.w_codes + ks * w_stage + wo[i], base + R::kOffW + (wave * R::kCW + i) * 1024);
+    } else if (idx == R::kCX + R::kCW) {
+      copy4_to_lds(g.x_scales + ks * xs_stage + xso, base + R::kOffXs + wave * 256);
     } else {
-      __builtin_amdgcn_global_load_lds(g.w_scales + ks * ws_stage + wso, (lds_void_t*)(base + kOffWs + wave * 256), 4,
-                                       0, 0);
+      copy4_to_lds(g.w_scales + ks * ws_stage + wso, base + R::kOffWs + wave * 256);
     }
   };
-  auto issue = [&](int ks, int slot) {
+  auto issue_range = [&](int ks, int slot, int first, int count) {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerStage; ++i) issue_one(i, ks, slot);
+    for (int i = 0; i < count; ++i) issue_one(first + i, ks, slot);
   };
 
-  // ---- per-lane LDS bases in ring slot 0; fragment f (32 rows) adds
-  // f * kChunkCodes.  Half h of a chunk holds this lane's blocks 2h (sub-step
-  // 0: plane A + plane L) and 2h+1 (sub-step 1: plane H + plane B).
+  // ---- per-lane LDS bases in ring slot 0; fragment f (32 rows) adds f chunks.
+  // Half h of a chunk holds this lane's blocks 2h (sub-step 0) and 2h+1
+  // (sub-step 1) in planes of 16 bytes per row (and, for the 6-bit types, of
+  // 8 bytes per row).
   const int wn = wave & 1, wm = wave >> 1;
   const int h = lane >> 5, j = lane & 31;
   const int wrow = feature_of_row<kLayout>(j);
-  const int w16 = kOffW + wn * 4 * kChunkCodes + h * kHalfBytes + wrow * 16;
-  const int x16 = kOffX + wm * 4 * kChunkCodes + h * kHalfBytes + j * 16;
-  const int w8 = kOffW + wn * 4 * kChunkCodes + h * kHalfBytes + wrow * 8;
-  const int x8 = kOffX + wm * 4 * kChunkCodes + h * kHalfBytes + j * 8;
-  const int wsc = kOffWs + wn * 4 * kChunkScales + wrow * 4 + 2 * h;
-  const int xsc = kOffXs + wm * 4 * kChunkScales + j * 4 + 2 * h;
+  const int w16 = R::kOffW + wn * 4 * R::kChunkW + h * R::kHalfW + wrow * 16;
+  const int x16 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 16;
+  const int w8 = R::kOffW + wn * 4 * R::kChunkW + h * R::kHalfW + wrow * 8;
+  const int x8 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 8;
+  const int wsc = R::kOffWs + wn * 4 * kChunkScales + wrow * 4 + 2 * h;
+  const int xsc = R::kOffXs + wm * 4 * kChunkScales + j * 4 + 2 * h;
 
   v16f acc[4][4];
 #pragma unroll
@@ -216,205 +285,214 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fn][fm][r] = 0.0f;
 
-  // One sub-step operand is a 16-byte and an 8-byte LDS read landing in
-  // adjacent registers (the MFMA reads 6 of the 8).  The 8-byte reads are
-  // volatile so they are not fused into one 16-byte read whose halves would
-  // belong to different operands (that costs register moves).
+  // One sub-step operand of a 6-bit type is a 16-byte and an 8-byte LDS read
+  // landing in adjacent registers (the MFMA reads 6 of the 8); of an 8-bit
+  // type two 16-byte reads; of a 4-bit type one 16-byte read (the MFMA reads
+  // 4 registers).  With 4- and 6-bit operands a lane's registers hold the 32
+  // elements of its half's block; with 8-bit operands registers 0-3 of both
+  // lane halves make the first 32-element block of the instruction's K = 64
+  // (scaled by the byte of lanes 0-31) and registers 4-7 the second (scaled
+  // by lanes 32-63), so in sub-step s lane half h holds bytes 16h..16h+15 of
+  // blocks s and 2 + s, which the 8-bit layout's planes 2s and 2s + 1 store.  The 8-byte reads are volatile so they are not fused into
+  // one 16-byte read whose halves would belong to different operands (that
+  // costs register moves).
   typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2_t;
   auto rd16 = [&](int off) { return *reinterpret_cast<const u32x4*>(lds + off); };
   auto rd8 = [&](int off) { return (u32x2)(*(lds_u32x2_t*)(lds + off)); };
-  auto op0 = [&](int b16, int b8) {
-    const u32x4 a = rd16(b16 + kPlaneA);
-    const u32x2 c = rd8(b8 + kPlaneL);
-    return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], 0, 0};
+  // operand of sub-step SUB for an operand of BITS-bit codes at lane bases b16 / b8
+  auto op = [&](auto bits_tag, auto sub_tag, int b16, int b8) {
+    constexpr int BITS = decltype(bits_tag)::value, SUB = decltype(sub_tag)::value;
+    if constexpr (BITS == 6) {
+      if constexpr (SUB == 0) {
+        const u32x4 a = rd16(b16 + kPlaneA);
+        const u32x2 c = rd8(b8 + kPlaneL);
+        return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], 0, 0};
+      } else {
+        const u32x2 c = rd8(b8 + kPlaneH);
+        const u32x4 a = rd16(b16 + kPlaneB);
+        return v8i{(int)c[0], (int)c[1], (int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0};
+      }
+    } else if constexpr (BITS == 8) {
+      const u32x4 a = rd16(b16 + (2 * SUB) * kPlaneStride16);
+      const u32x4 c = rd16(b16 + (2 * SUB + 1) * kPlaneStride16);
+      return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+    } else {
+      const u32x4 a = rd16(b16 + SUB * kPlaneStride16);
+      return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    }
   };
-  auto op1 = [&](int b16, int b8) {
-    const u32x2 c = rd8(b8 + kPlaneH);
-    const u32x4 a = rd16(b16 + kPlaneB);
-    return v8i{(int)c[0], (int)c[1], (int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0};
-  };
+  using bw_t = std::integral_constant<int, R::kBW>;
+  using bx_t = std::integral_constant<int, R::kBX>;
+  constexpr int kDsW = R::kBW == 4 ? 1 : 2, kDsX = R::kBX == 4 ? 1 : 2;  // LDS reads per operand
   struct Half {  // one sub-step's operands: 4 weight and 4 activation fragments
-    v8i w0, w1, w2, w3, x0, x1, x2, x3;
+    v8i w[4], x[4];
   };
   struct Scales {  // scale byte pairs (blocks 2h, 2h+1) of the 8 fragments
-    int w0, w1, w2, w3, x0, x1, x2, x3;
+    int w[4], x[4];
+  };
+  // fragment i (0..7) of a sub-step, in the order w0, x0, w1, x1, ...
+  auto read_frag = [&](Half& r, int so, auto i_tag, auto sub_tag) {
+    constexpr int I = decltype(i_tag)::value;
+    constexpr int F = I / 2;
+    if constexpr (I % 2 == 0)
+      r.w[F] = op(bw_t{}, sub_tag, so + w16 + F * R::kChunkW, so + w8 + F * R::kChunkW);
+    else
+      r.x[F] = op(bx_t{}, sub_tag, so + x16 + F * R::kChunkX, so + x8 + F * R::kChunkX);
   };
   auto read_half = [&](int sl, auto sub_tag) {
-    constexpr int SUB = decltype(sub_tag)::value;
-    const int so = sl * kSlotBytes;
-    auto op = [&](int b16, int b8, int f) {
-      return SUB == 0 ? op0(so + b16 + f * kChunkCodes, so + b8 + f * kChunkCodes)
-                      : op1(so + b16 + f * kChunkCodes, so + b8 + f * kChunkCodes);
-    };
+    const int so = sl * R::kSlot;
     Half r;
-    r.w0 = op(w16, w8, 0);
-    r.x0 = op(x16, x8, 0);
-    r.w1 = op(w16, w8, 1);
-    r.x1 = op(x16, x8, 1);
-    r.w2 = op(w16, w8, 2);
-    r.x2 = op(x16, x8, 2);
-    r.w3 = op(w16, w8, 3);
-    r.x3 = op(x16, x8, 3);
+    static_for([&](auto i) { if constexpr (decltype(i)::value < 8) read_frag(r, so, i, sub_tag); }, Seq16{});
     return r;
   };
   auto scale_at = [&](int so, int base, int f) {
     return (int)*reinterpret_cast<const uint16_t*>(lds + so + base + f * kChunkScales);
   };
   auto read_scales = [&](int sl) {
-    const int so = sl * kSlotBytes;
+    const int so = sl * R::kSlot;
     Scales c;
-    c.w0 = scale_at(so, wsc, 0);
-    c.w1 = scale_at(so, wsc, 1);
-    c.w2 = scale_at(so, wsc, 2);
-    c.w3 = scale_at(so, wsc, 3);
-    c.x0 = scale_at(so, xsc, 0);
-    c.x1 = scale_at(so, xsc, 1);
-    c.x2 = scale_at(so, xsc, 2);
-    c.x3 = scale_at(so, xsc, 3);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      c.w[f] = scale_at(so, wsc, f);
+      c.x[f] = scale_at(so, xsc, f);
+    }
     return c;
   };
-#define MXG_MFMA(FN, FM, S) \
-  acc[FN][FM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(r.w##FN, r.x##FM, acc[FN][FM], WF, XF, S, c.w##FN, S, c.x##FM)
+  // MFMA i (0..15) of a sub-step: weight fragment i / 4 against activation fragment i % 4
+  auto mfma = [&](const Half& r, const Scales& c, auto i_tag, auto sub_tag) {
+    constexpr int I = decltype(i_tag)::value, S = decltype(sub_tag)::value;
+    constexpr int FN = I / 4, FM = I % 4;
+    acc[FN][FM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(r.w[FN], r.x[FM], acc[FN][FM], WF, XF, S, c.w[FN],
+                                                                 S, c.x[FM]);
+  };
   // the 16 MFMAs of one sub-step
   auto mfmas = [&](const Half& r, const Scales& c, auto sub_tag) {
-    constexpr int S = decltype(sub_tag)::value;
-    MXG_MFMA(0, 0, S); MXG_MFMA(0, 1, S); MXG_MFMA(0, 2, S); MXG_MFMA(0, 3, S);
-    MXG_MFMA(1, 0, S); MXG_MFMA(1, 1, S); MXG_MFMA(1, 2, S); MXG_MFMA(1, 3, S);
-    MXG_MFMA(2, 0, S); MXG_MFMA(2, 1, S); MXG_MFMA(2, 2, S); MXG_MFMA(2, 3, S);
-    MXG_MFMA(3, 0, S); MXG_MFMA(3, 1, S); MXG_MFMA(3, 2, S); MXG_MFMA(3, 3, S);
+    static_for([&](auto i) { mfma(r, c, i, sub_tag); }, Seq16{});
   };
-  // The steady-state phases, written in issue order (the LDS reads and the
-  // copies into LDS keep their program order).  Each stage's 14 copies are
-  // split: copies 0..6 of stage ks+3 go out in phase 1 of stage ks (into the
-  // slot stage ks has just been read from), copies 7..13 in phase 0 of stage
-  // ks+1, so the vector-memory path sees 7 copies per 16 MFMAs throughout.
-  // Phase 1: sub-step 1 MFMAs, reads of the next stage's sub-step 0 operands
-  // and scales, first half of stage ks2's copies into slot slot2.
-  auto phase1 = [&](const Half& r, const Scales& c, int ks2, int slot2, int nsl, Half& nr, Scales& ns) {
-    const int so = nsl * kSlotBytes;
-#define MXG_RD(DST, B16, B8, F) nr.DST = op0(so + B16 + (F) * kChunkCodes, so + B8 + (F) * kChunkCodes)
-    MXG_MFMA(0, 0, 1); MXG_RD(w0, w16, w8, 0); issue_one(0, ks2, slot2);
-    MXG_MFMA(0, 1, 1); MXG_RD(x0, x16, x8, 0);
-    MXG_MFMA(0, 2, 1); MXG_RD(w1, w16, w8, 1); issue_one(1, ks2, slot2);
-    MXG_MFMA(0, 3, 1); MXG_RD(x1, x16, x8, 1);
-    MXG_MFMA(1, 0, 1); MXG_RD(w2, w16, w8, 2); issue_one(2, ks2, slot2);
-    MXG_MFMA(1, 1, 1); MXG_RD(x2, x16, x8, 2);
-    MXG_MFMA(1, 2, 1); MXG_RD(w3, w16, w8, 3); issue_one(3, ks2, slot2);
-    MXG_MFMA(1, 3, 1); MXG_RD(x3, x16, x8, 3);
-    MXG_MFMA(2, 0, 1); ns.w0 = scale_at(so, wsc, 0); ns.w1 = scale_at(so, wsc, 1); issue_one(4, ks2, slot2);
-    MXG_MFMA(2, 1, 1); ns.w2 = scale_at(so, wsc, 2); ns.w3 = scale_at(so, wsc, 3);
-    MXG_MFMA(2, 2, 1); ns.x0 = scale_at(so, xsc, 0); ns.x1 = scale_at(so, xsc, 1); issue_one(5, ks2, slot2);
-    MXG_MFMA(2, 3, 1); ns.x2 = scale_at(so, xsc, 2); ns.x3 = scale_at(so, xsc, 3);
-    MXG_MFMA(3, 0, 1); issue_one(6, ks2, slot2);
-    MXG_MFMA(3, 1, 1);
-    MXG_MFMA(3, 2, 1);
-    MXG_MFMA(3, 3, 1);
-    // pin that order for the scheduler
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-#undef MXG_RD
-  };
-  // phase 0 with the second half (copies 7..13) of stage ks2 interleaved
-  auto phase0 = [&](const Half& r, const Scales& c, int sl, Half& nr, int ks2, int slot2) {
-    const int so = sl * kSlotBytes;
-#define MXG_RD1(DST, B16, B8, F) nr.DST = op1(so + B16 + (F) * kChunkCodes, so + B8 + (F) * kChunkCodes)
-    MXG_MFMA(0, 0, 0); MXG_RD1(w0, w16, w8, 0);
-    MXG_MFMA(0, 1, 0); MXG_RD1(x0, x16, x8, 0); issue_one(7, ks2, slot2);
-    MXG_MFMA(0, 2, 0); MXG_RD1(w1, w16, w8, 1);
-    MXG_MFMA(0, 3, 0); MXG_RD1(x1, x16, x8, 1); issue_one(8, ks2, slot2);
-    MXG_MFMA(1, 0, 0); MXG_RD1(w2, w16, w8, 2);
-    MXG_MFMA(1, 1, 0); MXG_RD1(x2, x16, x8, 2); issue_one(9, ks2, slot2);
-    MXG_MFMA(1, 2, 0); MXG_RD1(w3, w16, w8, 3);
-    MXG_MFMA(1, 3, 0); MXG_RD1(x3, x16, x8, 3); issue_one(10, ks2, slot2);
-    MXG_MFMA(2, 0, 0);
-    MXG_MFMA(2, 1, 0); issue_one(11, ks2, slot2);
-    MXG_MFMA(2, 2, 0);
-    MXG_MFMA(2, 3, 0); issue_one(12, ks2, slot2);
-    MXG_MFMA(3, 0, 0);
-    MXG_MFMA(3, 1, 0); issue_one(13, ks2, slot2);
-    MXG_MFMA(3, 2, 0);
-    MXG_MFMA(3, 3, 0);
-#undef MXG_RD1
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-  };
-#undef MXG_MFMA
-  static_assert(kCopiesPerStage == 14, "the phases interleave 7 + 7 copies");
-  auto next_slot = [](int sl) { return sl == 2 ? 0 : sl + 1; };
   using sub0 = std::integral_constant<int, 0>;
   using sub1 = std::integral_constant<int, 1>;
-
-  // ---- main loop over the 3-slot ring, with the operand registers double
-  // buffered at half-stage granularity.  At the top of stage ks the lane holds
-  // stage ks's sub-step 0 operands (ra) and scales (sc); all copies of stage
-  // ks+1 and the first half of stage ks+2's are in flight.  Phase 0: sub-step
-  // 0 MFMAs while reading stage ks's sub-step 1 operands (rb) and issuing the
-  // second half of stage ks+2's copies.  Then wait until at most one stage's
-  // copies are outstanding (they complete in order: stage ks+1 has landed),
-  // and barrier: every wave's part of stage ks+1 is visible and every wave is
-  // done reading slot ks.  Phase 1: sub-step 1 MFMAs while reading stage
-  // ks+1's sub-step 0 operands and scales and issuing the first half of stage
-  // ks+3's copies into slot ks.
-  auto issue_half = [&](int ks2, int sl2, int first) {
+  // The steady-state phases, written in issue order (the LDS reads and the
+  // copies into LDS keep their program order) and pinned for the scheduler
+  // by sched_group_barrier: after MFMA i, the LDS reads of fragment i (i < 8)
+  // or of two scale pairs (phase 1, 8 <= i < 12), then the copies scheduled
+  // after it.
+  // Phase 1: sub-step 1 MFMAs, reads of the next stage's sub-step 0 operands
+  // and scales, and the first kFirst copies of stage ks2 into slot slot2.
+  auto phase1 = [&](const Half& r, const Scales& c, int ks2, int slot2, int nsl, Half& nr, Scales& ns) {
+    const int so = nsl * R::kSlot;
+    static_for(
+        [&](auto i) {
+          constexpr int I = decltype(i)::value;
+          mfma(r, c, i, sub1{});
+          if constexpr (I < 8) read_frag(nr, so, i, sub0{});
+          if constexpr (I >= 8 && I < 12) {
+            constexpr int F = 2 * ((I - 8) & 1);
+            if constexpr (I < 10) {
+              ns.w[F] = scale_at(so, wsc, F);
+              ns.w[F + 1] = scale_at(so, wsc, F + 1);
+            } else {
+              ns.x[F] = scale_at(so, xsc, F);
+              ns.x[F + 1] = scale_at(so, xsc, F + 1);
+            }
+          }
+          constexpr int n = copies_after(I, R::kFirst, 1), c0 = first_copy_after(I, R::kFirst, 1);
 #pragma unroll
-    for (int i = 0; i < 7; ++i) issue_one(first + i, ks2, sl2);
+          for (int k = 0; k < n; ++k) issue_one(c0 + k, ks2, slot2);
+        },
+        Seq16{});
+    static_for(
+        [&](auto i) {
+          constexpr int I = decltype(i)::value;
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          constexpr int ds = I < 8 ? (I % 2 == 0 ? kDsW : kDsX) : (I < 12 ? 2 : 0);
+          if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
+          constexpr int n = copies_after(I, R::kFirst, 1);
+          if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
+        },
+        Seq16{});
   };
-  if (nk > 0) issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  if (nk > 2) issue_half(2, 2, 0);
-  if (nk > 2)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage + 7));
-  else if (nk > 1)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
-  else
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  // Phase 0: sub-step 0 MFMAs, reads of the same stage's sub-step 1
+  // operands, and copies kFirst.. of stage ks2 into slot slot2.
+  auto phase0 = [&](const Half& r, const Scales& c, int sl, Half& nr, int ks2, int slot2) {
+    const int so = sl * R::kSlot;
+    static_for(
+        [&](auto i) {
+          constexpr int I = decltype(i)::value;
+          mfma(r, c, i, sub0{});
+          if constexpr (I < 8) read_frag(nr, so, i, sub1{});
+          constexpr int n = copies_after(I, R::kSecond, 0), c0 = first_copy_after(I, R::kSecond, 0);
+#pragma unroll
+          for (int k = 0; k < n; ++k) issue_one(R::kFirst + c0 + k, ks2, slot2);
+        },
+        Seq16{});
+    static_for(
+        [&](auto i) {
+          constexpr int I = decltype(i)::value;
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          constexpr int ds = I < 8 ? (I % 2 == 0 ? kDsW : kDsX) : 0;
+          if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
+          constexpr int n = copies_after(I, R::kSecond, 0);
+          if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
+        },
+        Seq16{});
+  };
+  auto next_slot = [](int sl) { return sl + 1 == R::kSlots ? 0 : sl + 1; };
+
+  // ---- main loop over the ring, with the operand registers double buffered
+  // at half-stage granularity.  At the top of stage ks the lane holds stage
+  // ks's sub-step 0 operands (ra) and scales (sc).  Phase 0: sub-step 0 MFMAs
+  // while reading stage ks's sub-step 1 operands (rb) (and, with three slots,
+  // issuing the second half of stage ks+2's copies).  Then wait until stage
+  // ks+1 has landed (copies complete in order: with three slots at most stage
+  // ks+2's copies may still be outstanding, with two none), and barrier: every
+  // wave's part of stage ks+1 is visible and every wave is done reading slot
+  // ks.  Phase 1: sub-step 1 MFMAs while reading stage ks+1's sub-step 0
+  // operands and scales and issuing copies of stage ks+kSlots into slot ks.
+  constexpr int kMidWait = R::kSlots == 3 ? R::kCopies : 0;
+  if (nk > 0) issue_range(0, 0, 0, R::kCopies);
+  if (nk > 1) issue_range(1, 1, 0, R::kCopies);
+  if constexpr (R::kSlots == 3) {
+    if (nk > 2) issue_range(2, 2, 0, R::kFirst);
+    if (nk > 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(R::kCopies + R::kFirst));
+    else if (nk > 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(R::kCopies));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  } else {
+    if (nk > 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(R::kCopies));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  }
   __builtin_amdgcn_s_barrier();
   Half ra = read_half(0, sub0{});
   Scales sc = read_scales(0);
   int ks = 0, slot = 0;
-  for (; ks + 3 < nk; ++ks) {
+  for (; ks + R::kSlots < nk; ++ks) {
     const int nsl = next_slot(slot);
     Half rb;
     phase0(ra, sc, slot, rb, ks + 2, next_slot(nsl));
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kMidWait));
     __builtin_amdgcn_s_barrier();
     Scales sn;
-    phase1(rb, sc, ks + 3, slot, nsl, ra, sn);
+    phase1(rb, sc, ks + R::kSlots, slot, nsl, ra, sn);
     __builtin_amdgcn_sched_barrier(0);
     sc = sn;
     slot = nsl;
   }
   for (; ks < nk; ++ks) {
     const int nsl = next_slot(slot);
-    if (ks + 2 < nk) issue_half(ks + 2, next_slot(nsl), 7);
+    if constexpr (R::kSlots == 3) {
+      if (ks + 2 < nk) issue_range(ks + 2, next_slot(nsl), R::kFirst, R::kSecond);
+    }
     const Half rb = read_half(slot, sub1{});
     mfmas(ra, sc, sub0{});
     Scales sn = sc;
     if (ks + 1 < nk) {
-      if (ks + 2 < nk)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerStage));
+      if (R::kSlots == 3 && ks + 2 < nk)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(R::kCopies));
       else
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
       __builtin_amdgcn_s_barrier();
@@ -590,8 +668,10 @@ void launch_epi(const GemmArgs& a, int out_kind, int out_fmt, dim3 grid, dim3 bl
     hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE3M2>), grid, block, 0, stream, a);
 }
 
+// The 6-bit pairs: every epilogue and output kind.
 template <int WF, int XF>
-hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream) {
+hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream,
+                          std::true_type) {
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
   if (epilogue == kEpiGeluTanh)
     launch_epi<WF, XF, kEpiGeluTanh>(a, out_kind, out_fmt, grid, block, stream);
@@ -602,13 +682,26 @@ hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out
   return hipGetLastError();
 }
 
+// The 4- and 8-bit operand formats: plain product, fp32 or bf16 output.
+template <int WF, int XF>
+hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int, hipStream_t stream, std::false_type) {
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+  if (epilogue != kEpiNone || out_kind == kOutMx) return hipErrorInvalidValue;
+  if (out_kind == kOutF32)
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, kEpiNone, kFmtE2M3>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, kEpiNone, kFmtE2M3>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // One translation unit per (weight, activation) format pair, so the variants
 // build in parallel.
 template <int WF, int XF>
 hipError_t launch_gemm_formats(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream) {
-  return launch_variant<WF, XF>(a, epilogue, out_kind, out_fmt, stream);
+  return launch_variant<WF, XF>(a, epilogue, out_kind, out_fmt, stream,
+                                std::integral_constant<bool, fmt_bits(WF) == 6 && fmt_bits(XF) == 6>{});
 }
 
 }  // namespace mxg

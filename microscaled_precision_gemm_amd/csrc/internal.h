@@ -16,12 +16,26 @@ constexpr int kOutMx = 2;
 constexpr int kLayoutRows = 0;
 constexpr int kLayoutTiled = 1;
 
-// Tiled MX layout: 128-element stages x 32-row groups, 3072 code bytes and
-// 128 scale bytes per (stage, group).
+// Element formats; the values are the format codes of the gfx950 scaled
+// f8f6f4 MFMA instructions.
+constexpr int kFmtE4M3 = 0;
+constexpr int kFmtE5M2 = 1;
+constexpr int kFmtE2M3 = 2;
+constexpr int kFmtE3M2 = 3;
+constexpr int kFmtE2M1 = 4;
+
+// Bits per element code: a 32-element block is 4 * bits bytes, and the
+// block's codes fill `bits` dwords.
+constexpr int fmt_bits(int fmt) { return fmt == kFmtE2M1 ? 4 : (fmt == kFmtE4M3 || fmt == kFmtE5M2) ? 8 : 6; }
+
+// Tiled MX layout: 128-element stages x 32-row groups, 512 * bits code bytes
+// (3072 for the 6-bit types) and 128 scale bytes per (stage, group).
 constexpr int kTileStageK = 128;
 constexpr int kTileGroupRows = 32;
 constexpr int kChunkCodes = 3072;
 constexpr int kChunkScales = 128;
+constexpr int chunk_codes(int bits) { return 512 * bits; }
+constexpr int half_codes(int bits) { return 256 * bits; }
 // Planes of one half (blocks 2h and 2h+1 of a stage, 32 rows) of a tiled chunk:
 // A = bytes 0..15 of block 2h (16 per row), L = its bytes 16..23 (8 per row),
 // H = bytes 0..7 of block 2h+1 (8 per row), B = its bytes 8..23 (16 per row).
@@ -30,6 +44,11 @@ constexpr int kPlaneA = 0;
 constexpr int kPlaneL = 512;
 constexpr int kPlaneH = 768;
 constexpr int kPlaneB = 1024;
+// 8-bit types: four planes of 16 bytes per row in each 2048-byte half h:
+// bytes 16h..16h+15 of blocks 0, 2, 1, 3 (plane 2s + r holds block 2r + s).
+// 4-bit types: two planes of 16 bytes per row in each 1024-byte half: block
+// 2h, then block 2h+1.
+constexpr int kPlaneStride16 = 512;  // one plane of 32 rows x 16 bytes
 
 constexpr int kEpiNone = 0;
 constexpr int kEpiGeluTanh = 1;
@@ -102,8 +121,8 @@ template <int WF, int XF>
 hipError_t launch_gemm_formats(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline int64_t tiled_codes_bytes(int64_t rows, int64_t k) {
-  return ceil_div(k, kTileStageK) * ceil_div(rows, kTileGroupRows) * kChunkCodes;
+inline int64_t tiled_codes_bytes(int64_t rows, int64_t k, int bits) {
+  return ceil_div(k, kTileStageK) * ceil_div(rows, kTileGroupRows) * chunk_codes(bits);
 }
 inline int64_t tiled_scales_bytes(int64_t rows, int64_t k) {
   return ceil_div(k, kTileStageK) * ceil_div(rows, kTileGroupRows) * kChunkScales;

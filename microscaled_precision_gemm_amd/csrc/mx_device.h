@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace mxg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -24,13 +26,20 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kFmtE2M3 = 2;
-constexpr int kFmtE3M2 = 3;
+typedef short v2s __attribute__((ext_vector_type(2)));
 
-// floor(log2(max magnitude)) of the element format: 7.5 = 1.875 * 2^2, 28 = 1.75 * 2^4.
+// floor(log2(max magnitude)) of the element format: E2M3 7.5 = 1.875 * 2^2,
+// E3M2 28 = 1.75 * 2^4, E2M1 6 = 1.5 * 2^2, E4M3 448 = 1.75 * 2^8, E5M2
+// 57344 = 1.75 * 2^15.
 template <int FMT>
 __device__ __forceinline__ constexpr int emax_elem() {
-  return FMT == kFmtE2M3 ? 2 : 4;
+  return FMT == kFmtE2M3 ? 2 : FMT == kFmtE3M2 ? 4 : FMT == kFmtE2M1 ? 2 : FMT == kFmtE4M3 ? 8 : 15;
+}
+
+// Largest finite magnitude of the element format.
+template <int FMT>
+__device__ __forceinline__ constexpr float max_elem() {
+  return FMT == kFmtE2M3 ? 7.5f : FMT == kFmtE3M2 ? 28.0f : FMT == kFmtE2M1 ? 6.0f : FMT == kFmtE4M3 ? 448.0f : 57344.0f;
 }
 
 // Result of the scale rule for one block.
@@ -107,6 +116,56 @@ __device__ __forceinline__ v6u cvt_f32x2x16(v16f a, v16f b, float scale) {
   else
     asm("v_cvt_scalef32_2xpk16_bf6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(a), "v"(b), "v"(scale));
   return r;
+}
+
+// One block of 32 fp32 values (element i in v[i]) -> its codes packed as
+// fmt_bits(FMT) dwords (element i at bits [b*i, b*i+b) of the block; E2M1:
+// element 2i in the low nibble of byte i).  The 6-bit types go through the
+// 2 x 16 conversion above, which saturates by itself.  For the 8- and 4-bit
+// types the values are first clamped to +-max_elem * scale (exact in fp32, an
+// infinity only where no finite input can exceed it), so the conversion only
+// rounds: its handling of out-of-range inputs never enters.  The clamp keeps
+// the sign of zeros.
+template <int FMT>
+__device__ __forceinline__ void cvt_block(const float (&v)[32], float scale, uint32_t (&q)[fmt_bits(FMT)]) {
+  if constexpr (fmt_bits(FMT) == 6) {
+    v16f even, odd;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      even[i] = v[2 * i];
+      odd[i] = v[2 * i + 1];
+    }
+    const v6u r = cvt_f32x2x16<FMT>(even, odd, scale);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) q[i] = r[i];
+  } else {
+    const float bound = max_elem<FMT>() * scale;
+    auto cl = [&](float x) { return __builtin_amdgcn_fmed3f(x, -bound, bound); };
+    if constexpr (fmt_bits(FMT) == 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v2s w = {0, 0};
+        if constexpr (FMT == kFmtE4M3) {
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(v[4 * i]), cl(v[4 * i + 1]), scale, false);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, cl(v[4 * i + 2]), cl(v[4 * i + 3]), scale, true);
+        } else {
+          w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, cl(v[4 * i]), cl(v[4 * i + 1]), scale, false);
+          w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(w, cl(v[4 * i + 2]), cl(v[4 * i + 3]), scale, true);
+        }
+        __builtin_memcpy(&q[i], &w, 4);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, cl(v[8 * i]), cl(v[8 * i + 1]), scale, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, cl(v[8 * i + 2]), cl(v[8 * i + 3]), scale, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, cl(v[8 * i + 4]), cl(v[8 * i + 5]), scale, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, cl(v[8 * i + 6]), cl(v[8 * i + 7]), scale, 3);
+        q[i] = w;
+      }
+    }
+  }
 }
 
 // GELU, tanh form, in fp32: 0.5 x (1 + tanh(u)) = x / (1 + e^{-2u}) with

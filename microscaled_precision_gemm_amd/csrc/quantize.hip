@@ -1,18 +1,22 @@
-// bf16 / fp32 -> MX (E2M3 or E3M2) quantizer for gfx950.
+// bf16 / fp32 -> MX quantizer for gfx950: the 6-bit element types E2M3 and
+// E3M2, and the 4- and 8-bit types E2M1, E4M3 and E5M2 that the same scaled
+// matrix instruction consumes.
 //
 // Each wave quantizes 64 consecutive 32-element blocks (row-major order over
-// [rows, K/32]).  HBM-bound (2 or 4 bytes in, 0.78 bytes out per element), so
-// the design is about full-width memory transactions:
+// [rows, K/32]).  HBM-bound (2 or 4 bytes in, 0.5 to 1 byte out per element),
+// so the design is about full-width memory transactions:
 //
 //  * loads: the wave reads its blocks as 16-byte pieces with consecutive lanes
 //    on consecutive pieces (the 128-bit coalesced loads of the page "Creating
 //    Custom Kernels for the AMD MI300", section "Fused RMS Norm Kernel"), and
 //    an LDS transpose hands each lane one whole block;
 //  * per block: amax on the raw magnitude bits, the E8M0 scale from the
-//    exponent bits, and one v_cvt_scalef32 instruction that rounds all 32
-//    elements (round-to-nearest-even, saturating, sign kept);
-//  * stores: the 64 x 24 code bytes of a wave are contiguous in the output, so
-//    they go back through LDS and leave as 16-byte stores of consecutive lanes.
+//    exponent bits, and the v_cvt_scalef32 conversions that round the 32
+//    elements (round-to-nearest-even, saturating, sign kept): one instruction
+//    for a 6-bit block, 16 two-element ones for a 4- or 8-bit block;
+//  * stores: the 64 blocks' code bytes of a wave are contiguous in the output,
+//    so they go back through LDS and leave as 16-byte stores of consecutive
+//    lanes.
 #include "internal.h"
 #include "mx_device.h"
 
@@ -24,7 +28,72 @@ constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / 64;
 constexpr int kInRowB = 16 * 5;                  // one block's bf16 bytes (64) padded to 80 for the LDS read
 constexpr int kInRowF = 16 * 9;                  // fp32 (128) padded to 144
-constexpr int kOutBytes = 64 * 24;               // code bytes of one wave
+constexpr int kOutBytes = 64 * 32;               // code bytes of one wave (at most 32 per block)
+
+// The 32 source values of a block held as 4 (bf16) or 8 (fp32) 16-byte pieces
+// -> fp32, element i in v[i].
+template <bool F32>
+__device__ __forceinline__ void block_to_f32(const u32x4* w, float (&v)[32]) {
+#pragma unroll
+  for (int i = 0; i < (F32 ? 8 : 4); ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (F32) {
+        v[4 * i + e] = __uint_as_float(w[i][e]);
+      } else {
+        v[8 * i + 2 * e] = __uint_as_float(w[i][e] << 16);
+        v[8 * i + 2 * e + 1] = __uint_as_float(w[i][e] & 0xffff0000u);
+      }
+    }
+}
+
+// Scale rule + conversion of one block given as 16-byte pieces.  The 6-bit
+// types convert bf16 directly with the 32-element instruction; everything else
+// goes through fp32 values.
+template <int FMT, bool F32>
+__device__ __forceinline__ uint32_t quantize_block(const u32x4* w, uint32_t (&q)[fmt_bits(FMT)]) {
+  BlockScale s;
+  if constexpr (!F32) {
+    // bf16: amax of the magnitude bits, two halves per dword (bit order = value order)
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = w[i][j] & 0x7fff7fffu;
+        u16x2 v;
+        __builtin_memcpy(&v, &a, 4);
+        m2 = __builtin_elementwise_max(m2, v);
+      }
+    s = scale_from_bf16_bits<FMT>(m2[0] > m2[1] ? m2[0] : m2[1]);
+  } else {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = w[i][j] & 0x7fffffffu;
+        amax = a > amax ? a : amax;
+      }
+    s = scale_from_f32_bits<FMT>(amax);
+  }
+  if constexpr (!F32 && fmt_bits(FMT) == 6) {
+    v32bf x;
+    __builtin_memcpy(&x, w, 64);
+    const v6u r = cvt_bf16x32<FMT>(x, s.scale);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) q[i] = r[i];
+  } else {
+    float v[32];
+    block_to_f32<F32>(w, v);
+    cvt_block<FMT>(v, s.scale, q);
+  }
+  if (s.nonfinite) {
+#pragma unroll
+    for (int i = 0; i < fmt_bits(FMT); ++i) q[i] = 0u;
+  }
+  return s.byte;
+}
 
 template <bool F32>
 struct QLayout {
@@ -65,79 +134,45 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint8_t* __re
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
   // ---- one block per lane
+  constexpr int kBits = fmt_bits(FMT), kEB = 4 * kBits;  // code dwords / bytes per block
   const int64_t b = wave_first + lane;
   u32x4 w[L::kPieces];
 #pragma unroll
   for (int i = 0; i < L::kPieces; ++i) w[i] = *reinterpret_cast<const u32x4*>(in + lane * L::kRow + i * 16);
-  BlockScale s;
-  v6u q;
-  if constexpr (!F32) {
-    // bf16: amax of the magnitude bits, two halves per dword (bit order = value order)
-    u16x2 m2 = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = w[i][j] & 0x7fff7fffu;
-        u16x2 v;
-        __builtin_memcpy(&v, &a, 4);
-        m2 = __builtin_elementwise_max(m2, v);
-      }
-    const uint32_t amax = m2[0] > m2[1] ? m2[0] : m2[1];
-    s = scale_from_bf16_bits<FMT>(amax);
-    v32bf x;
-    __builtin_memcpy(&x, w, 64);
-    q = cvt_bf16x32<FMT>(x, s.scale);
-  } else {
-    uint32_t amax = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = w[i][j] & 0x7fffffffu;
-        amax = a > amax ? a : amax;
-      }
-    s = scale_from_f32_bits<FMT>(amax);
-    // element 2i of the convert comes from the first operand, 2i+1 from the second
-    v16f even, odd;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      even[i] = __uint_as_float(w[i / 2][(2 * i) % 4]);
-      odd[i] = __uint_as_float(w[i / 2][(2 * i) % 4 + 1]);
-    }
-    q = cvt_f32x2x16<FMT>(even, odd, s.scale);
-  }
-  if (s.nonfinite) q = v6u{0, 0, 0, 0, 0, 0};
-  if (b < total_blocks) scales[b] = (uint8_t)s.byte;
+  uint32_t q[kBits];
+  const uint32_t byte = quantize_block<FMT, F32>(w, q);
+  if (b < total_blocks) scales[b] = (uint8_t)byte;
 
-  // ---- stores: the wave's code bytes are contiguous at codes + 24 * wave_first
+  // ---- stores: the wave's code bytes are contiguous at codes + kEB * wave_first
   const int nblk = (int)min((int64_t)64, total_blocks - wave_first);
   if (vec_out && nblk == 64) {
-    u32x2* o = reinterpret_cast<u32x2*>(outb + 24 * lane);
-    o[0] = u32x2{q[0], q[1]};
-    o[1] = u32x2{q[2], q[3]};
-    o[2] = u32x2{q[4], q[5]};
+#pragma unroll
+    for (int i = 0; i < kBits / 2; ++i)
+      *reinterpret_cast<u32x2*>(outb + kEB * lane + 8 * i) = u32x2{q[2 * i], q[2 * i + 1]};
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    uint8_t* dst = codes + 24 * wave_first;
-    *reinterpret_cast<u32x4*>(dst + 16 * lane) = *reinterpret_cast<const u32x4*>(outb + 16 * lane);
-    if (lane < 32)
-      *reinterpret_cast<u32x4*>(dst + 1024 + 16 * lane) = *reinterpret_cast<const u32x4*>(outb + 1024 + 16 * lane);
+    uint8_t* dst = codes + (int64_t)kEB * wave_first;
+#pragma unroll
+    for (int p = lane; p < 4 * kEB; p += 64)
+      *reinterpret_cast<u32x4*>(dst + 16 * p) = *reinterpret_cast<const u32x4*>(outb + 16 * p);
   } else if (b < total_blocks) {
-    u32x2* o = reinterpret_cast<u32x2*>(codes + 24 * b);
-    o[0] = u32x2{q[0], q[1]};
-    o[1] = u32x2{q[2], q[3]};
-    o[2] = u32x2{q[4], q[5]};
+    u32x2* o = reinterpret_cast<u32x2*>(codes + kEB * b);
+#pragma unroll
+    for (int i = 0; i < kBits / 2; ++i) o[i] = u32x2{q[2 * i], q[2 * i + 1]};
   }
 }
 
 // ---- tiled layout: one wave per (stage, 32-row group) chunk of 32 rows x 128
 // elements.  Loads: 256 (bf16) or 512 (fp32) contiguous bytes per row, 16 per
 // lane, consecutive lanes on consecutive bytes.  Each lane then converts two
-// blocks of one row (blocks 2h, 2h+1 for lane half h), whose 48 code bytes
-// fill that row's entries of the four planes of half h: the 32 lanes of a half
-// write runs of 512, 256, 256 and 512 contiguous bytes.  Rows >= rows and
-// blocks >= K/32 are written as padding (codes 0, scale 127).
+// blocks of one row (blocks 2h, 2h+1 for lane half h), whose code bytes fill
+// that row's entries of the planes of half h: for the 6-bit types 48 bytes in
+// four planes (the 32 lanes of a half write runs of 512, 256, 256 and 512
+// contiguous bytes), for the 8- and 4-bit types 64 or 32 bytes in 16-byte
+// planes (runs of 512 bytes; an 8-bit block is split between the two halves
+// of the chunk, the order in which the matrix instruction takes 8-bit
+// operands).  Rows >= rows and blocks >= K/32 are written as padding (codes
+// 0, scale 127).
 constexpr int kTWaves = 4;
 
 template <bool F32>
@@ -179,72 +214,71 @@ __global__ __launch_bounds__(kTWaves * 64) void quantize_tiled_kernel(const uint
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
+  constexpr int kBits = fmt_bits(FMT);
   const int j = lane & 31, h = lane >> 5;
   const int row = grp * 32 + j;
-  v6u q[2];
+  uint32_t q[2][kBits];
   uint32_t sb[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int qb = 2 * h + t;
     const uint8_t* p = in + j * L::kRow + qb * L::kBlockSrc;
-    BlockScale s;
-    v6u r;
-    if constexpr (!F32) {
-      u32x4 w[4];
+    u32x4 w[F32 ? 8 : 4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
-      u16x2 m2 = {0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a = w[i][e] & 0x7fff7fffu;
-          u16x2 vv;
-          __builtin_memcpy(&vv, &a, 4);
-          m2 = __builtin_elementwise_max(m2, vv);
-        }
-      s = scale_from_bf16_bits<FMT>(m2[0] > m2[1] ? m2[0] : m2[1]);
-      v32bf x;
-      __builtin_memcpy(&x, w, 64);
-      r = cvt_bf16x32<FMT>(x, s.scale);
-    } else {
-      u32x4 w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
-      uint32_t amax = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a = w[i][e] & 0x7fffffffu;
-          amax = a > amax ? a : amax;
-        }
-      s = scale_from_f32_bits<FMT>(amax);
-      v16f even, odd;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        even[i] = __uint_as_float(w[i / 2][(2 * i) % 4]);
-        odd[i] = __uint_as_float(w[i / 2][(2 * i) % 4 + 1]);
-      }
-      r = cvt_f32x2x16<FMT>(even, odd, s.scale);
-    }
-    uint32_t byte = s.byte;
-    if (s.nonfinite) r = v6u{0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < (F32 ? 8 : 4); ++i) w[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
+    sb[t] = quantize_block<FMT, F32>(w, q[t]);
     if (row >= rows || stage * 4 + qb >= kblocks) {  // padding
-      r = v6u{0, 0, 0, 0, 0, 0};
-      byte = 127u;
+#pragma unroll
+      for (int i = 0; i < kBits; ++i) q[t][i] = 0u;
+      sb[t] = 127u;
     }
-    q[t] = r;
-    sb[t] = byte;
   }
-  // the 48 code bytes of row j in the planes of half h
-  uint8_t* half = codes + (int64_t)chunk * kChunkCodes + h * kHalfBytes;
-  *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
-  *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
-  *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
-  *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
+  // the code bytes of row j in the planes of half h
+  uint8_t* half = codes + (int64_t)chunk * chunk_codes(kBits) + h * half_codes(kBits);
+  if constexpr (kBits == 6) {
+    *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
+    *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
+    *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
+    *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
+  } else if constexpr (kBits == 4) {
+    // 16-byte planes: block 2h, then block 2h+1
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      *reinterpret_cast<u32x4*>(half + t * kPlaneStride16 + j * 16) = u32x4{q[t][0], q[t][1], q[t][2], q[t][3]};
+  } else {
+    // 8 bits: block q = 2h + t goes to plane 2t + h of both halves, its bytes
+    // 0..15 in half 0 and 16..31 in half 1
+    uint8_t* chunk_base = codes + (int64_t)chunk * chunk_codes(kBits);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        *reinterpret_cast<u32x4*>(chunk_base + hh * half_codes(kBits) + (2 * t + h) * kPlaneStride16 + j * 16) =
+            u32x4{q[t][4 * hh], q[t][4 * hh + 1], q[t][4 * hh + 2], q[t][4 * hh + 3]};
+  }
   *reinterpret_cast<uint16_t*>(scales + (int64_t)chunk * kChunkScales + j * 4 + 2 * h) =
       (uint16_t)(sb[0] | (sb[1] << 8));
+}
+
+template <int FMT>
+void launch_rows_fmt(const uint8_t* s, bool f32, int64_t ldb, int64_t kblocks, int64_t total, uint8_t* codes,
+                     uint8_t* scales, int vec_out, dim3 g, dim3 blk, hipStream_t stream) {
+  if (f32)
+    hipLaunchKernelGGL((quantize_kernel<FMT, true>), g, blk, 0, stream, s, ldb, kblocks, total, codes, scales, vec_out);
+  else
+    hipLaunchKernelGGL((quantize_kernel<FMT, false>), g, blk, 0, stream, s, ldb, kblocks, total, codes, scales,
+                       vec_out);
+}
+
+template <int FMT>
+void launch_tiled_fmt(const uint8_t* s, bool f32, int64_t ldb, int rows, int k, int groups, int nchunks,
+                      uint8_t* codes, uint8_t* scales, dim3 g, dim3 blk, hipStream_t stream) {
+  if (f32)
+    hipLaunchKernelGGL((quantize_tiled_kernel<FMT, true>), g, blk, 0, stream, s, ldb, rows, k, groups, nchunks, codes,
+                       scales);
+  else
+    hipLaunchKernelGGL((quantize_tiled_kernel<FMT, false>), g, blk, 0, stream, s, ldb, rows, k, groups, nchunks, codes,
+                       scales);
 }
 
 }  // namespace
@@ -257,29 +291,19 @@ hipError_t launch_quantize(const void* src, int src_type, int64_t rows, int64_t 
   const int64_t grid = (total + 64 * kQWaves - 1) / (64 * kQWaves);
   const uint8_t* s = static_cast<const uint8_t*>(src);
   const int vec_out = ((uintptr_t)codes % 16) == 0;
-  const int64_t esize = src_type == kSrcBf16 ? 2 : 4;
+  const int64_t ldb = ld_src * (src_type == kSrcBf16 ? 2 : 4);
+  const bool f32 = src_type == kSrcF32;
   const dim3 g((unsigned)grid), blk(kQThreads);
-  if (src_type == kSrcBf16) {
-    if (fmt == kFmtE2M3)
-      hipLaunchKernelGGL((quantize_kernel<kFmtE2M3, false>), g, blk, 0, stream, s, ld_src * esize, kblocks, total,
-                         codes, scales, vec_out);
-    else
-      hipLaunchKernelGGL((quantize_kernel<kFmtE3M2, false>), g, blk, 0, stream, s, ld_src * esize, kblocks, total,
-                         codes, scales, vec_out);
-  } else {
-    if (fmt == kFmtE2M3)
-      hipLaunchKernelGGL((quantize_kernel<kFmtE2M3, true>), g, blk, 0, stream, s, ld_src * esize, kblocks, total,
-                         codes, scales, vec_out);
-    else
-      hipLaunchKernelGGL((quantize_kernel<kFmtE3M2, true>), g, blk, 0, stream, s, ld_src * esize, kblocks, total,
-                         codes, scales, vec_out);
+  switch (fmt) {
+    case kFmtE2M3: launch_rows_fmt<kFmtE2M3>(s, f32, ldb, kblocks, total, codes, scales, vec_out, g, blk, stream); break;
+    case kFmtE3M2: launch_rows_fmt<kFmtE3M2>(s, f32, ldb, kblocks, total, codes, scales, vec_out, g, blk, stream); break;
+    case kFmtE2M1: launch_rows_fmt<kFmtE2M1>(s, f32, ldb, kblocks, total, codes, scales, vec_out, g, blk, stream); break;
+    case kFmtE4M3: launch_rows_fmt<kFmtE4M3>(s, f32, ldb, kblocks, total, codes, scales, vec_out, g, blk, stream); break;
+    case kFmtE5M2: launch_rows_fmt<kFmtE5M2>(s, f32, ldb, kblocks, total, codes, scales, vec_out, g, blk, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-
-}  // namespace mxg
-
-namespace mxg {
 
 hipError_t launch_quantize_tiled(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,
                                  uint8_t* codes, uint8_t* scales, hipStream_t stream) {
@@ -289,20 +313,15 @@ hipError_t launch_quantize_tiled(const void* src, int src_type, int64_t rows, in
   const dim3 g((unsigned)ceil_div(nchunks, kTWaves)), blk(kTWaves * 64);
   const uint8_t* s = static_cast<const uint8_t*>(src);
   const int64_t ldb = ld_src * (src_type == kSrcBf16 ? 2 : 4);
-  if (src_type == kSrcBf16) {
-    if (fmt == kFmtE2M3)
-      hipLaunchKernelGGL((quantize_tiled_kernel<kFmtE2M3, false>), g, blk, 0, stream, s, ldb, (int)rows, (int)k,
-                         (int)groups, (int)nchunks, codes, scales);
-    else
-      hipLaunchKernelGGL((quantize_tiled_kernel<kFmtE3M2, false>), g, blk, 0, stream, s, ldb, (int)rows, (int)k,
-                         (int)groups, (int)nchunks, codes, scales);
-  } else {
-    if (fmt == kFmtE2M3)
-      hipLaunchKernelGGL((quantize_tiled_kernel<kFmtE2M3, true>), g, blk, 0, stream, s, ldb, (int)rows, (int)k,
-                         (int)groups, (int)nchunks, codes, scales);
-    else
-      hipLaunchKernelGGL((quantize_tiled_kernel<kFmtE3M2, true>), g, blk, 0, stream, s, ldb, (int)rows, (int)k,
-                         (int)groups, (int)nchunks, codes, scales);
+  const bool f32 = src_type == kSrcF32;
+  const int r = (int)rows, kk = (int)k, gr = (int)groups, nc = (int)nchunks;
+  switch (fmt) {
+    case kFmtE2M3: launch_tiled_fmt<kFmtE2M3>(s, f32, ldb, r, kk, gr, nc, codes, scales, g, blk, stream); break;
+    case kFmtE3M2: launch_tiled_fmt<kFmtE3M2>(s, f32, ldb, r, kk, gr, nc, codes, scales, g, blk, stream); break;
+    case kFmtE2M1: launch_tiled_fmt<kFmtE2M1>(s, f32, ldb, r, kk, gr, nc, codes, scales, g, blk, stream); break;
+    case kFmtE4M3: launch_tiled_fmt<kFmtE4M3>(s, f32, ldb, r, kk, gr, nc, codes, scales, g, blk, stream); break;
+    case kFmtE5M2: launch_tiled_fmt<kFmtE5M2>(s, f32, ldb, r, kk, gr, nc, codes, scales, g, blk, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -30,47 +30,60 @@ def oracle_mx(x64: np.ndarray, fmt: str):
     return codes, scales, O.dequantize(codes, scales, fmt)
 
 
-def tiled_chunk_offsets() -> np.ndarray:
-    """offsets[j, b]: where byte b (0..95) of row j's 96-byte packed slice of a
-    128-element stage sits inside its 3072-byte tiled chunk.  Half h (blocks 2h
-    and 2h+1) owns bytes [1536h, 1536h+1536): plane A (bytes 0..15 of block 2h,
-    16 per row), plane L (its bytes 16..23, 8 per row), plane H (bytes 0..7 of
-    block 2h+1, 8 per row), plane B (its bytes 8..23, 16 per row)."""
-    off = np.empty((32, 96), dtype=np.int64)
+def tiled_chunk_offsets(bits: int = 6) -> np.ndarray:
+    """offsets[j, b]: where byte b of row j's packed slice of a 128-element
+    stage (16 * bits bytes: four blocks of 4 * bits bytes) sits inside its
+    tiled chunk of 512 * bits bytes, as the library's header defines the
+    layout.  Half h (blocks 2h and 2h+1) owns bytes [256 bits h, 256 bits
+    (h+1)).  6 bits: plane A (bytes 0..15 of block 2h, 16 per row), plane L
+    (its bytes 16..23, 8 per row), plane H (bytes 0..7 of block 2h+1, 8 per
+    row), plane B (its bytes 8..23, 16 per row).  4 bits: planes of 16 bytes
+    per row, block 2h then block 2h+1.  8 bits: half h holds bytes 16h..16h+15
+    of blocks 0, 2, 1, 3 in four planes of 16 bytes per row."""
+    eb = 4 * bits
+    off = np.empty((32, 4 * eb), dtype=np.int64)
     for j in range(32):
-        for b in range(96):
-            q, t = divmod(b, 24)
-            base = (q >> 1) * 1536
-            if q % 2 == 0:
-                off[j, b] = base + (j * 16 + t if t < 16 else 512 + j * 8 + (t - 16))
+        for b in range(4 * eb):
+            q, t = divmod(b, eb)
+            base = (q >> 1) * 256 * bits
+            if bits == 6:
+                if q % 2 == 0:
+                    off[j, b] = base + (j * 16 + t if t < 16 else 512 + j * 8 + (t - 16))
+                else:
+                    off[j, b] = base + (768 + j * 8 + t if t < 8 else 1024 + j * 16 + (t - 8))
+            elif bits == 4:
+                off[j, b] = (q >> 1) * 1024 + (q % 2) * 512 + j * 16 + t
             else:
-                off[j, b] = base + (768 + j * 8 + t if t < 8 else 1024 + j * 16 + (t - 8))
+                hh = t // 16  # bytes 0..15 in half 0, 16..31 in half 1
+                off[j, b] = hh * 2048 + (2 * (q % 2) + (q >> 1)) * 512 + j * 16 + t % 16
     return off
 
 
-_CHUNK_OFFSETS = tiled_chunk_offsets()
+_CHUNK_OFFSETS = {b: tiled_chunk_offsets(b) for b in (4, 6, 8)}
 
 
-def tiled_to_rows(codes_t: np.ndarray, scales_t: np.ndarray, rows: int, k: int):
+def tiled_to_rows(codes_t: np.ndarray, scales_t: np.ndarray, rows: int, k: int, bits: int = 6):
     """Rearrange the tiled MX layout (128-element stages x 32-row groups, as the
-    library's header defines it) into row-major packed codes [rows, 3k/4] and
-    scales [rows, k/32].  Also returns the padding (codes and scale bytes of
-    rows >= rows or blocks >= k/32), which must be 0 and 127."""
+    library's header defines it) into row-major packed codes [rows, bits*k/8]
+    and scales [rows, k/32].  Also returns the padding (codes and scale bytes
+    of rows >= rows or blocks >= k/32), which must be 0 and 127."""
     stages, groups = -(-k // 128), -(-rows // 32)
-    c = np.asarray(codes_t).reshape(stages, groups, 3072)[:, :, _CHUNK_OFFSETS]  # [stage, group, row, byte]
-    c = c.transpose(1, 2, 0, 3).reshape(groups * 32, stages * 96)
+    row_bytes = 16 * bits  # packed bytes of one row of a stage
+    c = np.asarray(codes_t).reshape(stages, groups, 512 * bits)[:, :, _CHUNK_OFFSETS[bits]]
+    c = c.transpose(1, 2, 0, 3).reshape(groups * 32, stages * row_bytes)
     s = np.asarray(scales_t).reshape(stages, groups, 32, 4)       # [stage, group, row, block]
     s = s.transpose(1, 2, 0, 3).reshape(groups * 32, stages * 4)
-    pad_c = np.concatenate([c[rows:].ravel(), c[:rows, 3 * k // 4:].ravel()])
+    kb = bits * k // 8
+    pad_c = np.concatenate([c[rows:].ravel(), c[:rows, kb:].ravel()])
     pad_s = np.concatenate([s[rows:].ravel(), s[:rows, k // 32:].ravel()])
-    return c[:rows, :3 * k // 4], s[:rows, :k // 32], pad_c, pad_s
+    return c[:rows, :kb], s[:rows, :k // 32], pad_c, pad_s
 
 
 def mx_rows_view(gpu_mx):
     """Row-major (codes, scales) of a GPU MXTensor, checking tiled padding."""
     gc, gs = to_np(gpu_mx.codes), to_np(gpu_mx.scales)
     if gpu_mx.layout == "tiled":
-        gc, gs, pad_c, pad_s = tiled_to_rows(gc, gs, gpu_mx.rows, gpu_mx.k)
+        gc, gs, pad_c, pad_s = tiled_to_rows(gc, gs, gpu_mx.rows, gpu_mx.k, O.element_bits(gpu_mx.fmt))
         assert not pad_c.any(), "tiled padding codes must be 0"
         assert np.all(pad_s == 127), "tiled padding scales must be 127"
     return gc, gs
@@ -82,11 +95,11 @@ def assert_mx_equal(gpu_mx, codes_o: np.ndarray, scales_o: np.ndarray, what: str
     if rows is not None:
         gc, gs = gc[rows], gs[rows]
     k = codes_o.shape[1]
-    packed_o = O.pack(codes_o)
+    packed_o = O.pack(codes_o, gpu_mx.fmt)
     bad_s = np.argwhere(gs != scales_o)
     assert bad_s.size == 0, f"{what}: {len(bad_s)} scale bytes differ, first {bad_s[:5].tolist()}"
     if not np.array_equal(gc, packed_o):
-        cg = O.unpack(gc, k)
+        cg = O.unpack(gc, k, gpu_mx.fmt)
         bad = np.argwhere(cg != codes_o)
         raise AssertionError(f"{what}: {len(bad)} codes differ, first {bad[:5].tolist()} "
                              f"gpu {[int(cg[tuple(b)]) for b in bad[:5]]} oracle {[int(codes_o[tuple(b)]) for b in bad[:5]]}")
@@ -235,3 +248,62 @@ def check_mx_values(gpu_codes: np.ndarray, gpu_scales: np.ndarray, g32: np.ndarr
         assert bad.size == 0, f"{len(bad)} codes in scale-flipped blocks are not valid roundings"
     stats["exact"] = int((exact & same_scale).sum())
     return stats
+
+
+# ---------------------------------------------------------------- 8-bit operands: the instruction's product window
+
+MFMA_WINDOW_BITS = 13
+
+
+def mfma_window_bound(da: np.ndarray, dw: np.ndarray, block: int = 32) -> np.ndarray:
+    """Per-output bound on what the gfx950 scaled MFMA drops from C = A W^T
+    when its operands are 8-bit (E4M3 / E5M2).
+
+    Measured on the chip with constructed operands (tests/test_gpu_gemm.py
+    pins it): the instruction adds a group of products in a fixed-point
+    window whose last bit is 2**(E - 13), E the exponent of the group's
+    largest product, truncating each product toward zero onto that grid
+    (1 + 2**-13 is kept, 1 + 2**-14 and 1 - 2**-14 come back as 1, and
+    1 + 1.5 * 2**-13 as 1 + 2**-13).  Groups never span two 32-element
+    blocks, so taking E over the whole block only widens the bound: a product
+    loses less than min(|p|, 2**(E_block - 13)), and nothing when it is a
+    multiple of 2**(E_block - 13).  The 4- and 6-bit pairs the library runs
+    keep every product inside the window.
+
+    da [M, K], dw [N, K]: dequantized operands (float64).  Returns [M, N]."""
+    da = np.asarray(da, dtype=np.float64)
+    dw = np.asarray(dw, dtype=np.float64)
+    m, k = da.shape
+    n = dw.shape[0]
+    out = np.zeros((m, n))
+    for b in range(k // block):
+        p = da[:, None, b * block:(b + 1) * block] * dw[None, :, b * block:(b + 1) * block]  # exact
+        a = np.abs(p)
+        amax = a.max(axis=2, keepdims=True)
+        e = O.floor_log2(np.where(amax > 0, amax, 1.0))  # all-zero blocks lose nothing
+        unit = np.ldexp(1.0, e - MFMA_WINDOW_BITS)
+        q = a / unit  # exact: a power-of-two division
+        lossy = np.floor(q) != q
+        out += np.sum(np.where(lossy, np.minimum(a, unit), 0.0), axis=2)
+    return out
+
+
+def assert_close_window(gpu: np.ndarray, c: np.ndarray, s: np.ndarray, wb: np.ndarray, out_kind: str,
+                        what: str) -> int:
+    """fp32 / bf16 outputs against C with the 8-bit-operand tolerance: the
+    GEMM bar (1e-5 * S, or one bf16 ulp) plus the window bound.  Returns how
+    many outputs needed the window term."""
+    d = np.abs(np.asarray(gpu, dtype=np.float64) - c)
+    if out_kind == "f32":
+        base = O.GEMM_RTOL * s
+        ok = d <= base + wb
+    else:
+        u = O.ulp_bf16(c)
+        base = np.maximum(u, O.GEMM_RTOL * s + 0.5 * u)
+        ok = d <= base + wb + 0.5 * O.ulp_bf16(np.abs(c) + wb)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} outputs outside the bound; first {i}: gpu {gpu[i]!r} "
+                             f"oracle {c[i]!r} S {s[i]!r} window {wb[i]!r}")
+    return int(np.count_nonzero(d > base))

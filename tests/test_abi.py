@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mx.mx_version() == 100
+    assert mx.mx_version() == 200
     for st in range(-7, 1):
         assert mx.mx_status_string(st) and mx.mx_status_string(st) != "unknown status"
     assert mx.mx_status_string(-99) == "unknown status"
@@ -100,7 +100,9 @@ def test_rmsnorm_quantize_validation(L):
     assert rq(rows=-1) == B.MX_ERR_SHAPE
     assert rq(ld=96) == B.MX_ERR_SHAPE
     assert rq(src_type=5) == B.MX_ERR_FORMAT
-    assert rq(fmt=4) == B.MX_ERR_FORMAT
+    assert rq(fmt=7) == B.MX_ERR_FORMAT
+    assert rq(fmt=4) == B.MX_ERR_UNSUPPORTED  # the producer writes the 6-bit types
+    assert rq(fmt=0) == B.MX_ERR_UNSUPPORTED
     assert rq(x=NULL) == B.MX_ERR_NULL
     assert rq(codes=NULL) == B.MX_ERR_NULL
     assert rq(x=FAKE + 8) == B.MX_ERR_ALIGN
@@ -129,7 +131,13 @@ def g(**kw):
 def test_gemm_validation(L):
     assert g(k=100) == B.MX_ERR_SHAPE
     assert g(m=-1) == B.MX_ERR_SHAPE
-    assert g(a_fmt=4) == B.MX_ERR_FORMAT
+    assert g(a_fmt=7) == B.MX_ERR_FORMAT
+    assert g(a_fmt=4) == B.MX_ERR_UNSUPPORTED  # E2M1 x E2M3: operands of different widths
+    assert g(a_fmt=0, w_fmt=2) == B.MX_ERR_UNSUPPORTED
+    # 4- and 8-bit pairs: plain product, fp32 / bf16 output
+    assert g(a_fmt=4, w_fmt=4, epi=1) == B.MX_ERR_UNSUPPORTED
+    assert g(a_fmt=0, w_fmt=1, out_kind=2, out_scales=FAKE) == B.MX_ERR_UNSUPPORTED
+    assert g(a_fmt=4, w_fmt=4, m=0) == B.MX_OK and g(a_fmt=1, w_fmt=0, n=0) == B.MX_OK
     assert g(a_src=FAKE) == B.MX_ERR_NULL  # both activation forms
     assert g(a_codes=NULL) == B.MX_ERR_NULL  # neither
     assert g(a_scales=NULL) == B.MX_ERR_NULL
@@ -143,12 +151,13 @@ def test_gemm_validation(L):
     assert g(ldo=32) == B.MX_ERR_SHAPE
     assert g(out_kind=2, out_scales=FAKE, n=48) == B.MX_ERR_UNSUPPORTED
     assert g(out_kind=2, out_scales=NULL) == B.MX_ERR_NULL
-    assert g(out_kind=2, out_scales=FAKE, out_fmt=1) == B.MX_ERR_FORMAT
+    assert g(out_kind=2, out_scales=FAKE, out_fmt=9) == B.MX_ERR_FORMAT
+    assert g(out_kind=2, out_scales=FAKE, out_fmt=1) == B.MX_ERR_UNSUPPORTED  # MX output in the 6-bit types
     assert g(out_kind=2, out_scales=FAKE, out=FAKE + 4) == B.MX_ERR_ALIGN
     # bf16 activations need a workspace for the quantized copy
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=128) == B.MX_ERR_WORKSPACE
     need = mx.mx_gemm_workspace_size(64, 64, 128, True, 0)
-    assert need >= 2 * 3072 + 2 * 128  # 1 stage x 2 row groups, tiled
+    assert need >= 2 * 4096 + 2 * 128  # 1 stage x 2 row groups, tiled, sized for 8-bit codes
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=128, ws=FAKE, ws_bytes=need - 1) == B.MX_ERR_WORKSPACE
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=120, ws=FAKE, ws_bytes=need) == B.MX_ERR_SHAPE
     assert g(a_src=FAKE, a_codes=NULL, a_scales=NULL, lda=130, ws=FAKE, ws_bytes=need) == B.MX_ERR_ALIGN
@@ -198,6 +207,7 @@ def test_splitk_validation(L):
     assert sk(ws=NULL, **src) == B.MX_ERR_WORKSPACE
     assert sk(ws=FAKE + 16, **src) == B.MX_ERR_ALIGN
     assert sk(a_fmt=3) == B.MX_ERR_UNSUPPORTED
+    assert sk(a_fmt=0, w_fmt=0) == B.MX_ERR_UNSUPPORTED  # 6-bit types only
     assert sk(m=0) == B.MX_OK
 
 
@@ -208,8 +218,15 @@ def test_packed_bytes(L):
     assert mx.mx_packed_bytes(300, 416, "tiled", 0) == 4 * 10 * 3072
     assert mx.mx_packed_bytes(300, 416, "tiled", 1) == 4 * 10 * 128
     assert mx.mx_packed_bytes(300, 100, "tiled", 0) == 0  # invalid K
-    assert mx.lib().mx_packed_bytes(10, 64, 5, 0) == 0
-    assert mx.lib().mx_packed_bytes(10, 64, 1, 2) == 0
+    assert mx.lib().mx_packed_bytes(10, 64, 2, 5, 0) == 0  # bad layout
+    assert mx.lib().mx_packed_bytes(10, 64, 2, 1, 2) == 0  # bad selector
+    assert mx.lib().mx_packed_bytes(10, 64, 7, 1, 0) == 0  # bad format
+    # 4- and 8-bit element types: 16 / 32 code bytes per block, chunks of 2048 / 4096
+    assert mx.mx_packed_bytes(300, 416, "rows", 0, "e2m1") == 300 * 416 // 2
+    assert mx.mx_packed_bytes(300, 416, "rows", 0, "e4m3") == 300 * 416
+    assert mx.mx_packed_bytes(300, 416, "tiled", 0, "e2m1") == 4 * 10 * 2048
+    assert mx.mx_packed_bytes(300, 416, "tiled", 0, "e5m2") == 4 * 10 * 4096
+    assert mx.mx_packed_bytes(300, 416, "tiled", 1, "e4m3") == 4 * 10 * 128
 
 
 def test_workspace_sizes(L):
@@ -220,7 +237,7 @@ def test_workspace_sizes(L):
     # split-K keeps its partial sums on chip: the workspace only holds the
     # activations quantized in the call (128 stages x one 32-row group)
     sz = mx.mx_gemm_workspace_size(16, 13312, 16384, True, 16)
-    assert sz == mx.mx_gemm_workspace_size(16, 13312, 16384, True, 0) >= 128 * (3072 + 128)
+    assert sz == mx.mx_gemm_workspace_size(16, 13312, 16384, True, 0) >= 128 * (4096 + 128)
     assert mx.mx_gemm_workspace_size(16, 13312, 16384, False, 16) == 0
 
 

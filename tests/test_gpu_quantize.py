@@ -11,7 +11,7 @@ from tests.parity import assert_mx_equal, say
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["e2m3", "e3m2"]
+FMTS = ["e2m3", "e3m2", "e2m1", "e4m3", "e5m2"]
 LAYOUTS = ["tiled", "rows"]
 
 
@@ -80,6 +80,36 @@ def test_f32_source_full_mantissa(fmt, layout):
     torch.cuda.synchronize()
     c, s = O.quantize(x.astype(np.float64), fmt)
     assert_mx_equal(g, c, s, "f32 source")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_exact_ties_and_neighbours(fmt, layout):
+    """Every midpoint between neighbouring magnitudes of the element type (the
+    round-half-to-even cases), and the fp32 values just below and above it,
+    in blocks whose scale an anchor at the largest magnitude fixes to 2**e,
+    for scales across the E8M0 range; both signs; fp32 sources."""
+    mags = O.magnitudes(fmt)
+    mids = (mags[:-1] + mags[1:]) / 2
+    rng = np.random.default_rng(len(mids))
+    vals = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(np.inf)), mags]).astype(np.float32)
+    vals = np.concatenate([vals, -vals])
+    per = 31
+    nblk = -(-len(vals) // per)
+    vals = np.concatenate([vals, np.zeros(nblk * per - len(vals), np.float32)]).reshape(nblk, per)
+    rows = []
+    for e in (-120, -40, -3, 0, 5, 60, 100):
+        blk = np.concatenate([np.full((nblk, 1), mags[-1], np.float32), vals], axis=1)
+        rows.append(np.ldexp(blk.astype(np.float64), e).astype(np.float32))
+    x = np.concatenate(rows)
+    x = np.ascontiguousarray(x[:, rng.permutation(32)])  # the anchor anywhere in the block
+    x = x.reshape(-1, 128) if x.shape[0] % 4 == 0 else x
+    say(f"quantize ties {x.shape} {fmt} {layout}")
+    g = mx.mx_quantize(torch.from_numpy(x).cuda(), fmt, layout)
+    torch.cuda.synchronize()
+    c, s = O.quantize(x.astype(np.float64), fmt)
+    assert_mx_equal(g, c, s, "ties")
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -18,8 +18,8 @@ import torch
 import microscaled_precision_gemm_amd as mx
 from microscaled_precision_gemm_amd import synthetic as syn
 from oracle import mx_oracle as O
-from tests.parity import (assert_bf16_close, assert_fp32_close, bf16_tensor_to_f64, check_mx_epilogue,
-                          mx_rows_view, say, to_np)
+from tests.parity import (assert_bf16_close, assert_close_window, assert_fp32_close, bf16_tensor_to_f64,
+                          check_mx_epilogue, mfma_window_bound, mx_rows_view, say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +80,30 @@ def test_full_size_bf16_out(name, request):
     got = bf16_tensor_to_f64(y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)])
     c, s = O.gemm_ref(_deq_rows(a, rows, "e2m3"), _deq_rows(wt, cols, w.w_fmt))
     assert_bf16_close(got, c, s, f"{name} sampled")
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3"])
+def test_operand_formats_full_size(fmt):
+    """The MXFP4 / MXFP8 GEMM bench.py times: fc1's shape 20480 x 3072 x
+    12288, both operands quantized to `fmt`, bf16 out; sampled outputs
+    against the oracle (FP8 with the instruction's product-window bound)."""
+    w = syn.WORKLOADS["fc1"]
+    a, wt = syn.make_a(w), syn.make_w(w)
+    rng = np.random.default_rng([79, w.index, len(fmt)])
+    rows, cols = _pick(w.m, ROW_SAMPLE, rng), _pick(w.n, COL_SAMPLE, rng)
+    say(f"workload fc1-shaped {w.m}x{w.k}x{w.n} {fmt} x {fmt} bf16 out")
+    dev = torch.device("cuda:0")
+    aq, wq = mx.mx_quantize(a.to(dev), fmt), mx.mx_quantize(wt.to(dev), fmt)
+    y = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
+    mx.mx_gemm(aq, wq, out_kind="bf16", out=y)
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)])
+    da, dw = _deq_rows(a, rows, fmt), _deq_rows(wt, cols, fmt)
+    c, s = O.gemm_ref(da, dw)
+    if O.element_bits(fmt) == 8:
+        assert_close_window(got, c, s, mfma_window_bound(da, dw), "bf16", f"{fmt} sampled")
+    else:
+        assert_bf16_close(got, c, s, f"{fmt} sampled")
 
 
 def test_fc1_full_size_gelu_mx():

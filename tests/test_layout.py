@@ -52,3 +52,44 @@ def test_tiled_round_trip_with_padding():
     assert np.array_equal(c, packed) and np.array_equal(sc, scales)
     assert not pad_c.any() and np.all(pad_s == 127)
     assert np.array_equal(O.unpack(c, k), codes)
+
+
+def test_chunk_offsets_fp4_fp8_planes():
+    """4- and 8-bit chunks: a permutation of 512 * bits bytes, each block of a
+    row split into 16-byte runs in planes whose rows are 16 bytes apart."""
+    for bits in (4, 8):
+        off = tiled_chunk_offsets(bits)
+        eb = 4 * bits
+        assert off.shape == (32, 4 * eb)
+        assert np.array_equal(np.sort(off.ravel()), np.arange(512 * bits))
+        for j in (0, 9, 31):
+            for q in range(4):
+                for t in range(0, eb, 16):
+                    run = off[j, eb * q + t:eb * q + t + 16]
+                    assert np.array_equal(run, run[0] + np.arange(16))
+                    assert run[0] % 512 == j * 16
+        if bits == 8:  # block q's bytes 0..15 in half 0, 16..31 in half 1, plane 2 (q % 2) + q // 2
+            for q in range(4):
+                assert off[5, 32 * q] == (2 * (q % 2) + q // 2) * 512 + 5 * 16
+                assert off[5, 32 * q + 16] == 2048 + (2 * (q % 2) + q // 2) * 512 + 5 * 16
+
+
+def test_tiled_round_trip_fp4_fp8():
+    rng = np.random.default_rng(1)
+    rows, k = 45, 288
+    for fmt in ("e2m1", "e4m3"):
+        bits = O.element_bits(fmt)
+        codes = rng.integers(0, 1 << bits, size=(rows, k))
+        packed = O.pack(codes, fmt)
+        stages, groups, rb = 3, 2, 16 * bits
+        ct = np.zeros((stages, groups, 512 * bits), dtype=np.uint8)
+        st = np.full((stages, groups, 32, 4), 127, dtype=np.uint8)
+        off = tiled_chunk_offsets(bits)
+        for r in range(rows):
+            g, j = divmod(r, 32)
+            for s_ in range(stages):
+                sl = packed[r, rb * s_:rb * s_ + rb]
+                ct[s_, g, off[j, :len(sl)]] = sl
+        c, sc, pad_c, pad_s = tiled_to_rows(ct.ravel(), st.ravel(), rows, k, bits)
+        assert np.array_equal(c, packed) and not pad_c.any()
+        assert np.array_equal(O.unpack(c, k, fmt), codes)
