@@ -193,9 +193,14 @@ __global__ __launch_bounds__(kTWaves * 64) void quantize_tiled_kernel(const uint
   using L = TLayout<F32>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kTWaves * 32 * L::kRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunk = blockIdx.x * kTWaves + wave;
-  if (chunk >= nchunks) return;  // wave-level only: no workgroup barrier below
-  const int stage = chunk / groups, grp = chunk - stage * groups;
+  // Waves walk the chunks group by group (all stages of rows 32g .. 32g+31,
+  // then the next group), so the waves in flight read long runs of each row
+  // rather than one 256-byte piece of every row.
+  const int work = blockIdx.x * kTWaves + wave;
+  if (work >= nchunks) return;  // wave-level only: no workgroup barrier below
+  const int stages = nchunks / groups;
+  const int grp = work / stages, stage = work - grp * stages;
+  const int chunk = stage * groups + grp;
   uint8_t* in = lds + wave * 32 * L::kRow;
   const int kblocks = k / 32;
 

@@ -56,6 +56,36 @@ def test_producer_small(src, fmt, rows, d, per):
     _check(hq, xt, gamma, shift, scale, per, 1e-6, fmt)
 
 
+@pytest.mark.parametrize("src,rows,d", [("f32", 40, 2048), ("bf16", 64, 4096), ("bf16", 40, 5120),
+                                         ("f32", 40, 8192)])
+def test_producer_row_lengths(src, rows, d):
+    """Longer rows than the workloads' (up to 8192 fp32 elements, 32 KB per
+    row), bf16 and fp32 sources, a ragged row count."""
+    xt, gamma, shift, scale = _inputs(rows, d, 2, d, src)
+    say(f"producer {src} {rows}x{d}")
+    hq = mx.mx_rmsnorm_quantize(xt.cuda(), _t(gamma), _t(shift), _t(scale), 32, 1e-6, "e2m3")
+    torch.cuda.synchronize()
+    _check(hq, xt, gamma, shift, scale, 32, 1e-6, "e2m3")
+
+
+def test_producer_unaligned_parameter_vectors():
+    """gamma / shift / scale only 4-byte aligned (views one float into a buffer)."""
+    rows, d = 96, 512
+    xt, gamma, shift, scale = _inputs(rows, d, 3, 11, "bf16")
+    gbuf = torch.zeros(d + 1, dtype=torch.float32)
+    gbuf[1:] = torch.from_numpy(gamma)
+    sbuf = torch.zeros(3 * d + 1, dtype=torch.float32)
+    sbuf[1:] = torch.from_numpy(scale).reshape(-1)
+    hbuf = torch.zeros(3 * d + 1, dtype=torch.float32)
+    hbuf[1:] = torch.from_numpy(shift).reshape(-1)
+    g_, s_, h_ = gbuf.cuda()[1:], sbuf.cuda()[1:].view(3, d), hbuf.cuda()[1:].view(3, d)
+    assert g_.data_ptr() % 16 == 4
+    say("producer unaligned parameters")
+    hq = mx.mx_rmsnorm_quantize(xt.cuda(), g_, h_, s_, 32, 1e-6, "e2m3")
+    torch.cuda.synchronize()
+    _check(hq, xt, gamma, shift, scale, 32, 1e-6, "e2m3")
+
+
 @pytest.mark.parametrize("with_gamma", [True, False])
 def test_producer_without_modulation(with_gamma):
     """No shift / scale: the plain RMSNorm (with or without a gain) quantized."""
