@@ -331,9 +331,12 @@ def cpu_baseline(target_s: float = 15.0):
         O.gemm_ref(O.dequantize(codes, scales, "e2m3"), w2)
         return time.perf_counter() - t0
 
+    # size the sample from two probes (the first, on 32 rows, is dominated by
+    # fixed costs), then run it
     rows = 32
-    t = run(rows)
-    rows = int(min(fc1.m, max(32, rows * target_s / max(t, 1e-3))) // 32 * 32)
+    for frac in (0.2, 1.0):
+        t = run(rows)
+        rows = int(min(fc1.m, max(32, rows * frac * target_s / max(t, 1e-3))) // 32 * 32)
     t = run(rows)
     flops = 2 * 2.0 * rows * d * hdim
     threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
