@@ -7,19 +7,23 @@
 // stream of packed weights from HBM (0.78 bytes per weight), so the kernel is
 // built for memory-level parallelism, not for the matrix cores:
 //
-//  * One workgroup per 32-feature group of the weights, 4 waves.  Wave w
-//    streams the K-chunks w*spw .. w*spw+spw-1 (spw = ceil(S/4)), stage after
-//    stage, with kWindow stages of loads in flight across chunk boundaries.
-//    416 groups x 4 waves fit the GPU in one round.
+//  * One workgroup per pair of 32-feature weight groups, 8 waves.  Wave w
+//    streams the K-chunks w*spw .. w*spw+spw-1 (spw = ceil(S/8)) of both
+//    groups, stage after stage, with kWindow stages of loads in flight across
+//    chunk boundaries.  Each stage's activation operand is loaded once and
+//    used by the MFMAs of both groups: the activations are the same few
+//    hundred KB for every workgroup and come from L2, so sharing them halves
+//    those load instructions per weight byte (they measured a fifth of the
+//    kernel's time with one group per wave).  208 workgroups of 8 waves for
+//    N = 13312 fit the GPU in one round.
 //  * Both operands are in the tiled MX layout.  Per 128-element stage each
 //    lane loads its row's entries of the four planes of half h (16 + 8 + 8 +
 //    16 bytes), so every load instruction reads contiguous runs of 512 or 256
-//    bytes.  The weights are read once (non-temporal); the activations (a few
-//    hundred KB, the same for every group) come from L2.
+//    bytes.  The weights are read once (non-temporal).
 //  * V_MFMA_SCALE_F32_32X32X64_F8F6F4 with the weights as the A operand and
 //    the tokens as the B operand; token rows 16..31 are layout padding (zero
 //    codes), so M = 8 or 16 costs no extra weight bytes and no branches.
-//  * When a chunk ends, its fp32 partial goes to LDS; after one barrier the
+//  * When a chunk ends, its fp32 partials go to LDS; after one barrier the
 //    workgroup adds the S partials in the fixed order 0 .. S-1 (deterministic)
 //    and rounds once into the output.  No partials touch HBM and no second
 //    kernel is launched.
@@ -32,9 +36,10 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kSkWaves = 4;
+constexpr int kSkWaves = 8;
 constexpr int kSkThreads = 64 * kSkWaves;
-constexpr int kWindow = 5;  // stages of loads in flight per wave (two waves per SIMD fit)
+constexpr int kSkGroups = 2;  // 32-feature weight groups per workgroup (and per wave)
+constexpr int kWindow = 4;    // stages of loads in flight per wave (two waves per SIMD fit)
 
 // One operand pair of a stage as loaded: the lane's entries of planes A, L,
 // H and B of half h (block 2h = A + L, block 2h+1 = H + B).  The window keeps
@@ -45,8 +50,8 @@ struct Pieces {
 };
 
 struct StageOps {
-  Pieces w, x;
-  int ws, xs;  // scale pairs (bytes 2h, 2h+1 of the lane's row)
+  Pieces w0, w1, x;  // the two weight groups' pieces and the activations'
+  int ws0, ws1, xs;  // scale pairs (bytes 2h, 2h+1 of the lane's row)
 };
 
 template <bool NT>
@@ -77,27 +82,28 @@ __device__ __forceinline__ v8i op1(const Pieces& p) {
   return v8i{(int)p.hh[0], (int)p.hh[1], (int)p.b[0], (int)p.b[1], (int)p.b[2], (int)p.b[3], 0, 0};
 }
 
-// grid: one workgroup per 32-feature group.
+// grid: one workgroup per pair of 32-feature groups.
 template <int WF, int XF, int OUT>
 __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) {
-  // partial sums [split][token][feature], tokens 0..15
-  __shared__ __attribute__((aligned(16))) float part[kMaxSplits][16][32];
+  // partial sums [split][token][feature], tokens 0..15, features of both groups
+  __shared__ __attribute__((aligned(16))) float part[kMaxSplits][16][32 * kSkGroups];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, j = lane & 31;
-  const int grp = blockIdx.x;
-  const int sps = g.K / kTileStageK / g.splits;       // stages per chunk
+  const int grp = blockIdx.x * kSkGroups;                 // first of the workgroup's groups
+  const bool has1 = grp + 1 < g.gw;                      // the second group exists
+  const int sps = g.K / kTileStageK / g.splits;          // stages per chunk
   const int spw = (g.splits + kSkWaves - 1) / kSkWaves;  // chunks per wave
   const int c0 = wave * spw;
   const int c1 = min(g.splits, c0 + spw);
-  const int nst = c1 > c0 ? (c1 - c0) * sps : 0;      // stages this wave streams
-  const int nc = c1 > c0 ? c1 - c0 : 0;               // chunks of this wave
+  const int nst = c1 > c0 ? (c1 - c0) * sps : 0;         // stages this wave streams
+  const int nc = c1 > c0 ? c1 - c0 : 0;                  // chunks of this wave
   // Every workgroup walks its chunks in a rotated order and each chunk's
   // stages from a rotated start, so that the workgroups, which all read the
   // same activations, spread their requests over many lines instead of
-  // hammering the same few at the same time.  The order is fixed per group
-  // (deterministic); the chunks' partials still meet in order 0 .. S-1.
-  const int r0 = sps > 0 ? grp % sps : 0;
-  const int q0 = nc > 0 ? (grp / max(sps, 1)) % nc : 0;
+  // hammering the same few at the same time.  The order is fixed per pair of
+  // groups (deterministic); the chunks' partials still meet in order 0 .. S-1.
+  const int r0 = sps > 0 ? blockIdx.x % sps : 0;
+  const int q0 = nc > 0 ? (blockIdx.x / max(sps, 1)) % nc : 0;
   const int lane_off = h * kHalfBytes;
   const int scale_off = j * 4 + 2 * h;
   const uint8_t* wc = g.w_codes + (int64_t)grp * kChunkCodes + lane_off;
@@ -122,8 +128,16 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
   };
   auto load = [&](int st) {
     StageOps o;
-    o.w = load_pieces<true>(wc + st * w_step, j);
-    o.ws = *reinterpret_cast<const uint16_t*>(ws + st * ws_step);
+    o.w0 = load_pieces<true>(wc + st * w_step, j);
+    o.ws0 = *reinterpret_cast<const uint16_t*>(ws + st * ws_step);
+    if (has1) {  // the next group's chunk follows in memory
+      o.w1 = load_pieces<true>(wc + st * w_step + kChunkCodes, j);
+      o.ws1 = *reinterpret_cast<const uint16_t*>(ws + st * ws_step + kChunkScales);
+    } else {
+      o.w1.a = o.w1.b = u32x4{0u, 0u, 0u, 0u};
+      o.w1.l = o.w1.hh = u32x2{0u, 0u};
+      o.ws1 = 0x7f7f;
+    }
     if (token) {
       o.x = load_pieces<false>(xc + (int64_t)st * kChunkCodes, j);
       o.xs = *reinterpret_cast<const uint16_t*>(xs + (int64_t)st * kChunkScales);
@@ -135,9 +149,9 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
     return o;
   };
 
-  v16f acc;
+  v16f acc0, acc1;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
   StageOps win[kWindow];
 #pragma unroll
   for (int i = 0; i < kWindow; ++i)
@@ -149,20 +163,26 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
       if (i + k < nst) {
         const StageOps o = win[k];
         if (i + k + kWindow < nst) win[k] = load(next_stage());
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op0(o.w), op0(o.x), acc, WF, XF, 0, o.ws, 0, o.xs);
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op1(o.w), op1(o.x), acc, WF, XF, 1, o.ws, 1, o.xs);
+        const v8i x0 = op0(o.x), x1 = op1(o.x);
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op0(o.w0), x0, acc0, WF, XF, 0, o.ws0, 0, o.xs);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op0(o.w1), x0, acc1, WF, XF, 0, o.ws1, 0, o.xs);
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op1(o.w0), x1, acc0, WF, XF, 1, o.ws0, 1, o.xs);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op1(o.w1), x1, acc1, WF, XF, 1, o.ws1, 1, o.xs);
         if (--left == 0) {
           int chunk = cc + q0;
           chunk = c0 + (chunk >= nc ? chunk - nc : chunk);
           // lane (h, j) holds, for token j, features 8a + 4h + b in register 4a + b
           if (token) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a) {
               *reinterpret_cast<v4f*>(&part[chunk][j][8 * a + 4 * h]) =
-                  v4f{acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+                  v4f{acc0[4 * a], acc0[4 * a + 1], acc0[4 * a + 2], acc0[4 * a + 3]};
+              *reinterpret_cast<v4f*>(&part[chunk][j][32 + 8 * a + 4 * h]) =
+                  v4f{acc1[4 * a], acc1[4 * a + 1], acc1[4 * a + 2], acc1[4 * a + 3]};
+            }
           }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+          for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
           ++cc;
           left = sps;
         }
@@ -173,8 +193,8 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
 
   // out[m, n] = round(sum_{s=0}^{S-1} part[s][m][n - 32 grp]), in that order
   const bool empty = sps == 0;  // K == 0
-  for (int t = threadIdx.x; t < g.M * 32; t += kSkThreads) {
-    const int m = t >> 5, f = t & 31, n = grp * 32 + f;
+  for (int t = threadIdx.x; t < g.M * 32 * kSkGroups; t += kSkThreads) {
+    const int m = t / (32 * kSkGroups), f = t % (32 * kSkGroups), n = grp * 32 + f;
     float sum = 0.0f;
     if (!empty)
       for (int s = 0; s < g.splits; ++s) sum += part[s][m][f];
@@ -191,7 +211,7 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
 
 template <int OUT>
 hipError_t launch_out(const SplitKArgs& a, int x_fmt, int w_fmt, hipStream_t stream) {
-  const dim3 grid((unsigned)a.gw), block(kSkThreads);
+  const dim3 grid((unsigned)ceil_div(a.gw, kSkGroups)), block(kSkThreads);
   if (w_fmt == kFmtE2M3 && x_fmt == kFmtE2M3)
     hipLaunchKernelGGL((splitk_kernel<kFmtE2M3, kFmtE2M3, OUT>), grid, block, 0, stream, a);
   else if (w_fmt == kFmtE3M2 && x_fmt == kFmtE2M3)
