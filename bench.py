@@ -40,7 +40,14 @@ PEAK_HBM_GBS = 8000.0
 
 # rocprofv3 names of the two GEMM instantiations <W fmt, A fmt, out kind, epilogue, out fmt>
 # (E2M3 x E2M3; fc1: MX out + GELU, fc2: bf16 out, no epilogue)
-KERNEL_NAMES = {"fc1": "gemm_kernel<2, 2, 2, 1, 2>", "fc2": "gemm_kernel<2, 2, 1, 0, 2>"}
+# demangled GEMM kernel names: gemm_kernel<weights, activations, output kind, epilogue,
+# output format, tile width>; fc1 = E2M3 x E2M3 -> GELU-tanh -> MX E2M3, fc2 = -> bf16
+KERNEL_PREFIX = {"fc1": "gemm_kernel<2, 2, 2, 1, 2", "fc2": "gemm_kernel<2, 2, 1, 0, 2"}
+
+
+def kernel_name(gemm: str, config) -> str:
+    tile_n = 256 if config is None else int(config.tile_n)
+    return f"{KERNEL_PREFIX[gemm]}, {tile_n}>"
 # the sources the GEMM kernel is built from: measured HBM traffic is only reported
 # while they are unchanged since the counters were taken
 GEMM_SOURCES = ["gemm_kernel.h", "internal.h", "mx_device.h", "gemm_we2m3_e2m3.hip"]
@@ -65,7 +72,7 @@ def settle(fn, seconds: float = SETTLE_S):
         torch.cuda.synchronize()
 
 
-def bench_mlp(steps: int, warmup: int, tune: bool = True):
+def bench_mlp(steps: int, warmup: int, tune: bool = True, table_path: str | None = None):
     fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
     m, d, hdim = fc1.m, fc1.k, fc1.n
     dev = torch.device("cuda:0")
@@ -75,17 +82,27 @@ def bench_mlp(steps: int, warmup: int, tune: bool = True):
     xq = mx.MXTensor.empty(m, d, "e2m3", "tiled", dev)
     h = mx.MXTensor.empty(m, hdim, "e2m3", "tiled", dev)
     y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
-    # per-shape tile order from the tuning table (tuned here, untimed, on these operands)
-    table = tuning.TuningTable()
+    # per-shape tile order and width from the tuning table: tuned here, untimed, on
+    # these operands, or read from `table_path` when it holds both shapes (tuned
+    # there and saved, when it does not)
+    table = tuning.TuningTable(table_path)
+    cfg1 = table.lookup(m, hdim, d, epilogue="gelu_tanh", out_kind="mx")
+    cfg2 = table.lookup(m, d, hdim, epilogue="none", out_kind="bf16")
     tuned = {}
-    if tune:
+    if tune and (cfg1 is None or cfg2 is None):
         mx.mx_quantize(x, "e2m3", "tiled", out=xq)
         tuned["fc1"] = tuning.tune_gemm(table, xq, w1, out_kind="mx", epilogue="gelu_tanh")
         h_t = mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh")
         tuned["fc2"] = tuning.tune_gemm(table, h_t, w2, out_kind="bf16")
         del h_t
-    cfg1 = table.lookup(m, hdim, d, epilogue="gelu_tanh", out_kind="mx")
-    cfg2 = table.lookup(m, d, hdim, epilogue="none", out_kind="bf16")
+        if table_path is not None:
+            table.save()
+        cfg1 = table.lookup(m, hdim, d, epilogue="gelu_tanh", out_kind="mx")
+        cfg2 = table.lookup(m, d, hdim, epilogue="none", out_kind="bf16")
+    elif tune:
+        key1 = tuning.gemm_key(m, hdim, d, "e2m3", "e2m3", "gelu_tanh", "mx", "e2m3", tuning.device_name())
+        key2 = tuning.gemm_key(m, d, hdim, "e2m3", "e2m3", "none", "bf16", "e2m3", tuning.device_name())
+        tuned = {"fc1": table.entries[key1], "fc2": table.entries[key2]}
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -129,6 +146,7 @@ def bench_mlp(steps: int, warmup: int, tune: bool = True):
         "fc1_bytes": m * d * 3 // 4 + m * d // 32 + hdim * d * 3 // 4 + hdim * d // 32 + m * hdim * 3 // 4 + m * hdim // 32,
         "fc2_bytes": m * hdim * 3 // 4 + m * hdim // 32 + d * hdim * 3 // 4 + d * hdim // 32 + m * d * 2,
         "tuning": {k: {"config": v["config"], "us": v["us"], "default_us": v["default_us"]} for k, v in tuned.items()},
+        "kernels": {"fc1": kernel_name("fc1", cfg1), "fc2": kernel_name("fc2", cfg2)},
     }
 
 
@@ -281,19 +299,21 @@ def gemm_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` ("fc1" / "fc2") from the committed
+def measured_traffic(gemm: str, kernel: str):
+    """HBM bytes per launch of `gemm` ("fc1" / "fc2") from the committed
     rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same
     counter's reading for a copy of known size), or None when the summary is
-    missing or the GEMM sources changed since it was taken."""
+    missing, was taken of another kernel (tile width) than `kernel`, or the
+    GEMM sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             text = f.read()
     except OSError:
         return None
     m = re.search(r"^kernel_sources_sha256: ([0-9a-f]{64})$", text, re.M)
-    t = re.search(rf"^{kernel}_traffic_bytes_per_launch: (\d+)$", text, re.M)
-    if not m or not t or m.group(1) != gemm_sources_sha256():
+    t = re.search(rf"^{gemm}_traffic_bytes_per_launch: (\d+)$", text, re.M)
+    k = re.search(rf"^{gemm}_kernel: (.+)$", text, re.M)
+    if not m or not t or not k or m.group(1) != gemm_sources_sha256() or k.group(1).strip() != kernel:
         return None
     return int(t.group(1))
 
@@ -352,7 +372,9 @@ def main():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skinny-iters", type=int, default=100)
-    p.add_argument("--no-tune", action="store_true", help="use the default tile order instead of tuning it")
+    p.add_argument("--no-tune", action="store_true", help="use the default tile order and width instead of tuning")
+    p.add_argument("--tuning-table", default=None,
+                   help="JSON tuning table: read the MLP's configurations from it, or tune and save them there")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = p.parse_args()
@@ -363,7 +385,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
 
-    r = bench_mlp(args.steps, args.warmup, tune=not args.no_tune)
+    r = bench_mlp(args.steps, args.warmup, tune=not args.no_tune, table_path=args.tuning_table)
     ms_step = r["wall_ms_per_step"]
     value = r["flops_per_step"] / ms_step / 1e9  # TFLOP/s
     # dominant kernel: the slower of the two GEMMs, timed with events on its own stream
@@ -390,9 +412,9 @@ def main():
         "config": {"workload": "DiT MLP forward: quantize x, fc1 20480x3072x12288 (GELU-tanh -> E2M3), "
                                "fc2 20480x12288x3072 (bf16 out)",
                    "tokens": 20480, "d_model": 3072, "d_hidden": 12288, "frac_of_mxfp6_peak": round(value / PEAK_MXFP6_TFLOPS, 4)},
-        "roofline": {"bound": "mfma", "kernel": f"{KERNEL_NAMES[dom]} ({dom})", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": f"{r['kernels'][dom]} ({dom})", "achieved": round(achieved, 1),
                      "peak": PEAK_MXFP6_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MXFP6_TFLOPS, 4),
-                     "traffic": measured_traffic(dom), "traffic_unit": "bytes per launch",
+                     "traffic": measured_traffic(dom, r["kernels"][dom]), "traffic_unit": "bytes per launch",
                      "algorithmic_bytes": r[f"{dom}_bytes"], "avg_launch_ms": round(dom_ms, 4)},
         "kernels_ms": {"quantize": round(r["quantize_ms"], 4), "fc1": round(r["fc1_ms"], 4), "fc2": round(r["fc2_ms"], 4),
                        "fc1_tflops": round(r["flops_per_gemm"] / r["fc1_ms"] / 1e9, 1),

@@ -249,10 +249,11 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
             int32_t out_fmt, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Launch configuration of mx_gemm: the order in which the 256 x 256 output
- * tiles are handed to workgroups.  It changes the speed (which operand stages
- * the workgroups in flight share in each XCD's L2), never the result: every
- * configuration computes each output with the same arithmetic.  The Hedra
+ * Launch configuration of mx_gemm: the output tile width and the order in
+ * which the tiles are handed to workgroups.  It changes the speed (which
+ * operand stages the workgroups in flight share in each XCD's L2, how many
+ * workgroups share a CU), never the result: every configuration computes each
+ * output with the same arithmetic (the same MFMA sequence over K per output).  The Hedra
  * post (section "We tuned before writing custom kernels") keeps per-shape
  * choices found by timing candidates on real data; a table of such choices
  * (microscaled_precision_gemm_amd/tuning.py) passes them here.
@@ -261,6 +262,11 @@ typedef struct {
   int32_t group_m;   /* m-tiles per group of the tile walk, 1 .. 16 (default 4)             */
   int32_t xcd_remap; /* 1: each XCD walks a contiguous range of the grouped order (default);
                         0: tiles in plain grouped order, dealt round-robin to the XCDs        */
+  int32_t tile_n;    /* output features per tile: 256 (default; 4 waves of 128 x 128, one
+                        workgroup per CU) or 128 (4 waves of 128 x 64 and a two-slot LDS
+                        ring, two workgroups per CU, so one's prologue, waits and epilogue
+                        overlap the other's matrix work; the 6-bit format pairs with
+                        MX_EPI_NONE or MX_EPI_GELU_TANH only, else MX_ERR_UNSUPPORTED)      */
 } mx_gemm_config;
 
 /* mx_gemm_default_config - fill *config with the defaults mx_gemm uses. */

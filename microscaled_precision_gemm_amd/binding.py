@@ -55,12 +55,17 @@ EXPORTED = ("mx_quantize", "mx_rmsnorm_quantize", "mx_packed_bytes", "mx_gemm", 
 
 
 class MXGemmConfig(ctypes.Structure):
-    """mx_gemm_config: the tile order of mx_gemm (speed only, never the result)."""
+    """mx_gemm_config: the tile order and tile width of mx_gemm (speed only,
+    never the result).  Built from (group_m, xcd_remap[, tile_n]); tile_n
+    defaults to 256."""
 
-    _fields_ = [("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32)]
+    _fields_ = [("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("tile_n", ctypes.c_int32)]
 
-    def key(self) -> tuple[int, int]:
-        return (int(self.group_m), int(self.xcd_remap))
+    def __init__(self, group_m: int = 4, xcd_remap: int = 1, tile_n: int = 256):
+        super().__init__(group_m, xcd_remap, tile_n)
+
+    def key(self) -> tuple[int, int, int]:
+        return (int(self.group_m), int(self.xcd_remap), int(self.tile_n))
 
 
 class MXError(RuntimeError):
@@ -266,12 +271,13 @@ def mx_gemm_default_config() -> MXGemmConfig:
 
 def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epilogue: str = "none",
             out_fmt: str = "e2m3", a_fmt: str = "e2m3", out: torch.Tensor | MXTensor | None = None,
-            workspace: torch.Tensor | None = None, config: MXGemmConfig | tuple[int, int] | None = None):
+            workspace: torch.Tensor | None = None, config: MXGemmConfig | tuple[int, ...] | None = None):
     """C = A W^T.  ``a`` is a bf16/fp32 tensor (quantized to ``a_fmt`` inside the
     call) or an MXTensor.  Returns a [m, n_out] tensor, or an MXTensor for
     out_kind="mx"; n_out = n, or n / 2 for epilogue="swiglu" (``w`` then holds
     stacked gate/up rows, see include/mxgemm.h).  ``config``: the tile order
-    (an MXGemmConfig or (group_m, xcd_remap)); None = the library default."""
+    and width (an MXGemmConfig or (group_m, xcd_remap[, tile_n])); None = the
+    library default."""
     _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
     n_out = n // 2 if epilogue == "swiglu" else n

@@ -108,7 +108,7 @@ hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, in
 
 extern "C" {
 
-int mx_version(void) { return 200; }
+int mx_version(void) { return 300; }
 
 const char* mx_status_string(int status) {
   switch (status) {
@@ -183,6 +183,7 @@ void mx_gemm_default_config(mx_gemm_config* config) {
   if (!config) return;
   config->group_m = 4;
   config->xcd_remap = 1;
+  config->tile_n = 256;
 }
 
 int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
@@ -202,7 +203,8 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   mx_gemm_config cfg;
   mx_gemm_default_config(&cfg);
   if (config) {
-    if (config->group_m < 1 || config->group_m > 16 || (config->xcd_remap != 0 && config->xcd_remap != 1))
+    if (config->group_m < 1 || config->group_m > 16 || (config->xcd_remap != 0 && config->xcd_remap != 1) ||
+        (config->tile_n != 256 && config->tile_n != 128))
       return MX_ERR_FORMAT;
     cfg = *config;
   }
@@ -214,6 +216,8 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   if (epilogue == MX_EPI_SWIGLU && n % 128 != 0) return MX_ERR_UNSUPPORTED;
   // the 4- and 8-bit operand formats have the plain product with fp32 / bf16 output
   if (!fp6_fmt(w_fmt) && (epilogue != MX_EPI_NONE || out_kind == MX_OUT_MX)) return MX_ERR_UNSUPPORTED;
+  // 128-feature tiles: the 6-bit pairs without the SwiGLU pairing
+  if (cfg.tile_n == 128 && (!fp6_fmt(w_fmt) || epilogue == MX_EPI_SWIGLU)) return MX_ERR_UNSUPPORTED;
   const int64_t n_out = epilogue == MX_EPI_SWIGLU ? n / 2 : n;
   if (!out) return MX_ERR_NULL;
   if (out_kind == MX_OUT_MX) {
@@ -254,7 +258,8 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   g.N = (int32_t)n;
   g.K = (int32_t)k;
   g.tiles_m = (int32_t)ceil_div(m, kTileM);
-  g.tiles_n = (int32_t)ceil_div(n, kTileN);
+  g.tiles_n = (int32_t)ceil_div(n, cfg.tile_n);
+  g.tile_n = cfg.tile_n;
   g.gx = (int32_t)ceil_div(m, kTileGroupRows);
   g.gw = (int32_t)ceil_div(n, kTileGroupRows);
   const int64_t esize = out_kind == MX_OUT_F32 ? 4 : 2;

@@ -52,9 +52,8 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
-constexpr int kGroupsPerTile = kTileM / kTileGroupRows;            // 8
-constexpr int kStageScales = kGroupsPerTile * kChunkScales;         // 1 KB per operand
-static_assert(kTileM == kTileN, "the loader assumes square tiles");
+constexpr int kGroupsPerTile = kTileM / kTileGroupRows;            // 8 activation groups per tile
+constexpr int kStageScales = kGroupsPerTile * kChunkScales;         // 1 KB of activation scales
 static_assert(kStageScales == 4 * 64 * 4, "one 4-byte copy per lane per wave covers a stage's scales");
 
 // LDS ring and copy schedule for weight format WF and activation format XF.
@@ -67,42 +66,64 @@ static_assert(kStageScales == 4 * 64 * 4, "one 4-byte copy per lane per wave cov
 // ks+2's copies all go out in phase 1 of stage ks (the slot it refills is
 // free from the middle of stage ks on, and the copies have a whole stage of
 // matrix work to land).
-template <int WF, int XF>
+//
+// TN is the tile's width in output features: 256 (4 waves of 128 x 128, 256
+// accumulator registers each, one workgroup per CU) or 128 (4 waves of
+// 128 x 64, 128 accumulators, and a two-slot ring of 37.5 KB slots, so that
+// two workgroups share a CU and one's waits, prologue and epilogue overlap
+// the other's matrix work).
+template <int WF, int XF, int TN = 256>
 struct Ring {
   static constexpr int kBW = fmt_bits(WF), kBX = fmt_bits(XF);
   static constexpr int kChunkW = chunk_codes(kBW), kChunkX = chunk_codes(kBX);
   static constexpr int kHalfW = half_codes(kBW), kHalfX = half_codes(kBX);
-  static constexpr int kStageW = kGroupsPerTile * kChunkW, kStageX = kGroupsPerTile * kChunkX;
+  static constexpr int kGroupsW = TN / kTileGroupRows;                // weight groups per tile
+  static constexpr int kFW = TN / 64;                                 // weight fragments per wave
+  static constexpr int kMfmaPhase = 4 * kFW;                          // MFMAs per sub-step
+  static constexpr int kStageW = kGroupsW * kChunkW, kStageX = kGroupsPerTile * kChunkX;
+  static constexpr int kStageScalesW = kGroupsW * kChunkScales;
   static constexpr int kOffX = 0;
   static constexpr int kOffW = kStageX;
   static constexpr int kOffXs = kStageX + kStageW;
   static constexpr int kOffWs = kOffXs + kStageScales;
-  static constexpr int kSlot = kStageX + kStageW + 2 * kStageScales;  // 51200 for two 6-bit operands
-  static constexpr int kSlots = 3 * kSlot <= 160 * 1024 ? 3 : 2;
+  static constexpr int kSlot = kStageX + kStageW + kStageScales + kStageScalesW;  // 51200 for 6-bit, TN 256
+  static constexpr int kSlots = TN == 256 && 3 * kSlot <= 160 * 1024 ? 3 : 2;
   static constexpr int kLds = kSlots * kSlot;
   static constexpr int kCX = kStageX / 1024 / 4, kCW = kStageW / 1024 / 4;  // 1 KB code copies per wave
   static constexpr int kCopies = kCX + kCW + 2;
   static constexpr int kFirst = kSlots == 3 ? (kCopies + 1) / 2 : kCopies;  // issued in phase 1
   static constexpr int kSecond = kCopies - kFirst;                           // issued in phase 0
   static_assert(kLds <= 160 * 1024, "gfx950 LDS is 160 KB per workgroup");
+  static_assert(TN == 256 || 2 * kLds <= 160 * 1024, "two TN = 128 workgroups share a CU's LDS");
+  static_assert(kStageScalesW == 1024 || kStageScalesW == 512, "weight scales: 4 (or 2 duplicated) waves x 256 B");
   static_assert(kCopies + kFirst <= 63, "vmcnt counts at most 63 outstanding copies");
 };
 
-// MFMA (0..15) of a phase after which copy c of n goes out: every other MFMA
-// when they fit (phase 1 from the first, phase 0 from the second), spread
-// evenly otherwise.
-constexpr int copy_slot(int c, int n, int phase) {
-  return n <= 8 ? 2 * c + (phase == 0 ? 1 : 0) : c * 16 / n;
+// MFMA (0 .. m-1) of a phase of m MFMAs after which copy c of n goes out:
+// every other MFMA when they fit (phase 1 from the first, phase 0 from the
+// second), spread evenly otherwise.
+constexpr int copy_slot(int c, int n, int phase, int m) {
+  return 2 * n <= m ? 2 * c + (phase == 0 ? 1 : 0) : c * m / n;
 }
-constexpr int copies_after(int i, int n, int phase) {
+constexpr int copies_after(int i, int n, int phase, int m) {
   int k = 0;
-  for (int c = 0; c < n; ++c) k += copy_slot(c, n, phase) == i;
+  for (int c = 0; c < n; ++c) k += copy_slot(c, n, phase, m) == i;
   return k;
 }
-constexpr int first_copy_after(int i, int n, int phase) {
+constexpr int first_copy_after(int i, int n, int phase, int m) {
   for (int c = 0; c < n; ++c)
-    if (copy_slot(c, n, phase) == i) return c;
+    if (copy_slot(c, n, phase, m) == i) return c;
   return n;
+}
+// Phase 1's scale-pair reads: nf fragment reads go first, one per MFMA; the
+// ns scale reads follow, two (or more, if the MFMAs run out) per MFMA.
+constexpr int scales_per_mfma(int nf, int ns, int m) {
+  return (ns + (m - nf) - 1) / (m - nf) > 2 ? (ns + (m - nf) - 1) / (m - nf) : 2;
+}
+constexpr int scale_reads_after(int i, int nf, int ns, int m) {
+  const int per = scales_per_mfma(nf, ns, m);
+  const int first = (i - nf) * per;
+  return i < nf || first >= ns ? 0 : (ns - first < per ? ns - first : per);
 }
 
 template <int... I>
@@ -117,7 +138,8 @@ template <class F, int... I>
 __device__ __forceinline__ void static_for(F&& f, Seq<I...>) {
   (f(std::integral_constant<int, I>{}), ...);
 }
-using Seq16 = MakeSeq<16>::type;
+template <int N>
+using SeqN = typename MakeSeq<N>::type;
 
 // global -> LDS copies of 16 bytes (codes) and 4 bytes (scales) per lane.
 // Kept out of the kernel template: the host compilation cannot check the
@@ -200,9 +222,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
-template <int WF, int XF, int OUT, int EPI, int OFMT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
-  using R = Ring<WF, XF>;
+template <int WF, int XF, int OUT, int EPI, int OFMT, int TN = 256>
+__global__ __launch_bounds__(kThreads, TN == 256 ? 1 : 2) void gemm_kernel(const GemmArgs g) {
+  using R = Ring<WF, XF, TN>;
+  static_assert(TN == 256 || EPI != kEpiSwiglu, "the SwiGLU pairing needs 128 weight rows per wave");
   __shared__ __attribute__((aligned(16))) uint8_t lds[R::kLds];
   constexpr int kLayout = OUT == kOutMx ? kLayoutMx : kLayoutContig;
 
@@ -211,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, g.xcd_remap, tm, tn);
-  const int m0 = tm * kTileM, n0 = tn * kTileN;
+  const int m0 = tm * kTileM, n0 = tn * TN;
   const int nk = (g.K + kTileStageK - 1) / kTileStageK;
   const int gx0 = m0 / kTileGroupRows, gw0 = n0 / kTileGroupRows;
 
@@ -237,7 +260,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     const int off = wave * 256 + lane * 4;
     const int grp = off / kChunkScales, within = off - grp * kChunkScales;
     xso = (uint32_t)min(gx0 + grp, g.gx - 1) * kChunkScales + within;
-    wso = (uint32_t)min(gw0 + grp, g.gw - 1) * kChunkScales + within;
+    // TN = 128: a 512-byte weight scale run; waves 2 and 3 copy the same bytes
+    // as waves 0 and 1 (identical data), so every wave issues the same copies
+    const int woff = (R::kStageScalesW == 1024 ? wave : (wave & 1)) * 256 + lane * 4;
+    const int wgrp = woff / kChunkScales, wwithin = woff - wgrp * kChunkScales;
+    wso = (uint32_t)min(gw0 + wgrp, g.gw - 1) * kChunkScales + wwithin;
   }
   const int64_t x_stage = (int64_t)g.gx * R::kChunkX, w_stage = (int64_t)g.gw * R::kChunkW;
   const int64_t xs_stage = (int64_t)g.gx * kChunkScales, ws_stage = (int64_t)g.gw * kChunkScales;
@@ -255,7 +282,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     } else if (idx == R::kCX + R::kCW) {
       copy4_to_lds(g.x_scales + ks * xs_stage + xso, base + R::kOffXs + wave * 256);
     } else {
-      copy4_to_lds(g.w_scales + ks * ws_stage + wso, base + R::kOffWs + wave * 256);
+      copy4_to_lds(g.w_scales + ks * ws_stage + wso,
+                   base + R::kOffWs + (R::kStageScalesW == 1024 ? wave : (wave & 1)) * 256);
     }
   };
   auto issue_range = [&](int ks, int slot, int first, int count) {
@@ -270,16 +298,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   const int wn = wave & 1, wm = wave >> 1;
   const int h = lane >> 5, j = lane & 31;
   const int wrow = feature_of_row<kLayout>(j);
-  const int w16 = R::kOffW + wn * 4 * R::kChunkW + h * R::kHalfW + wrow * 16;
+  constexpr int kFW = R::kFW, kMP = R::kMfmaPhase;
+  const int w16 = R::kOffW + wn * kFW * R::kChunkW + h * R::kHalfW + wrow * 16;
   const int x16 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 16;
-  const int w8 = R::kOffW + wn * 4 * R::kChunkW + h * R::kHalfW + wrow * 8;
+  const int w8 = R::kOffW + wn * kFW * R::kChunkW + h * R::kHalfW + wrow * 8;
   const int x8 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 8;
-  const int wsc = R::kOffWs + wn * 4 * kChunkScales + wrow * 4 + 2 * h;
+  const int wsc = R::kOffWs + wn * kFW * kChunkScales + wrow * 4 + 2 * h;
   const int xsc = R::kOffXs + wm * 4 * kChunkScales + j * 4 + 2 * h;
 
-  v16f acc[4][4];
+  v16f acc[kFW][4];
 #pragma unroll
-  for (int fn = 0; fn < 4; ++fn)
+  for (int fn = 0; fn < kFW; ++fn)
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
@@ -293,9 +322,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   // lane halves make the first 32-element block of the instruction's K = 64
   // (scaled by the byte of lanes 0-31) and registers 4-7 the second (scaled
   // by lanes 32-63), so in sub-step s lane half h holds bytes 16h..16h+15 of
-  // blocks s and 2 + s, which the 8-bit layout's planes 2s and 2s + 1 store.  The 8-byte reads are volatile so they are not fused into
-  // one 16-byte read whose halves would belong to different operands (that
-  // costs register moves).
+  // blocks s and 2 + s, which the 8-bit layout's planes 2s and 2s + 1 store.
+  // The 8-byte reads are volatile so they are not fused into one 16-byte read
+  // whose halves would belong to different operands (that costs register
+  // moves).
   typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2_t;
   auto rd16 = [&](int off) { return *reinterpret_cast<const u32x4*>(lds + off); };
   auto rd8 = [&](int off) { return (u32x2)(*(lds_u32x2_t*)(lds + off)); };
@@ -324,17 +354,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   using bw_t = std::integral_constant<int, R::kBW>;
   using bx_t = std::integral_constant<int, R::kBX>;
   constexpr int kDsW = R::kBW == 4 ? 1 : 2, kDsX = R::kBX == 4 ? 1 : 2;  // LDS reads per operand
-  struct Half {  // one sub-step's operands: 4 weight and 4 activation fragments
-    v8i w[4], x[4];
+  constexpr int kNF = kFW + 4;  // fragments per sub-step (and scale pairs per stage)
+  struct Half {  // one sub-step's operands: kFW weight and 4 activation fragments
+    v8i w[kFW], x[4];
   };
-  struct Scales {  // scale byte pairs (blocks 2h, 2h+1) of the 8 fragments
-    int w[4], x[4];
+  struct Scales {  // scale byte pairs (blocks 2h, 2h+1) of the fragments
+    int w[kFW], x[4];
   };
-  // fragment i (0..7) of a sub-step, in the order w0, x0, w1, x1, ...
+  // fragment i (0 .. kNF-1) of a sub-step, in the order w0, x0, w1, x1, ...,
+  // then the activation fragments left over
+  auto frag_is_w = [](int i) { return i < 2 * kFW && i % 2 == 0; };
+  auto frag_index = [](int i) { return i < 2 * kFW ? i / 2 : i - kFW; };
   auto read_frag = [&](Half& r, int so, auto i_tag, auto sub_tag) {
     constexpr int I = decltype(i_tag)::value;
-    constexpr int F = I / 2;
-    if constexpr (I % 2 == 0)
+    constexpr int F = frag_index(I);
+    if constexpr (frag_is_w(I))
       r.w[F] = op(bw_t{}, sub_tag, so + w16 + F * R::kChunkW, so + w8 + F * R::kChunkW);
     else
       r.x[F] = op(bx_t{}, sub_tag, so + x16 + F * R::kChunkX, so + x8 + F * R::kChunkX);
@@ -342,40 +376,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   auto read_half = [&](int sl, auto sub_tag) {
     const int so = sl * R::kSlot;
     Half r;
-    static_for([&](auto i) { if constexpr (decltype(i)::value < 8) read_frag(r, so, i, sub_tag); }, Seq16{});
+    static_for([&](auto i) { if constexpr (decltype(i)::value < kNF) read_frag(r, so, i, sub_tag); }, SeqN<kMP>{});
     return r;
   };
   auto scale_at = [&](int so, int base, int f) {
     return (int)*reinterpret_cast<const uint16_t*>(lds + so + base + f * kChunkScales);
   };
+  // scale pair s (0 .. kNF-1): the weight fragments' first, then the activations'
+  auto read_scale = [&](Scales& c, int so, auto s_tag) {
+    constexpr int S = decltype(s_tag)::value;
+    if constexpr (S < kFW)
+      c.w[S] = scale_at(so, wsc, S);
+    else
+      c.x[S - kFW] = scale_at(so, xsc, S - kFW);
+  };
   auto read_scales = [&](int sl) {
     const int so = sl * R::kSlot;
     Scales c;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      c.w[f] = scale_at(so, wsc, f);
-      c.x[f] = scale_at(so, xsc, f);
-    }
+    static_for([&](auto i) { if constexpr (decltype(i)::value < kNF) read_scale(c, so, i); }, SeqN<kMP>{});
     return c;
   };
-  // MFMA i (0..15) of a sub-step: weight fragment i / 4 against activation fragment i % 4
+  // MFMA i (0 .. kMP-1) of a sub-step: weight fragment i / 4 against activation fragment i % 4
   auto mfma = [&](const Half& r, const Scales& c, auto i_tag, auto sub_tag) {
     constexpr int I = decltype(i_tag)::value, S = decltype(sub_tag)::value;
     constexpr int FN = I / 4, FM = I % 4;
     acc[FN][FM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(r.w[FN], r.x[FM], acc[FN][FM], WF, XF, S, c.w[FN],
                                                                  S, c.x[FM]);
   };
-  // the 16 MFMAs of one sub-step
+  // the MFMAs of one sub-step
   auto mfmas = [&](const Half& r, const Scales& c, auto sub_tag) {
-    static_for([&](auto i) { mfma(r, c, i, sub_tag); }, Seq16{});
+    static_for([&](auto i) { mfma(r, c, i, sub_tag); }, SeqN<kMP>{});
   };
   using sub0 = std::integral_constant<int, 0>;
   using sub1 = std::integral_constant<int, 1>;
   // The steady-state phases, written in issue order (the LDS reads and the
   // copies into LDS keep their program order) and pinned for the scheduler
-  // by sched_group_barrier: after MFMA i, the LDS reads of fragment i (i < 8)
-  // or of two scale pairs (phase 1, 8 <= i < 12), then the copies scheduled
-  // after it.
+  // by sched_group_barrier: after MFMA i, the LDS reads of fragment i (i <
+  // kNF) or, in phase 1, of the scale pairs scheduled after it, then the
+  // copies scheduled after it.
   // Phase 1: sub-step 1 MFMAs, reads of the next stage's sub-step 0 operands
   // and scales, and the first kFirst copies of stage ks2 into slot slot2.
   auto phase1 = [&](const Half& r, const Scales& c, int ks2, int slot2, int nsl, Half& nr, Scales& ns) {
@@ -384,32 +422,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
         [&](auto i) {
           constexpr int I = decltype(i)::value;
           mfma(r, c, i, sub1{});
-          if constexpr (I < 8) read_frag(nr, so, i, sub0{});
-          if constexpr (I >= 8 && I < 12) {
-            constexpr int F = 2 * ((I - 8) & 1);
-            if constexpr (I < 10) {
-              ns.w[F] = scale_at(so, wsc, F);
-              ns.w[F + 1] = scale_at(so, wsc, F + 1);
-            } else {
-              ns.x[F] = scale_at(so, xsc, F);
-              ns.x[F + 1] = scale_at(so, xsc, F + 1);
-            }
+          if constexpr (I < kNF) read_frag(nr, so, i, sub0{});
+          constexpr int nsr = scale_reads_after(I, kNF, kNF, kMP);
+          if constexpr (nsr > 0) {
+            constexpr int s0 = (I - kNF) * scales_per_mfma(kNF, kNF, kMP);
+            static_for([&](auto k) {
+              if constexpr (decltype(k)::value < nsr) read_scale(ns, so, std::integral_constant<int, s0 + decltype(k)::value>{});
+            }, SeqN<kMP>{});
           }
-          constexpr int n = copies_after(I, R::kFirst, 1), c0 = first_copy_after(I, R::kFirst, 1);
+          constexpr int n = copies_after(I, R::kFirst, 1, kMP), c0 = first_copy_after(I, R::kFirst, 1, kMP);
 #pragma unroll
           for (int k = 0; k < n; ++k) issue_one(c0 + k, ks2, slot2);
         },
-        Seq16{});
+        SeqN<kMP>{});
     static_for(
         [&](auto i) {
           constexpr int I = decltype(i)::value;
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          constexpr int ds = I < 8 ? (I % 2 == 0 ? kDsW : kDsX) : (I < 12 ? 2 : 0);
+          constexpr int ds = (I < kNF ? (frag_is_w(I) ? kDsW : kDsX) : 0) + scale_reads_after(I, kNF, kNF, kMP);
           if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
-          constexpr int n = copies_after(I, R::kFirst, 1);
+          constexpr int n = copies_after(I, R::kFirst, 1, kMP);
           if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
         },
-        Seq16{});
+        SeqN<kMP>{});
   };
   // Phase 0: sub-step 0 MFMAs, reads of the same stage's sub-step 1
   // operands, and copies kFirst.. of stage ks2 into slot slot2.
@@ -419,22 +454,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
         [&](auto i) {
           constexpr int I = decltype(i)::value;
           mfma(r, c, i, sub0{});
-          if constexpr (I < 8) read_frag(nr, so, i, sub1{});
-          constexpr int n = copies_after(I, R::kSecond, 0), c0 = first_copy_after(I, R::kSecond, 0);
+          if constexpr (I < kNF) read_frag(nr, so, i, sub1{});
+          constexpr int n = copies_after(I, R::kSecond, 0, kMP), c0 = first_copy_after(I, R::kSecond, 0, kMP);
 #pragma unroll
           for (int k = 0; k < n; ++k) issue_one(R::kFirst + c0 + k, ks2, slot2);
         },
-        Seq16{});
+        SeqN<kMP>{});
     static_for(
         [&](auto i) {
           constexpr int I = decltype(i)::value;
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          constexpr int ds = I < 8 ? (I % 2 == 0 ? kDsW : kDsX) : 0;
+          constexpr int ds = I < kNF ? (frag_is_w(I) ? kDsW : kDsX) : 0;
           if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
-          constexpr int n = copies_after(I, R::kSecond, 0);
+          constexpr int n = copies_after(I, R::kSecond, 0, kMP);
           if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
         },
-        Seq16{});
+        SeqN<kMP>{});
   };
   auto next_slot = [](int sl) { return sl + 1 == R::kSlots ? 0 : sl + 1; };
 
@@ -505,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   }
 
   // ---- epilogue
-  const int mw0 = m0 + wm * 128, nw0 = n0 + wn * 128;
+  const int mw0 = m0 + wm * 128, nw0 = n0 + wn * (TN / 2);
   // SwiGLU: this wave's 128 stacked rows are the gate rows (fragments 0, 1)
   // and the up rows (fragments 2, 3) of output features nw0/2 .. nw0/2 + 63.
   constexpr bool kSwiglu = EPI == kEpiSwiglu;
@@ -589,21 +624,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
         }
         emit_pair(va, vb, m, gm, nw0 / (2 * kTileStageK), (nw0 / kTileStageK) & 1);
       } else {
+        // the wave's kFW fragments are kFW / 2 block pairs of output stage nw0 / 128
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
+        for (int pr = 0; pr < kFW / 2; ++pr) {
           v16f va = acc[2 * pr][fm], vb = acc[2 * pr + 1][fm];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             va[r] = act(va[r]);
             vb[r] = act(vb[r]);
           }
-          emit_pair(va, vb, m, gm, nw0 / kTileStageK, pr);
+          emit_pair(va, vb, m, gm, nw0 / kTileStageK, (nw0 % kTileStageK) / 64 + pr);
         }
       }
     }
     return;
   }
-  constexpr int kOutFrags = kSwiglu ? 2 : 4;
+  constexpr int kOutFrags = kSwiglu ? 2 : kFW;
 #pragma unroll
   for (int fn = 0; fn < kOutFrags; ++fn) {
 #pragma unroll
@@ -656,16 +692,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
   }
 }
 
-template <int WF, int XF, int EPI>
+template <int WF, int XF, int EPI, int TN>
 void launch_epi(const GemmArgs& a, int out_kind, int out_fmt, dim3 grid, dim3 block, hipStream_t stream) {
   if (out_kind == kOutF32)
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, EPI, kFmtE2M3>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, EPI, kFmtE2M3, TN>), grid, block, 0, stream, a);
   else if (out_kind == kOutBf16)
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, EPI, kFmtE2M3>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, EPI, kFmtE2M3, TN>), grid, block, 0, stream, a);
   else if (out_fmt == kFmtE2M3)
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE2M3>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE2M3, TN>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE3M2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE3M2, TN>), grid, block, 0, stream, a);
 }
 
 // The 6-bit pairs: every epilogue and output kind.
@@ -673,12 +709,21 @@ template <int WF, int XF>
 hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream,
                           std::true_type) {
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+  if (a.tile_n == 128) {
+    if (epilogue == kEpiGeluTanh)
+      launch_epi<WF, XF, kEpiGeluTanh, 128>(a, out_kind, out_fmt, grid, block, stream);
+    else if (epilogue == kEpiNone)
+      launch_epi<WF, XF, kEpiNone, 128>(a, out_kind, out_fmt, grid, block, stream);
+    else
+      return hipErrorInvalidValue;  // SwiGLU needs 256-feature tiles (rejected before this point)
+    return hipGetLastError();
+  }
   if (epilogue == kEpiGeluTanh)
-    launch_epi<WF, XF, kEpiGeluTanh>(a, out_kind, out_fmt, grid, block, stream);
+    launch_epi<WF, XF, kEpiGeluTanh, 256>(a, out_kind, out_fmt, grid, block, stream);
   else if (epilogue == kEpiSwiglu)
-    launch_epi<WF, XF, kEpiSwiglu>(a, out_kind, out_fmt, grid, block, stream);
+    launch_epi<WF, XF, kEpiSwiglu, 256>(a, out_kind, out_fmt, grid, block, stream);
   else
-    launch_epi<WF, XF, kEpiNone>(a, out_kind, out_fmt, grid, block, stream);
+    launch_epi<WF, XF, kEpiNone, 256>(a, out_kind, out_fmt, grid, block, stream);
   return hipGetLastError();
 }
 
@@ -686,7 +731,7 @@ hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out
 template <int WF, int XF>
 hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int, hipStream_t stream, std::false_type) {
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
-  if (epilogue != kEpiNone || out_kind == kOutMx) return hipErrorInvalidValue;
+  if (epilogue != kEpiNone || out_kind == kOutMx || a.tile_n != 256) return hipErrorInvalidValue;
   if (out_kind == kOutF32)
     hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, kEpiNone, kFmtE2M3>), grid, block, 0, stream, a);
   else

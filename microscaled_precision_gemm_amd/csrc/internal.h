@@ -54,9 +54,8 @@ constexpr int kEpiNone = 0;
 constexpr int kEpiGeluTanh = 1;
 constexpr int kEpiSwiglu = 2;   // stacked gate/up rows (runs of 64 + 64), out[:, f] = silu(gate f) * up f
 
-// Main GEMM tile: 256 tokens x 256 output features, K staged 128 at a time.
+// Main GEMM tile: 256 tokens x 256 (or 128) output features, K staged 128 at a time.
 constexpr int kTileM = 256;
-constexpr int kTileN = 256;
 constexpr int kStageK = 128;
 
 struct GemmArgs {
@@ -73,6 +72,7 @@ struct GemmArgs {
   int32_t vec_store;        // 1 when 16-byte vector stores of a row segment are aligned
   int32_t group_m;          // tile order: m-tiles per group (1 .. 16)
   int32_t xcd_remap;        // tile order: 1 = contiguous tile ranges per XCD
+  int32_t tile_n;           // output features per tile: 256 or 128
 };
 
 hipError_t launch_quantize(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,

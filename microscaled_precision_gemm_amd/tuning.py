@@ -3,16 +3,19 @@
 The Hedra post on Krea 3 (section "We tuned before writing custom kernels")
 found library kernels falling back to a generic configuration for shapes
 missing from their dispatch tables, and kept per-shape choices found by timing
-candidates on real data.  This module does that for the one knob of mx_gemm
-that is free to choose per shape: the order in which output tiles are handed
-to workgroups (``MXGemmConfig``: group width and XCD remapping), which decides
-which operand stages the tiles in flight share in each XCD's L2.
+candidates on real data.  This module does that for the knobs of mx_gemm that
+are free to choose per shape (``MXGemmConfig``): the order in which output
+tiles are handed to workgroups (group width and XCD remapping), which decides
+which operand stages the tiles in flight share in each XCD's L2, and the tile
+width (256 output features with one workgroup per CU, or 128 with two, which
+pays off where K is short and per-tile fixed costs weigh more).
 
 * ``tune_gemm`` times every candidate on the caller's own operands (HIP events
   on the current stream, after a warm-up), requires each candidate's output to
-  be bit-identical to the default configuration's (the tile order never
-  changes the arithmetic, and the check holds the library to that on the real
-  data), and records the fastest, keeping the default unless a candidate beats
+  be bit-identical to the default configuration's (neither the tile order nor
+  the tile width changes the arithmetic: each output takes the same matrix-core
+  sequence over K; the check holds the library to that on the real data), and
+  records the fastest, keeping the default unless a candidate beats
   it by more than ``margin``.
 * ``TuningTable.lookup`` returns the recorded configuration for a call, or
   None (the library default) for shapes never tuned.
@@ -30,8 +33,16 @@ import torch
 
 from .binding import MXGemmConfig, MXTensor, mx_gemm, mx_gemm_default_config
 
-CANDIDATES = ((4, 1), (2, 1), (8, 1), (16, 1), (1, 1), (4, 0), (8, 0))
-FORMAT_VERSION = 1
+CANDIDATES = ((4, 1, 256), (2, 1, 256), (8, 1, 256), (16, 1, 256), (1, 1, 256), (4, 0, 256), (8, 0, 256),
+              (4, 1, 128), (2, 1, 128), (8, 1, 128), (16, 1, 128))
+FORMAT_VERSION = 2
+FP6 = ("e2m3", "e3m2")
+
+
+def supports(config: tuple[int, int, int], a_fmt: str, w_fmt: str, epilogue: str) -> bool:
+    """Whether mx_gemm accepts this configuration for the call (128-feature
+    tiles: 6-bit operands without the SwiGLU pairing)."""
+    return config[2] == 256 or (a_fmt in FP6 and w_fmt in FP6 and epilogue != "swiglu")
 
 
 def device_name(device: torch.device | None = None) -> str:
@@ -81,7 +92,8 @@ class TuningTable:
             raise ValueError(f"{path}: unknown tuning table format {data.get('format')!r}")
         for key, e in data["entries"].items():
             cfg = e.get("config")
-            if not (isinstance(cfg, list) and len(cfg) == 2 and 1 <= cfg[0] <= 16 and cfg[1] in (0, 1)):
+            if not (isinstance(cfg, list) and len(cfg) == 3 and 1 <= cfg[0] <= 16 and cfg[1] in (0, 1)
+                    and cfg[2] in (128, 256)):
                 raise ValueError(f"{path}: bad entry {key!r}")
         self.entries.update(data["entries"])
 
@@ -114,17 +126,18 @@ def _time_us(fn, iters: int) -> float:
 def tune_gemm(table: TuningTable, a: MXTensor, w: MXTensor, out_kind: str = "bf16", epilogue: str = "none",
               out_fmt: str = "e2m3", candidates=CANDIDATES, iters: int = 10, rounds: int = 3,
               margin: float = 0.01) -> dict:
-    """Time the candidate tile orders for this call on these operands and
-    record the fastest in ``table`` (see the module docstring).  Returns the
-    recorded entry; raises if a candidate's output differs from the default's."""
+    """Time the candidate configurations this call supports on these operands
+    and record the fastest in ``table`` (see the module docstring).  Returns
+    the recorded entry; raises if a candidate's output differs from the
+    default's."""
     default = mx_gemm_default_config().key()
-    cands = [default] + [c for c in candidates if c != default]
+    cands = [default] + [c for c in candidates if c != default and supports(c, a.fmt, w.fmt, epilogue)]
     ref = mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, config=default)
     outs = {c: mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, config=c) for c in cands}
     torch.cuda.synchronize()
     for c, o in outs.items():
         if not _same(o, ref):
-            raise RuntimeError(f"tile order {c} changed the result of mx_gemm; not recorded")
+            raise RuntimeError(f"configuration {c} changed the result of mx_gemm; not recorded")
     for _ in range(3):  # warm-up, and let the clocks settle
         for c in cands:
             mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, out=outs[c], config=c)
@@ -139,7 +152,7 @@ def tune_gemm(table: TuningTable, a: MXTensor, w: MXTensor, out_kind: str = "bf1
     if best[pick] > best[default] * (1.0 - margin):
         pick = default
     entry = {"config": list(pick), "us": round(best[pick], 2), "default_us": round(best[default], 2),
-             "candidates": {f"{c[0]},{c[1]}": round(t, 2) for c, t in best.items()}}
+             "candidates": {",".join(map(str, c)): round(t, 2) for c, t in best.items()}}
     key = gemm_key(a.rows, w.rows, w.k, a.fmt, w.fmt, epilogue, out_kind, out_fmt, device_name())
     table.record(key, entry)
     return entry

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mx.mx_version() == 200
+    assert mx.mx_version() == 300
     for st in range(-7, 1):
         assert mx.mx_status_string(st) and mx.mx_status_string(st) != "unknown status"
     assert mx.mx_status_string(-99) == "unknown status"
@@ -176,13 +176,23 @@ def test_gemm_config_validation(L):
                 out_fmt=2, ws=NULL, ws_bytes=0)
     d = B.MXGemmConfig()
     L.mx_gemm_default_config(ctypes.byref(d))
-    assert d.key() == (4, 1)
-    for bad in ((0, 1), (17, 1), (4, 2), (4, -1)):
+    assert d.key() == (4, 1, 256)
+    for bad in ((0, 1), (17, 1), (4, 2), (4, -1), (4, 1, 64), (4, 1, 0), (4, 1, 512)):
         c = B.MXGemmConfig(*bad)
         assert L.mx_gemm_with_config(*args.values(), ctypes.byref(c), NULL) == B.MX_ERR_FORMAT
     ok = B.MXGemmConfig(8, 0)
     assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(ok), NULL) == B.MX_OK
     assert L.mx_gemm_with_config(*dict(args, k=100).values(), ctypes.byref(ok), NULL) == B.MX_ERR_SHAPE
+    # 128-feature tiles: the 6-bit pairs without SwiGLU; other pairs and SwiGLU are refused
+    narrow = B.MXGemmConfig(4, 1, 128)
+    assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(narrow), NULL) == B.MX_OK
+    assert L.mx_gemm_with_config(*dict(args, m=0, epi=1).values(), ctypes.byref(narrow), NULL) == B.MX_OK
+    assert L.mx_gemm_with_config(*dict(args, m=0, out_kind=2, out_scales=FAKE).values(), ctypes.byref(narrow),
+                                 NULL) == B.MX_OK
+    assert L.mx_gemm_with_config(*dict(args, epi=2, n=128).values(), ctypes.byref(narrow),
+                                 NULL) == B.MX_ERR_UNSUPPORTED
+    assert L.mx_gemm_with_config(*dict(args, a_fmt=0, w_fmt=0).values(), ctypes.byref(narrow),
+                                 NULL) == B.MX_ERR_UNSUPPORTED
 
 
 def sk(**kw):

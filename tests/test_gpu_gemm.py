@@ -179,6 +179,44 @@ def test_gemm_gelu_f32_output(a_fmt, w_fmt):
     assert bad.size == 0, f"{len(bad)} GELU outputs off; first {bad[0].tolist()}"
 
 
+NARROW = (4, 1, 128)  # 128-feature tiles, two workgroups per CU
+
+
+@pytest.mark.parametrize("a_fmt,w_fmt", FORMAT_PAIRS)
+@pytest.mark.parametrize("m,n,k", [(300, 544, 416), (37, 288, 160), (512, 384, 640)])
+def test_gemm_narrow_tiles(a_fmt, w_fmt, m, n, k):
+    """The 128-feature tile: plain fp32 / bf16 outputs against the oracle,
+    ragged in M and N, and bit-identical to the 256-feature tile (each output
+    takes the same matrix-core sequence over K), for every output kind and
+    both epilogues it serves."""
+    a, w, qa, qw, c, s = _operands(m, n, k, a_fmt, w_fmt, seed=3 * m + n + k)
+    say(f"gemm narrow tiles {m}x{n}x{k} a={a_fmt} w={w_fmt}")
+    wq = _gpu_weights(w, w_fmt, qw)
+    aq = mx.mx_quantize(a.cuda(), a_fmt)
+    for out_kind in ("f32", "bf16"):
+        o = mx.mx_gemm(aq, wq, out_kind=out_kind, config=NARROW)
+        o_in = mx.mx_gemm(a.cuda(), wq, out_kind=out_kind, a_fmt=a_fmt, config=NARROW)
+        wide = mx.mx_gemm(aq, wq, out_kind=out_kind)
+        torch.cuda.synchronize()
+        g = o.float().cpu().numpy().astype(np.float64)
+        (assert_fp32_close if out_kind == "f32" else assert_bf16_close)(g, c, s, f"narrow {out_kind}")
+        assert torch.equal(o, wide) and torch.equal(o, o_in)
+    for epi in ("gelu_tanh", "none"):
+        for out_kind in ("f32", "mx"):
+            o = mx.mx_gemm(aq, wq, out_kind=out_kind, epilogue=epi, config=NARROW)
+            wide = mx.mx_gemm(aq, wq, out_kind=out_kind, epilogue=epi)
+            torch.cuda.synchronize()
+            if out_kind == "mx":
+                assert torch.equal(o.codes, wide.codes) and torch.equal(o.scales, wide.scales)
+            else:
+                assert torch.equal(o, wide)
+    o = mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", out_fmt="e3m2", config=NARROW)
+    torch.cuda.synchronize()
+    oc, os_ = mx_rows_view(o)
+    stats = check_mx_epilogue(oc, os_, c, s, True, "e3m2")
+    assert stats["code_steps"] <= 1e-3 * stats["elements"]
+
+
 def test_chained_fc1_fc2_small():
     """fc1 (GELU, MX out) feeding fc2 directly, as in the fused MLP: the MX
     intermediate is consumed as fc2's activations without re-quantization."""
