@@ -421,6 +421,7 @@ def main():
                        "fc2_tflops": round(r["flops_per_gemm"] / r["fc2_ms"] / 1e9, 1),
                        "quantize_gb_s": round(r["quantize_bytes"] / r["quantize_ms"] / 1e6, 1)},
         "tuning": r["tuning"],
+        "gemm_kernels": r["kernels"],
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
         "swiglu_mlp": swiglu,
         "producer": producer,

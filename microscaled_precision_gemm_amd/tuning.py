@@ -46,7 +46,12 @@ def supports(config: tuple[int, int, int], a_fmt: str, w_fmt: str, epilogue: str
 
 
 def device_name(device: torch.device | None = None) -> str:
-    return torch.cuda.get_device_name(device)
+    """The device part of a table key: the ISA name and the compute-unit count
+    (the marketing name is generic on some boards and empty under some
+    profilers)."""
+    p = torch.cuda.get_device_properties(device)
+    arch = (getattr(p, "gcnArchName", "") or "").split(":")[0]
+    return f"{arch or p.name or 'gpu'}/{p.multi_processor_count}cu"
 
 
 def gemm_key(m: int, n: int, k: int, a_fmt: str, w_fmt: str, epilogue: str, out_kind: str, out_fmt: str,
