@@ -72,7 +72,7 @@ def settle(fn, seconds: float = SETTLE_S):
         torch.cuda.synchronize()
 
 
-def bench_mlp(steps: int, warmup: int, tune: bool = True, table_path: str | None = None):
+def bench_mlp(table, steps: int, warmup: int, tune: bool = True):
     fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
     m, d, hdim = fc1.m, fc1.k, fc1.n
     dev = torch.device("cuda:0")
@@ -82,10 +82,8 @@ def bench_mlp(steps: int, warmup: int, tune: bool = True, table_path: str | None
     xq = mx.MXTensor.empty(m, d, "e2m3", "tiled", dev)
     h = mx.MXTensor.empty(m, hdim, "e2m3", "tiled", dev)
     y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
-    # per-shape tile order and width from the tuning table: tuned here, untimed, on
-    # these operands, or read from `table_path` when it holds both shapes (tuned
-    # there and saved, when it does not)
-    table = tuning.TuningTable(table_path)
+    # per-shape launch configurations from the tuning table: tuned here, untimed,
+    # on these operands, unless the table (read from a file) already holds them
     cfg1 = table.lookup(m, hdim, d, epilogue="gelu_tanh", out_kind="mx")
     cfg2 = table.lookup(m, d, hdim, epilogue="none", out_kind="bf16")
     tuned = {}
@@ -95,14 +93,14 @@ def bench_mlp(steps: int, warmup: int, tune: bool = True, table_path: str | None
         h_t = mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh")
         tuned["fc2"] = tuning.tune_gemm(table, h_t, w2, out_kind="bf16")
         del h_t
-        if table_path is not None:
-            table.save()
         cfg1 = table.lookup(m, hdim, d, epilogue="gelu_tanh", out_kind="mx")
         cfg2 = table.lookup(m, d, hdim, epilogue="none", out_kind="bf16")
     elif tune:
         key1 = tuning.gemm_key(m, hdim, d, "e2m3", "e2m3", "gelu_tanh", "mx", "e2m3", tuning.device_name())
         key2 = tuning.gemm_key(m, d, hdim, "e2m3", "e2m3", "none", "bf16", "e2m3", tuning.device_name())
         tuned = {"fc1": table.entries[key1], "fc2": table.entries[key2]}
+    else:
+        cfg1 = cfg2 = None  # the library default
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -201,11 +199,12 @@ def bench_swiglu_mlp(steps: int, warmup: int):
 PEAK_BY_FMT = {"e2m3": 10100.0, "e2m1": 10100.0, "e4m3": 5000.0, "e5m2": 5000.0}
 
 
-def bench_formats(iters: int = 20):
+def bench_formats(table, iters: int = 20, tune: bool = True):
     """The operand formats of the same scaled matrix instruction on fc1's shape
     (20480 x 3072 x 12288, both operands pre-quantized, bf16 out, no
     epilogue): MXFP6 E2M3, MXFP4 E2M1 and MXFP8 E4M3, each against its own
-    dense peak (10.1 PF for FP6 and FP4, 5.0 PF for FP8)."""
+    dense peak (10.1 PF for FP6 and FP4, 5.0 PF for FP8), each in the launch
+    configuration the tuning table picks for it (tuned untimed, first)."""
     w = syn.WORKLOADS["fc1"]
     dev = torch.device("cuda:0")
     a_src = syn.make_a(w).to(dev)
@@ -215,9 +214,15 @@ def bench_formats(iters: int = 20):
     res = {}
     for fmt in ("e2m3", "e2m1", "e4m3"):
         aq, wq = mx.mx_quantize(a_src, fmt), mx.mx_quantize(w_src, fmt)
+        cfg = table.lookup(w.m, w.n, w.k, fmt, fmt, "none", "bf16")
+        if tune and cfg is None:
+            tuning.tune_gemm(table, aq, wq, out_kind="bf16")
+            cfg = table.lookup(w.m, w.n, w.k, fmt, fmt, "none", "bf16")
+        elif not tune:
+            cfg = None
 
         def call():
-            mx.mx_gemm(aq, wq, out_kind="bf16", out=out)
+            mx.mx_gemm(aq, wq, out_kind="bf16", out=out, config=cfg)
 
         settle(call, 0.2)
         e0, e1 = _events(2)
@@ -229,7 +234,8 @@ def bench_formats(iters: int = 20):
         ms = e0.elapsed_time(e1) / iters
         tf = flops / ms / 1e9
         res[fmt] = {"ms": round(ms, 4), "tflops": round(tf, 1), "peak_tflops": PEAK_BY_FMT[fmt],
-                    "frac": round(tf / PEAK_BY_FMT[fmt], 4)}
+                    "frac": round(tf / PEAK_BY_FMT[fmt], 4),
+                    "config": list(cfg.key()) if cfg is not None else list(mx.mx_gemm_default_config().key())}
         del aq, wq
     return {"workload": "fc1-shaped GEMM 20480x3072x12288, pre-quantized operands, bf16 out", **res}
 
@@ -385,7 +391,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
 
-    r = bench_mlp(args.steps, args.warmup, tune=not args.no_tune, table_path=args.tuning_table)
+    table = tuning.TuningTable(args.tuning_table)
+    r = bench_mlp(table, args.steps, args.warmup, tune=not args.no_tune)
     ms_step = r["wall_ms_per_step"]
     value = r["flops_per_step"] / ms_step / 1e9  # TFLOP/s
     # dominant kernel: the slower of the two GEMMs, timed with events on its own stream
@@ -395,7 +402,9 @@ def main():
     skinny = [bench_skinny(16, 16, args.skinny_iters), bench_skinny(8, 16, args.skinny_iters)]
     swiglu = bench_swiglu_mlp(args.steps, args.warmup)
     producer = bench_producer()
-    formats = bench_formats()
+    formats = bench_formats(table, tune=not args.no_tune)
+    if args.tuning_table and not args.no_tune:
+        table.save()
     line = {
         "metric": METRIC,
         "value": round(value, 2),

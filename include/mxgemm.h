@@ -249,8 +249,8 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
             int32_t out_fmt, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Launch configuration of mx_gemm: the output tile width and the order in
- * which the tiles are handed to workgroups.  It changes the speed (which
+ * Launch configuration of mx_gemm: the output tile width, the waves per
+ * workgroup and the order in which the tiles are handed to workgroups.  It changes the speed (which
  * operand stages the workgroups in flight share in each XCD's L2, how many
  * workgroups share a CU), never the result: every configuration computes each
  * output with the same arithmetic (the same MFMA sequence over K per output).  The Hedra
@@ -267,6 +267,9 @@ typedef struct {
                         ring, two workgroups per CU, so one's prologue, waits and epilogue
                         overlap the other's matrix work; the 6-bit format pairs with
                         MX_EPI_NONE or MX_EPI_GELU_TANH only, else MX_ERR_UNSUPPORTED)      */
+  int32_t waves;     /* waves per workgroup: 4 (default) or, with tile_n = 256, 8 (2 x 4 waves
+                        of 128 x 64, two per SIMD, sharing the tile's operand ring; any format
+                        pair, not MX_EPI_SWIGLU, else MX_ERR_UNSUPPORTED)                     */
 } mx_gemm_config;
 
 /* mx_gemm_default_config - fill *config with the defaults mx_gemm uses. */

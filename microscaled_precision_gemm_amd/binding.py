@@ -55,17 +55,18 @@ EXPORTED = ("mx_quantize", "mx_rmsnorm_quantize", "mx_packed_bytes", "mx_gemm", 
 
 
 class MXGemmConfig(ctypes.Structure):
-    """mx_gemm_config: the tile order and tile width of mx_gemm (speed only,
-    never the result).  Built from (group_m, xcd_remap[, tile_n]); tile_n
-    defaults to 256."""
+    """mx_gemm_config: the tile order, tile width and waves per workgroup of
+    mx_gemm (speed only, never the result).  Built from (group_m, xcd_remap[,
+    tile_n[, waves]]); tile_n defaults to 256, waves to 4."""
 
-    _fields_ = [("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("tile_n", ctypes.c_int32)]
+    _fields_ = [("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("waves", ctypes.c_int32)]
 
-    def __init__(self, group_m: int = 4, xcd_remap: int = 1, tile_n: int = 256):
-        super().__init__(group_m, xcd_remap, tile_n)
+    def __init__(self, group_m: int = 4, xcd_remap: int = 1, tile_n: int = 256, waves: int = 4):
+        super().__init__(group_m, xcd_remap, tile_n, waves)
 
-    def key(self) -> tuple[int, int, int]:
-        return (int(self.group_m), int(self.xcd_remap), int(self.tile_n))
+    def key(self) -> tuple[int, int, int, int]:
+        return (int(self.group_m), int(self.xcd_remap), int(self.tile_n), int(self.waves))
 
 
 class MXError(RuntimeError):
@@ -276,8 +277,8 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
     call) or an MXTensor.  Returns a [m, n_out] tensor, or an MXTensor for
     out_kind="mx"; n_out = n, or n / 2 for epilogue="swiglu" (``w`` then holds
     stacked gate/up rows, see include/mxgemm.h).  ``config``: the tile order
-    and width (an MXGemmConfig or (group_m, xcd_remap[, tile_n])); None = the
-    library default."""
+    and shape (an MXGemmConfig or (group_m, xcd_remap[, tile_n[, waves]]));
+    None = the library default."""
     _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
     n_out = n // 2 if epilogue == "swiglu" else n

@@ -108,7 +108,7 @@ hipError_t launch_gemm(const GemmArgs& a, int x_fmt, int w_fmt, int epilogue, in
 
 extern "C" {
 
-int mx_version(void) { return 300; }
+int mx_version(void) { return 400; }
 
 const char* mx_status_string(int status) {
   switch (status) {
@@ -184,6 +184,7 @@ void mx_gemm_default_config(mx_gemm_config* config) {
   config->group_m = 4;
   config->xcd_remap = 1;
   config->tile_n = 256;
+  config->waves = 4;
 }
 
 int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
@@ -204,7 +205,7 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   mx_gemm_default_config(&cfg);
   if (config) {
     if (config->group_m < 1 || config->group_m > 16 || (config->xcd_remap != 0 && config->xcd_remap != 1) ||
-        (config->tile_n != 256 && config->tile_n != 128))
+        (config->tile_n != 256 && config->tile_n != 128) || (config->waves != 4 && config->waves != 8))
       return MX_ERR_FORMAT;
     cfg = *config;
   }
@@ -218,6 +219,8 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   if (!fp6_fmt(w_fmt) && (epilogue != MX_EPI_NONE || out_kind == MX_OUT_MX)) return MX_ERR_UNSUPPORTED;
   // 128-feature tiles: the 6-bit pairs without the SwiGLU pairing
   if (cfg.tile_n == 128 && (!fp6_fmt(w_fmt) || epilogue == MX_EPI_SWIGLU)) return MX_ERR_UNSUPPORTED;
+  // eight waves: 256-feature tiles, not the SwiGLU pairing
+  if (cfg.waves == 8 && (cfg.tile_n != 256 || epilogue == MX_EPI_SWIGLU)) return MX_ERR_UNSUPPORTED;
   const int64_t n_out = epilogue == MX_EPI_SWIGLU ? n / 2 : n;
   if (!out) return MX_ERR_NULL;
   if (out_kind == MX_OUT_MX) {
@@ -260,6 +263,7 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   g.tiles_m = (int32_t)ceil_div(m, kTileM);
   g.tiles_n = (int32_t)ceil_div(n, cfg.tile_n);
   g.tile_n = cfg.tile_n;
+  g.waves = cfg.waves;
   g.gx = (int32_t)ceil_div(m, kTileGroupRows);
   g.gw = (int32_t)ceil_div(n, kTileGroupRows);
   const int64_t esize = out_kind == MX_OUT_F32 ? 4 : 2;

@@ -51,7 +51,6 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;
 constexpr int kGroupsPerTile = kTileM / kTileGroupRows;            // 8 activation groups per tile
 constexpr int kStageScales = kGroupsPerTile * kChunkScales;         // 1 KB of activation scales
 static_assert(kStageScales == 4 * 64 * 4, "one 4-byte copy per lane per wave covers a stage's scales");
@@ -71,14 +70,20 @@ static_assert(kStageScales == 4 * 64 * 4, "one 4-byte copy per lane per wave cov
 // accumulator registers each, one workgroup per CU) or 128 (4 waves of
 // 128 x 64, 128 accumulators, and a two-slot ring of 37.5 KB slots, so that
 // two workgroups share a CU and one's waits, prologue and epilogue overlap
-// the other's matrix work).
-template <int WF, int XF, int TN = 256>
+// the other's matrix work).  WV is the number of waves: 4 (2 x 2 waves over
+// the tile) or, for TN = 256, 8 (2 x 4 waves of 128 x 64, two waves per
+// SIMD sharing the three-slot ring; each wave issues half the copies, and
+// its one scale copy is the activations' (waves 0-3) or the weights'
+// (waves 4-7) 256-byte quarter).
+template <int WF, int XF, int TN = 256, int WV = 4>
 struct Ring {
+  static constexpr int kWaves = WV, kThreads = 64 * WV;
+  static constexpr int kWN = WV / 2;                                  // waves along N (2 along M)
   static constexpr int kBW = fmt_bits(WF), kBX = fmt_bits(XF);
   static constexpr int kChunkW = chunk_codes(kBW), kChunkX = chunk_codes(kBX);
   static constexpr int kHalfW = half_codes(kBW), kHalfX = half_codes(kBX);
   static constexpr int kGroupsW = TN / kTileGroupRows;                // weight groups per tile
-  static constexpr int kFW = TN / 64;                                 // weight fragments per wave
+  static constexpr int kFW = TN / kWN / 32;                           // weight fragments per wave
   static constexpr int kMfmaPhase = 4 * kFW;                          // MFMAs per sub-step
   static constexpr int kStageW = kGroupsW * kChunkW, kStageX = kGroupsPerTile * kChunkX;
   static constexpr int kStageScalesW = kGroupsW * kChunkScales;
@@ -89,14 +94,17 @@ struct Ring {
   static constexpr int kSlot = kStageX + kStageW + kStageScales + kStageScalesW;  // 51200 for 6-bit, TN 256
   static constexpr int kSlots = TN == 256 && 3 * kSlot <= 160 * 1024 ? 3 : 2;
   static constexpr int kLds = kSlots * kSlot;
-  static constexpr int kCX = kStageX / 1024 / 4, kCW = kStageW / 1024 / 4;  // 1 KB code copies per wave
-  static constexpr int kCopies = kCX + kCW + 2;
+  static constexpr int kCX = kStageX / 1024 / WV, kCW = kStageW / 1024 / WV;  // 1 KB code copies per wave
+  static constexpr int kScaleCopies = WV == 8 ? 1 : 2;                      // 256-byte scale copies per wave
+  static constexpr int kCopies = kCX + kCW + kScaleCopies;
   static constexpr int kFirst = kSlots == 3 ? (kCopies + 1) / 2 : kCopies;  // issued in phase 1
   static constexpr int kSecond = kCopies - kFirst;                           // issued in phase 0
   static_assert(kLds <= 160 * 1024, "gfx950 LDS is 160 KB per workgroup");
   static_assert(TN == 256 || 2 * kLds <= 160 * 1024, "two TN = 128 workgroups share a CU's LDS");
   static_assert(kStageScalesW == 1024 || kStageScalesW == 512, "weight scales: 4 (or 2 duplicated) waves x 256 B");
   static_assert(kCopies + kFirst <= 63, "vmcnt counts at most 63 outstanding copies");
+  static_assert(WV == 4 || (WV == 8 && TN == 256), "eight waves tile 256 x 256 as 2 x 4 waves of 128 x 64");
+  static_assert(kStageX % (1024 * WV) == 0 && kStageW % (1024 * WV) == 0, "every wave copies whole 1 KB runs");
 };
 
 // MFMA (0 .. m-1) of a phase of m MFMAs after which copy c of n goes out:
@@ -222,10 +230,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
-template <int WF, int XF, int OUT, int EPI, int OFMT, int TN = 256>
-__global__ __launch_bounds__(kThreads, TN == 256 ? 1 : 2) void gemm_kernel(const GemmArgs g) {
-  using R = Ring<WF, XF, TN>;
-  static_assert(TN == 256 || EPI != kEpiSwiglu, "the SwiGLU pairing needs 128 weight rows per wave");
+template <int WF, int XF, int OUT, int EPI, int OFMT, int TN = 256, int WV = 4>
+__global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const GemmArgs g) {
+  using R = Ring<WF, XF, TN, WV>;
+  static_assert((TN == 256 && WV == 4) || EPI != kEpiSwiglu, "the SwiGLU pairing needs 128 weight rows per wave");
   __shared__ __attribute__((aligned(16))) uint8_t lds[R::kLds];
   constexpr int kLayout = OUT == kOutMx ? kLayoutMx : kLayoutContig;
 
@@ -255,19 +263,27 @@ __global__ __launch_bounds__(kThreads, TN == 256 ? 1 : 2) void gemm_kernel(const
     const int grp = off / R::kChunkW, within = off - grp * R::kChunkW;
     wo[i] = (uint32_t)min(gw0 + grp, g.gw - 1) * R::kChunkW + within;
   }
+  // scale copies: quarter q (256 bytes) of the activations' and of the
+  // weights' 1 KB scale run of a stage (4 waves: quarter `wave` of both; 8
+  // waves: waves 0-3 the activations', waves 4-7 the weights')
+  const int xq = WV == 8 ? (wave & 3) : wave;
+  const int wq = WV == 8 ? (wave & 3) : wave;
   uint32_t xso, wso;
   {
-    const int off = wave * 256 + lane * 4;
+    const int off = xq * 256 + lane * 4;
     const int grp = off / kChunkScales, within = off - grp * kChunkScales;
     xso = (uint32_t)min(gx0 + grp, g.gx - 1) * kChunkScales + within;
     // TN = 128: a 512-byte weight scale run; waves 2 and 3 copy the same bytes
     // as waves 0 and 1 (identical data), so every wave issues the same copies
-    const int woff = (R::kStageScalesW == 1024 ? wave : (wave & 1)) * 256 + lane * 4;
+    const int woff = (R::kStageScalesW == 1024 ? wq : (wq & 1)) * 256 + lane * 4;
     const int wgrp = woff / kChunkScales, wwithin = woff - wgrp * kChunkScales;
     wso = (uint32_t)min(gw0 + wgrp, g.gw - 1) * kChunkScales + wwithin;
   }
   const int64_t x_stage = (int64_t)g.gx * R::kChunkX, w_stage = (int64_t)g.gw * R::kChunkW;
   const int64_t xs_stage = (int64_t)g.gx * kChunkScales, ws_stage = (int64_t)g.gw * kChunkScales;
+  const int xs_dst = R::kOffXs + xq * 256;
+  const int ws_dst = R::kOffWs + (R::kStageScalesW == 1024 ? wq : (wq & 1)) * 256;
+  const bool x_scale_wave = WV == 4 || wave < 4;  // 8 waves: which scale run this wave copies
 
   // copy number idx (0 .. kCopies-1) of this wave's share of stage ks into
   // ring slot `slot`: activation codes, weight codes, activation scales,
@@ -279,11 +295,10 @@ __global__ __launch_bounds__(kThreads, TN == 256 ? 1 : 2) void gemm_kernel(const
     } else if (idx < R::kCX + R::kCW) {
       const int i = idx - R::kCX;
       copy16_to_lds(g.w_codes + ks * w_stage + wo[i], base + R::kOffW + (wave * R::kCW + i) * 1024);
-    } else if (idx == R::kCX + R::kCW) {
-      copy4_to_lds(g.x_scales + ks * xs_stage + xso, base + R::kOffXs + wave * 256);
+    } else if (idx == R::kCX + R::kCW && x_scale_wave) {
+      copy4_to_lds(g.x_scales + ks * xs_stage + xso, base + xs_dst);
     } else {
-      copy4_to_lds(g.w_scales + ks * ws_stage + wso,
-                   base + R::kOffWs + (R::kStageScalesW == 1024 ? wave : (wave & 1)) * 256);
+      copy4_to_lds(g.w_scales + ks * ws_stage + wso, base + ws_dst);
     }
   };
   auto issue_range = [&](int ks, int slot, int first, int count) {
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kThreads, TN == 256 ? 1 : 2) void gemm_kernel(const
   // Half h of a chunk holds this lane's blocks 2h (sub-step 0) and 2h+1
   // (sub-step 1) in planes of 16 bytes per row (and, for the 6-bit types, of
   // 8 bytes per row).
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % R::kWN, wm = wave / R::kWN;
   const int h = lane >> 5, j = lane & 31;
   const int wrow = feature_of_row<kLayout>(j);
   constexpr int kFW = R::kFW, kMP = R::kMfmaPhase;
@@ -540,7 +555,7 @@ __global__ __launch_bounds__(kThreads, TN == 256 ? 1 : 2) void gemm_kernel(const
   }
 
   // ---- epilogue
-  const int mw0 = m0 + wm * 128, nw0 = n0 + wn * (TN / 2);
+  const int mw0 = m0 + wm * 128, nw0 = n0 + wn * (TN / R::kWN);
   // SwiGLU: this wave's 128 stacked rows are the gate rows (fragments 0, 1)
   // and the up rows (fragments 2, 3) of output features nw0/2 .. nw0/2 + 63.
   constexpr bool kSwiglu = EPI == kEpiSwiglu;
@@ -692,46 +707,66 @@ __global__ __launch_bounds__(kThreads, TN == 256 ? 1 : 2) void gemm_kernel(const
   }
 }
 
-template <int WF, int XF, int EPI, int TN>
-void launch_epi(const GemmArgs& a, int out_kind, int out_fmt, dim3 grid, dim3 block, hipStream_t stream) {
+template <int WF, int XF, int EPI, int TN, int WV = 4>
+void launch_epi(const GemmArgs& a, int out_kind, int out_fmt, dim3 grid, hipStream_t stream) {
+  const dim3 block(64 * WV);
   if (out_kind == kOutF32)
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, EPI, kFmtE2M3, TN>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, EPI, kFmtE2M3, TN, WV>), grid, block, 0, stream, a);
   else if (out_kind == kOutBf16)
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, EPI, kFmtE2M3, TN>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, EPI, kFmtE2M3, TN, WV>), grid, block, 0, stream, a);
   else if (out_fmt == kFmtE2M3)
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE2M3, TN>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE2M3, TN, WV>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE3M2, TN>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutMx, EPI, kFmtE3M2, TN, WV>), grid, block, 0, stream, a);
 }
 
 // The 6-bit pairs: every epilogue and output kind.
 template <int WF, int XF>
 hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out_fmt, hipStream_t stream,
                           std::true_type) {
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
   if (a.tile_n == 128) {
+    if (a.waves != 4) return hipErrorInvalidValue;
     if (epilogue == kEpiGeluTanh)
-      launch_epi<WF, XF, kEpiGeluTanh, 128>(a, out_kind, out_fmt, grid, block, stream);
+      launch_epi<WF, XF, kEpiGeluTanh, 128>(a, out_kind, out_fmt, grid, stream);
     else if (epilogue == kEpiNone)
-      launch_epi<WF, XF, kEpiNone, 128>(a, out_kind, out_fmt, grid, block, stream);
+      launch_epi<WF, XF, kEpiNone, 128>(a, out_kind, out_fmt, grid, stream);
     else
       return hipErrorInvalidValue;  // SwiGLU needs 256-feature tiles (rejected before this point)
     return hipGetLastError();
   }
+  if (a.waves == 8) {
+    if (epilogue == kEpiGeluTanh)
+      launch_epi<WF, XF, kEpiGeluTanh, 256, 8>(a, out_kind, out_fmt, grid, stream);
+    else if (epilogue == kEpiNone)
+      launch_epi<WF, XF, kEpiNone, 256, 8>(a, out_kind, out_fmt, grid, stream);
+    else
+      return hipErrorInvalidValue;  // SwiGLU needs 128 weight rows per wave (rejected before this point)
+    return hipGetLastError();
+  }
   if (epilogue == kEpiGeluTanh)
-    launch_epi<WF, XF, kEpiGeluTanh, 256>(a, out_kind, out_fmt, grid, block, stream);
+    launch_epi<WF, XF, kEpiGeluTanh, 256>(a, out_kind, out_fmt, grid, stream);
   else if (epilogue == kEpiSwiglu)
-    launch_epi<WF, XF, kEpiSwiglu, 256>(a, out_kind, out_fmt, grid, block, stream);
+    launch_epi<WF, XF, kEpiSwiglu, 256>(a, out_kind, out_fmt, grid, stream);
   else
-    launch_epi<WF, XF, kEpiNone, 256>(a, out_kind, out_fmt, grid, block, stream);
+    launch_epi<WF, XF, kEpiNone, 256>(a, out_kind, out_fmt, grid, stream);
   return hipGetLastError();
 }
 
 // The 4- and 8-bit operand formats: plain product, fp32 or bf16 output.
 template <int WF, int XF>
 hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int, hipStream_t stream, std::false_type) {
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(kThreads);
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
   if (epilogue != kEpiNone || out_kind == kOutMx || a.tile_n != 256) return hipErrorInvalidValue;
+  if (a.waves == 8) {
+    const dim3 block(Ring<WF, XF, 256, 8>::kThreads);
+    if (out_kind == kOutF32)
+      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, kEpiNone, kFmtE2M3, 256, 8>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutBf16, kEpiNone, kFmtE2M3, 256, 8>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 block(Ring<WF, XF>::kThreads);
   if (out_kind == kOutF32)
     hipLaunchKernelGGL((gemm_kernel<WF, XF, kOutF32, kEpiNone, kFmtE2M3>), grid, block, 0, stream, a);
   else

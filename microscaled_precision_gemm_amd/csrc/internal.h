@@ -73,6 +73,7 @@ struct GemmArgs {
   int32_t group_m;          // tile order: m-tiles per group (1 .. 16)
   int32_t xcd_remap;        // tile order: 1 = contiguous tile ranges per XCD
   int32_t tile_n;           // output features per tile: 256 or 128
+  int32_t waves;            // waves per workgroup: 4 or 8 (tile_n 256)
 };
 
 hipError_t launch_quantize(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,

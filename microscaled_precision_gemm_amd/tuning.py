@@ -7,13 +7,14 @@ candidates on real data.  This module does that for the knobs of mx_gemm that
 are free to choose per shape (``MXGemmConfig``): the order in which output
 tiles are handed to workgroups (group width and XCD remapping), which decides
 which operand stages the tiles in flight share in each XCD's L2, and the tile
-width (256 output features with one workgroup per CU, or 128 with two, which
-pays off where K is short and per-tile fixed costs weigh more).
+shape: 256 output features with 4 waves and one workgroup per CU, 128 with
+two workgroups per CU (pays off where K is short and per-tile fixed costs
+weigh more), or 256 with 8 waves, two per SIMD.
 
 * ``tune_gemm`` times every candidate on the caller's own operands (HIP events
   on the current stream, after a warm-up), requires each candidate's output to
   be bit-identical to the default configuration's (neither the tile order nor
-  the tile width changes the arithmetic: each output takes the same matrix-core
+  the tile shape changes the arithmetic: each output takes the same matrix-core
   sequence over K; the check holds the library to that on the real data), and
   records the fastest, keeping the default unless a candidate beats
   it by more than ``margin``.
@@ -33,16 +34,23 @@ import torch
 
 from .binding import MXGemmConfig, MXTensor, mx_gemm, mx_gemm_default_config
 
-CANDIDATES = ((4, 1, 256), (2, 1, 256), (8, 1, 256), (16, 1, 256), (1, 1, 256), (4, 0, 256), (8, 0, 256),
-              (4, 1, 128), (2, 1, 128), (8, 1, 128), (16, 1, 128))
-FORMAT_VERSION = 2
+# (group_m, xcd_remap, tile_n, waves)
+CANDIDATES = ((4, 1, 256, 4), (2, 1, 256, 4), (8, 1, 256, 4), (16, 1, 256, 4), (1, 1, 256, 4), (4, 0, 256, 4),
+              (8, 0, 256, 4),
+              (4, 1, 128, 4), (2, 1, 128, 4), (8, 1, 128, 4), (16, 1, 128, 4),
+              (4, 1, 256, 8), (2, 1, 256, 8), (8, 1, 256, 8))
+FORMAT_VERSION = 3
 FP6 = ("e2m3", "e3m2")
 
 
-def supports(config: tuple[int, int, int], a_fmt: str, w_fmt: str, epilogue: str) -> bool:
-    """Whether mx_gemm accepts this configuration for the call (128-feature
-    tiles: 6-bit operands without the SwiGLU pairing)."""
-    return config[2] == 256 or (a_fmt in FP6 and w_fmt in FP6 and epilogue != "swiglu")
+def supports(config: tuple[int, int, int, int], a_fmt: str, w_fmt: str, epilogue: str) -> bool:
+    """Whether mx_gemm accepts this configuration for the call: 128-feature
+    tiles take 6-bit operands, and neither they nor 8 waves take the SwiGLU
+    pairing."""
+    _, _, tile_n, waves = config
+    if tile_n == 128:
+        return waves == 4 and a_fmt in FP6 and w_fmt in FP6 and epilogue != "swiglu"
+    return waves == 4 or epilogue != "swiglu"
 
 
 def device_name(device: torch.device | None = None) -> str:
@@ -97,8 +105,8 @@ class TuningTable:
             raise ValueError(f"{path}: unknown tuning table format {data.get('format')!r}")
         for key, e in data["entries"].items():
             cfg = e.get("config")
-            if not (isinstance(cfg, list) and len(cfg) == 3 and 1 <= cfg[0] <= 16 and cfg[1] in (0, 1)
-                    and cfg[2] in (128, 256)):
+            if not (isinstance(cfg, list) and len(cfg) == 4 and 1 <= cfg[0] <= 16 and cfg[1] in (0, 1)
+                    and cfg[2] in (128, 256) and cfg[3] in (4, 8) and not (cfg[2] == 128 and cfg[3] == 8)):
                 raise ValueError(f"{path}: bad entry {key!r}")
         self.entries.update(data["entries"])
 

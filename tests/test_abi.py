@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mx.mx_version() == 300
+    assert mx.mx_version() == 400
     for st in range(-7, 1):
         assert mx.mx_status_string(st) and mx.mx_status_string(st) != "unknown status"
     assert mx.mx_status_string(-99) == "unknown status"
@@ -176,8 +176,9 @@ def test_gemm_config_validation(L):
                 out_fmt=2, ws=NULL, ws_bytes=0)
     d = B.MXGemmConfig()
     L.mx_gemm_default_config(ctypes.byref(d))
-    assert d.key() == (4, 1, 256)
-    for bad in ((0, 1), (17, 1), (4, 2), (4, -1), (4, 1, 64), (4, 1, 0), (4, 1, 512)):
+    assert d.key() == (4, 1, 256, 4)
+    for bad in ((0, 1), (17, 1), (4, 2), (4, -1), (4, 1, 64), (4, 1, 0), (4, 1, 512), (4, 1, 256, 2),
+                (4, 1, 256, 16), (4, 1, 256, 0)):
         c = B.MXGemmConfig(*bad)
         assert L.mx_gemm_with_config(*args.values(), ctypes.byref(c), NULL) == B.MX_ERR_FORMAT
     ok = B.MXGemmConfig(8, 0)
@@ -193,6 +194,15 @@ def test_gemm_config_validation(L):
                                  NULL) == B.MX_ERR_UNSUPPORTED
     assert L.mx_gemm_with_config(*dict(args, a_fmt=0, w_fmt=0).values(), ctypes.byref(narrow),
                                  NULL) == B.MX_ERR_UNSUPPORTED
+    # eight waves: 256-feature tiles of every pair, not SwiGLU, not with 128-feature tiles
+    eight = B.MXGemmConfig(4, 1, 256, 8)
+    assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(eight), NULL) == B.MX_OK
+    assert L.mx_gemm_with_config(*dict(args, m=0, a_fmt=0, w_fmt=0).values(), ctypes.byref(eight),
+                                 NULL) == B.MX_OK
+    assert L.mx_gemm_with_config(*dict(args, epi=2, n=128).values(), ctypes.byref(eight),
+                                 NULL) == B.MX_ERR_UNSUPPORTED
+    narrow8 = B.MXGemmConfig(4, 1, 128, 8)
+    assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(narrow8), NULL) == B.MX_ERR_UNSUPPORTED
 
 
 def sk(**kw):

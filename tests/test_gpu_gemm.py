@@ -14,6 +14,8 @@ from tests.parity import (assert_bf16_close, assert_close_window, assert_fp32_cl
 pytestmark = pytest.mark.gpu
 
 FORMAT_PAIRS = [("e2m3", "e2m3"), ("e2m3", "e3m2"), ("e3m2", "e2m3")]  # (activations, weights)
+NARROW = (4, 1, 128, 4)  # 128-feature tiles, two workgroups per CU
+EIGHT = (4, 1, 256, 8)   # 256-feature tiles, 8 waves (two per SIMD)
 
 
 def _operands(m, n, k, a_fmt, w_fmt, seed=0, a_std=1.0, w_std=0.02, t_outliers=False):
@@ -90,6 +92,10 @@ def test_gemm_fp4_fp8_operands(a_fmt, w_fmt, m, n, k, out_kind):
         else:
             assert_bf16_close(g, c, s, tag)
     assert torch.equal(out, out2)
+    # eight waves per workgroup: the same bytes
+    out8 = mx.mx_gemm(aq, wq, out_kind=out_kind, config=EIGHT)
+    torch.cuda.synchronize()
+    assert torch.equal(out8, out2)
 
 
 def _window_case(rows, fmt):
@@ -179,38 +185,36 @@ def test_gemm_gelu_f32_output(a_fmt, w_fmt):
     assert bad.size == 0, f"{len(bad)} GELU outputs off; first {bad[0].tolist()}"
 
 
-NARROW = (4, 1, 128)  # 128-feature tiles, two workgroups per CU
-
-
+@pytest.mark.parametrize("cfg", [NARROW, EIGHT], ids=["tile128", "waves8"])
 @pytest.mark.parametrize("a_fmt,w_fmt", FORMAT_PAIRS)
 @pytest.mark.parametrize("m,n,k", [(300, 544, 416), (37, 288, 160), (512, 384, 640)])
-def test_gemm_narrow_tiles(a_fmt, w_fmt, m, n, k):
-    """The 128-feature tile: plain fp32 / bf16 outputs against the oracle,
-    ragged in M and N, and bit-identical to the 256-feature tile (each output
-    takes the same matrix-core sequence over K), for every output kind and
-    both epilogues it serves."""
+def test_gemm_other_tile_shapes(a_fmt, w_fmt, m, n, k, cfg):
+    """The 128-feature tile and the 8-wave 256-feature tile: plain fp32 / bf16
+    outputs against the oracle, ragged in M and N, and bit-identical to the
+    default 4-wave 256-feature tile (each output takes the same matrix-core
+    sequence over K), for every output kind and both epilogues they serve."""
     a, w, qa, qw, c, s = _operands(m, n, k, a_fmt, w_fmt, seed=3 * m + n + k)
-    say(f"gemm narrow tiles {m}x{n}x{k} a={a_fmt} w={w_fmt}")
+    say(f"gemm tile shape {cfg} {m}x{n}x{k} a={a_fmt} w={w_fmt}")
     wq = _gpu_weights(w, w_fmt, qw)
     aq = mx.mx_quantize(a.cuda(), a_fmt)
     for out_kind in ("f32", "bf16"):
-        o = mx.mx_gemm(aq, wq, out_kind=out_kind, config=NARROW)
-        o_in = mx.mx_gemm(a.cuda(), wq, out_kind=out_kind, a_fmt=a_fmt, config=NARROW)
+        o = mx.mx_gemm(aq, wq, out_kind=out_kind, config=cfg)
+        o_in = mx.mx_gemm(a.cuda(), wq, out_kind=out_kind, a_fmt=a_fmt, config=cfg)
         wide = mx.mx_gemm(aq, wq, out_kind=out_kind)
         torch.cuda.synchronize()
         g = o.float().cpu().numpy().astype(np.float64)
-        (assert_fp32_close if out_kind == "f32" else assert_bf16_close)(g, c, s, f"narrow {out_kind}")
+        (assert_fp32_close if out_kind == "f32" else assert_bf16_close)(g, c, s, f"{cfg} {out_kind}")
         assert torch.equal(o, wide) and torch.equal(o, o_in)
     for epi in ("gelu_tanh", "none"):
         for out_kind in ("f32", "mx"):
-            o = mx.mx_gemm(aq, wq, out_kind=out_kind, epilogue=epi, config=NARROW)
+            o = mx.mx_gemm(aq, wq, out_kind=out_kind, epilogue=epi, config=cfg)
             wide = mx.mx_gemm(aq, wq, out_kind=out_kind, epilogue=epi)
             torch.cuda.synchronize()
             if out_kind == "mx":
                 assert torch.equal(o.codes, wide.codes) and torch.equal(o.scales, wide.scales)
             else:
                 assert torch.equal(o, wide)
-    o = mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", out_fmt="e3m2", config=NARROW)
+    o = mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", out_fmt="e3m2", config=cfg)
     torch.cuda.synchronize()
     oc, os_ = mx_rows_view(o)
     stats = check_mx_epilogue(oc, os_, c, s, True, "e3m2")

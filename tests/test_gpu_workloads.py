@@ -110,8 +110,8 @@ def test_fc1_full_size_gelu_mx():
     """fc1 20480 x 3072 x 12288 with the GELU-tanh -> E2M3 epilogue: sampled
     token rows x sampled whole 32-feature blocks, under the boundary-aware
     rule (one element step at a rounding midpoint, one scale step at a power
-    of two, only within the fp32 accumulation and GELU error).  Both tile
-    widths the tuner chooses between for this shape give the same bytes."""
+    of two, only within the fp32 accumulation and GELU error).  Every tile
+    shape the tuner chooses between for this shape gives the same bytes."""
     w = syn.WORKLOADS["fc1"]
     a, wt = syn.make_a(w), syn.make_w(w)
     rng = np.random.default_rng([78, w.index])
@@ -124,10 +124,11 @@ def test_fc1_full_size_gelu_mx():
     wq = mx.mx_quantize(wt.to(dev), w.w_fmt)
     h = mx.MXTensor.empty(w.m, w.n, "e2m3", "tiled", dev)
     mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", out=h)
-    h_narrow = mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", config=(4, 1, 128))
-    torch.cuda.synchronize()
-    assert torch.equal(h.codes, h_narrow.codes) and torch.equal(h.scales, h_narrow.scales)
-    del h_narrow
+    for cfg in ((4, 1, 128, 4), (4, 1, 256, 8)):
+        h_other = mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", config=cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(h.codes, h_other.codes) and torch.equal(h.scales, h_other.scales), cfg
+        del h_other
     gc, gs = mx_rows_view(h)
     codes_g = O.unpack(gc[rows], w.n)[:, cols]
     scales_g = gs[rows][:, blocks]

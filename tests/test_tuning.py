@@ -22,27 +22,33 @@ def test_key_names_every_dimension():
 def test_save_load_round_trip(tmp_path):
     t = T.TuningTable()
     key = T.gemm_key(256, 512, 1024, "e2m3", "e2m3", "none", "bf16", "e2m3", "devX")
-    t.record(key, {"config": [8, 1, 128], "us": 12.5, "default_us": 13.0,
-                   "candidates": {"4,1,256": 13.0, "8,1,128": 12.5}})
+    t.record(key, {"config": [8, 1, 128, 4], "us": 12.5, "default_us": 13.0,
+                   "candidates": {"4,1,256,4": 13.0, "8,1,128,4": 12.5}})
     p = t.save(str(tmp_path / "sub" / "tuning.json"))
     u = T.TuningTable(p)
-    assert u.lookup(256, 512, 1024, device="devX").key() == (8, 1, 128)
+    assert u.lookup(256, 512, 1024, device="devX").key() == (8, 1, 128, 4)
     assert u.lookup(256, 512, 1024, device="other") is None  # entries are per device
     assert u.lookup(256, 512, 2048, device="devX") is None  # untuned shape: library default
 
 
 def test_candidates_the_call_supports():
-    # 128-feature tiles exist for the 6-bit pairs without SwiGLU only
-    assert T.supports((4, 1, 128), "e2m3", "e3m2", "gelu_tanh")
-    assert not T.supports((4, 1, 128), "e2m3", "e2m3", "swiglu")
-    assert not T.supports((4, 1, 128), "e4m3", "e4m3", "none")
-    assert T.supports((4, 1, 256), "e2m1", "e2m1", "none")
-    assert T.CANDIDATES[0] == (4, 1, 256) and {c[2] for c in T.CANDIDATES} == {128, 256}
+    # 128-feature tiles exist for the 6-bit pairs without SwiGLU only; 8 waves
+    # for 256-feature tiles of every pair, without SwiGLU
+    assert T.supports((4, 1, 128, 4), "e2m3", "e3m2", "gelu_tanh")
+    assert not T.supports((4, 1, 128, 4), "e2m3", "e2m3", "swiglu")
+    assert not T.supports((4, 1, 128, 4), "e4m3", "e4m3", "none")
+    assert not T.supports((4, 1, 128, 8), "e2m3", "e2m3", "none")
+    assert T.supports((4, 1, 256, 4), "e2m1", "e2m1", "none")
+    assert T.supports((4, 1, 256, 8), "e4m3", "e5m2", "none")
+    assert T.supports((4, 1, 256, 4), "e2m3", "e2m3", "swiglu")
+    assert not T.supports((4, 1, 256, 8), "e2m3", "e2m3", "swiglu")
+    assert T.CANDIDATES[0] == (4, 1, 256, 4)
+    assert {(c[2], c[3]) for c in T.CANDIDATES} == {(256, 4), (128, 4), (256, 8)}
 
 
 def test_load_rejects_bad_entries(tmp_path):
     p = tmp_path / "bad.json"
-    for cfg in ([0, 1, 256], [4, 1, 64], [4, 1]):
+    for cfg in ([0, 1, 256, 4], [4, 1, 64, 4], [4, 1, 256], [4, 1, 128, 8], [4, 1, 256, 6]):
         p.write_text(json.dumps({"format": T.FORMAT_VERSION, "entries": {"k": {"config": cfg}}}))
         with pytest.raises(ValueError):
             T.TuningTable(str(p))
@@ -61,7 +67,8 @@ def test_tune_real_call_and_apply(tmp_path):
     say("tuning 2048x512x2048 gelu->mx")
     table = T.TuningTable(str(tmp_path / "t.json"))
     entry = T.tune_gemm(table, a, w, out_kind="mx", epilogue="gelu_tanh", iters=3, rounds=2)
-    assert set(entry["candidates"]) >= {"4,1,256", "8,1,256", "1,1,256", "4,0,256", "4,1,128"}
+    assert set(entry["candidates"]) >= {"4,1,256,4", "8,1,256,4", "1,1,256,4", "4,0,256,4", "4,1,128,4",
+                                        "4,1,256,8"}
     cfg = table.lookup(m, n, k, epilogue="gelu_tanh", out_kind="mx")
     assert cfg is not None and cfg.key() == tuple(entry["config"])
     got = table.gemm(a, w, out_kind="mx", epilogue="gelu_tanh")
@@ -77,3 +84,5 @@ def test_tune_real_call_and_apply(tmp_path):
         mx.mx_gemm(a, w, out_kind="bf16", config=(4, 2))
     with pytest.raises(mx.MXError):
         mx.mx_gemm(a, w, out_kind="bf16", config=(4, 1, 64))
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm(a, w, out_kind="bf16", config=(4, 1, 128, 8))
