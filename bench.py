@@ -41,13 +41,13 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 names of the two GEMM instantiations <W fmt, A fmt, out kind, epilogue, out fmt>
 # (E2M3 x E2M3; fc1: MX out + GELU, fc2: bf16 out, no epilogue)
 # demangled GEMM kernel names: gemm_kernel<weights, activations, output kind, epilogue,
-# output format, tile width>; fc1 = E2M3 x E2M3 -> GELU-tanh -> MX E2M3, fc2 = -> bf16
+# output format, tile width, waves>; fc1 = E2M3 x E2M3 -> GELU-tanh -> MX E2M3, fc2 = -> bf16
 KERNEL_PREFIX = {"fc1": "gemm_kernel<2, 2, 2, 1, 2", "fc2": "gemm_kernel<2, 2, 1, 0, 2"}
 
 
 def kernel_name(gemm: str, config) -> str:
-    tile_n = 256 if config is None else int(config.tile_n)
-    return f"{KERNEL_PREFIX[gemm]}, {tile_n}>"
+    tile_n, waves = (256, 4) if config is None else (int(config.tile_n), int(config.waves))
+    return f"{KERNEL_PREFIX[gemm]}, {tile_n}, {waves}>"
 # the sources the GEMM kernel is built from: measured HBM traffic is only reported
 # while they are unchanged since the counters were taken
 GEMM_SOURCES = ["gemm_kernel.h", "internal.h", "mx_device.h", "gemm_we2m3_e2m3.hip"]
