@@ -148,7 +148,7 @@ def bench_mlp(table, steps: int, warmup: int, tune: bool = True):
     }
 
 
-def bench_swiglu_mlp(steps: int, warmup: int):
+def bench_swiglu_mlp(table, steps: int, warmup: int):
     """The SwiGLU variant of the MLP step (the activation the Krea 3 post names):
     quantize x, stacked gate/up GEMM 20480 x 3072 x 16384 with SwiGLU -> E2M3
     (8192 features), down projection 20480 x 8192 x 3072 to bf16."""
@@ -162,6 +162,9 @@ def bench_swiglu_mlp(steps: int, warmup: int):
     xq = mx.MXTensor.empty(m, d, "e2m3", "tiled", dev)
     h = mx.MXTensor.empty(m, hdim, "e2m3", "tiled", dev)
     y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
+    # launch configurations from the tuning table where it has these shapes
+    cfg1 = table.lookup(m, n1, d, epilogue="swiglu", out_kind="mx")
+    cfg2 = table.lookup(m, d, hdim, epilogue="none", out_kind="bf16")
 
     def step(ev=None):
         if ev is not None:
@@ -169,10 +172,10 @@ def bench_swiglu_mlp(steps: int, warmup: int):
         mx.mx_quantize(x, "e2m3", "tiled", out=xq)
         if ev is not None:
             ev[1].record()
-        mx.mx_gemm(xq, w1, out_kind="mx", epilogue="swiglu", out=h)
+        mx.mx_gemm(xq, w1, out_kind="mx", epilogue="swiglu", out=h, config=cfg1)
         if ev is not None:
             ev[2].record()
-        mx.mx_gemm(h, w2, out_kind="bf16", out=y)
+        mx.mx_gemm(h, w2, out_kind="bf16", out=y, config=cfg2)
         if ev is not None:
             ev[3].record()
 
@@ -193,7 +196,8 @@ def bench_swiglu_mlp(steps: int, warmup: int):
                         "features), down 20480x8192x3072 (bf16 out)",
             "ms_per_step": round(wall * 1e3 / steps, 4), "tflops": round((fl1 + fl2) / (wall / steps) / 1e12, 1),
             "fc1_ms": round(float(f1), 4), "fc1_tflops": round(fl1 / f1 / 1e9, 1),
-            "fc2_ms": round(float(f2), 4), "fc2_tflops": round(fl2 / f2 / 1e9, 1)}
+            "fc2_ms": round(float(f2), 4), "fc2_tflops": round(fl2 / f2 / 1e9, 1),
+            "configs": [list(c.key()) if c is not None else None for c in (cfg1, cfg2)]}
 
 
 PEAK_BY_FMT = {"e2m3": 10100.0, "e2m1": 10100.0, "e4m3": 5000.0, "e5m2": 5000.0}
@@ -378,9 +382,11 @@ def main():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skinny-iters", type=int, default=100)
-    p.add_argument("--no-tune", action="store_true", help="use the default tile order and width instead of tuning")
-    p.add_argument("--tuning-table", default=None,
-                   help="JSON tuning table: read the MLP's configurations from it, or tune and save them there")
+    p.add_argument("--no-tune", action="store_true", help="use the library's default launch configuration")
+    p.add_argument("--tuning-table", default=tuning.SHIPPED_TABLE,
+                   help="JSON tuning table to read the GEMM configurations from (default: the table shipped "
+                        "with the package); shapes it lacks for this device are tuned here, untimed")
+    p.add_argument("--save-tuning", default=None, help="write the resulting tuning table to this path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = p.parse_args()
@@ -391,7 +397,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
 
-    table = tuning.TuningTable(args.tuning_table)
+    table = tuning.TuningTable(args.tuning_table if args.tuning_table and os.path.exists(args.tuning_table) else None)
     r = bench_mlp(table, args.steps, args.warmup, tune=not args.no_tune)
     ms_step = r["wall_ms_per_step"]
     value = r["flops_per_step"] / ms_step / 1e9  # TFLOP/s
@@ -400,11 +406,11 @@ def main():
     dom_ms = r[f"{dom}_ms"]
     achieved = r["flops_per_gemm"] / dom_ms / 1e9
     skinny = [bench_skinny(16, 16, args.skinny_iters), bench_skinny(8, 16, args.skinny_iters)]
-    swiglu = bench_swiglu_mlp(args.steps, args.warmup)
+    swiglu = bench_swiglu_mlp(table if not args.no_tune else tuning.TuningTable(), args.steps, args.warmup)
     producer = bench_producer()
     formats = bench_formats(table, tune=not args.no_tune)
-    if args.tuning_table and not args.no_tune:
-        table.save()
+    if args.save_tuning and not args.no_tune:
+        table.save(args.save_tuning)
     line = {
         "metric": METRIC,
         "value": round(value, 2),

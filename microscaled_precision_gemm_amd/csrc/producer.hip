@@ -15,12 +15,13 @@
 //
 //  * one workgroup (4 waves) per 32-row group.  Pass 1: each wave reduces the
 //    sum of squares of 8 rows with 16-byte loads (consecutive lanes on
-//    consecutive bytes, four loads in flight) and a wave-wide shuffle
+//    consecutive bytes, up to eight loads in flight) and a wave-wide shuffle
 //    reduction, and parks 1/rms in LDS.  Pass 2: the waves take the group's
 //    128-element stages in turn, exactly as the tiled quantizer does (the chunk
 //    of 32 rows x 128 is staged through LDS so each lane owns two whole
-//    blocks of one row), apply the norm and the modulation in fp32 and convert
-//    with v_cvt_scalef32_2xpk16 (round to nearest even, saturating).
+//    blocks of one row, and the wave's next chunk is loaded while this one is
+//    converted), apply the norm and the modulation in fp32 and convert with
+//    v_cvt_scalef32_2xpk16 (round to nearest even, saturating).
 //  * the second read of the group's rows comes from the caches: a group is
 //    32 rows (192 KB for d = 3072) and was streamed just before.
 //  * all rows of a group share one conditioning row (rows_per_cond is a
@@ -35,6 +36,7 @@ namespace {
 
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
+constexpr int kPass1Loads = 8;  // 16-byte loads per lane in flight in pass 1 (a 3072-wide bf16 row: 6)
 
 template <bool F32>
 struct PLayout {
@@ -86,16 +88,16 @@ __global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const Produ
     float ss = 0.0f;
     if (row < a.rows) {
       const uint8_t* xr = src + (int64_t)row * a.ld_bytes;
-      for (int k0 = 0; k0 < d; k0 += 4 * kSpan) {
-        u32x4 w[4];
+      for (int k0 = 0; k0 < d; k0 += kPass1Loads * kSpan) {
+        u32x4 w[kPass1Loads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kPass1Loads; ++u) {
           const int e = k0 + u * kSpan + lane * kElemsPerLoad;
           // plain (cached) loads: pass 2 reads the same rows again
           w[u] = e < d ? *reinterpret_cast<const u32x4*>(xr + (int64_t)e * L::kEsize) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kPass1Loads; ++u) {
           float f[4 * (F32 ? 1 : 2)];
           piece_to_f32<F32>(w[u], f);
 #pragma unroll
@@ -118,18 +120,30 @@ __global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const Produ
   const int j = lane & 31, h = lane >> 5;
   const int row = grp * 32 + j;
   const float inv = lds_inv[j];
-  for (int stage = wave; stage < stages; stage += kPWaves) {
+  // the chunk of 32 rows x 128 elements of stage `stage`, 16 bytes per lane and load
+  auto load = [&](int stage, u32x4 (&v)[L::kCopies]) {
 #pragma unroll
     for (int i = 0; i < L::kCopies; ++i) {
       const int c = 64 * i + lane;
       const int jr = c / L::kPieces, piece = c % L::kPieces;
       const int r = grp * 32 + jr;
       const int e = stage * kTileStageK + piece * (16 / L::kEsize);
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      v[i] = u32x4{0u, 0u, 0u, 0u};
       if (r < a.rows && e < d)
-        v = *reinterpret_cast<const u32x4*>(src + (int64_t)r * a.ld_bytes + (int64_t)e * L::kEsize);
-      *reinterpret_cast<u32x4*>(in + jr * L::kRow + piece * 16) = v;
+        v[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * a.ld_bytes + (int64_t)e * L::kEsize);
     }
+  };
+  u32x4 v[L::kCopies];
+  if (wave < stages) load(wave, v);
+  for (int stage = wave; stage < stages; stage += kPWaves) {
+#pragma unroll
+    for (int i = 0; i < L::kCopies; ++i) {
+      const int c = 64 * i + lane;
+      const int jr = c / L::kPieces, piece = c % L::kPieces;
+      *reinterpret_cast<u32x4*>(in + jr * L::kRow + piece * 16) = v[i];
+    }
+    // the wave's next stage is in flight while this one is converted
+    if (stage + kPWaves < stages) load(stage + kPWaves, v);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int k = stage * kTileStageK + 2 * lane + t;

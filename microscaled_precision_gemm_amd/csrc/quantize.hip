@@ -17,6 +17,8 @@
 //  * stores: the 64 blocks' code bytes of a wave are contiguous in the output,
 //    so they go back through LDS and leave as 16-byte stores of consecutive
 //    lanes.
+#include <algorithm>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -174,6 +176,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint8_t* __re
 // operands).  Rows >= rows and blocks >= K/32 are written as padding (codes
 // 0, scale 127).
 constexpr int kTWaves = 4;
+// workgroups resident at once on gfx950: 256 CUs x 4 (the 34 KB LDS each allows)
+constexpr int64_t kTResident = 256 * 4;
 
 template <bool F32>
 struct TLayout {
@@ -193,76 +197,99 @@ __global__ __launch_bounds__(kTWaves * 64) void quantize_tiled_kernel(const uint
   using L = TLayout<F32>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kTWaves * 32 * L::kRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // Waves walk the chunks group by group (all stages of rows 32g .. 32g+31,
-  // then the next group), so the waves in flight read long runs of each row
-  // rather than one 256-byte piece of every row.
-  const int work = blockIdx.x * kTWaves + wave;
+  // Each wave converts chunks work, work + nwaves, ... in the group-major order
+  // (all stages of rows 32g .. 32g+31, then the next group), so the waves in
+  // flight read long runs of each row.  The next chunk's loads are issued
+  // before the current one is converted, so every wave keeps a chunk of loads
+  // in flight: the grid holds only as many workgroups as are resident at once.
+  const int nwaves = gridDim.x * kTWaves;
+  int work = blockIdx.x * kTWaves + wave;
   if (work >= nchunks) return;  // wave-level only: no workgroup barrier below
   const int stages = nchunks / groups;
-  const int grp = work / stages, stage = work - grp * stages;
-  const int chunk = stage * groups + grp;
   uint8_t* in = lds + wave * 32 * L::kRow;
   const int kblocks = k / 32;
-
-#pragma unroll
-  for (int i = 0; i < L::kCopies; ++i) {
-    const int c = 64 * i + lane;
-    const int jr = c / L::kPieces, piece = c % L::kPieces;
-    const int row = grp * 32 + jr;
-    const int blk = stage * 4 + piece * 16 / L::kBlockSrc;  // block this 16-byte piece belongs to
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (row < rows && blk < kblocks)
-      v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          src + (int64_t)row * ld_bytes + (int64_t)stage * 4 * L::kBlockSrc + piece * 16));
-    *reinterpret_cast<u32x4*>(in + jr * L::kRow + piece * 16) = v;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-
   constexpr int kBits = fmt_bits(FMT);
   const int j = lane & 31, h = lane >> 5;
-  const int row = grp * 32 + j;
-  uint32_t q[2][kBits];
-  uint32_t sb[2];
+
+  // loads of chunk `w` (group-major order) into registers
+  auto load = [&](int w, u32x4 (&v)[L::kCopies]) {
+    const int grp = w / stages, stage = w - grp * stages;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int qb = 2 * h + t;
-    const uint8_t* p = in + j * L::kRow + qb * L::kBlockSrc;
-    u32x4 w[F32 ? 8 : 4];
-#pragma unroll
-    for (int i = 0; i < (F32 ? 8 : 4); ++i) w[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
-    sb[t] = quantize_block<FMT, F32>(w, q[t]);
-    if (row >= rows || stage * 4 + qb >= kblocks) {  // padding
-#pragma unroll
-      for (int i = 0; i < kBits; ++i) q[t][i] = 0u;
-      sb[t] = 127u;
+    for (int i = 0; i < L::kCopies; ++i) {
+      const int c = 64 * i + lane;
+      const int jr = c / L::kPieces, piece = c % L::kPieces;
+      const int row = grp * 32 + jr;
+      const int blk = stage * 4 + piece * 16 / L::kBlockSrc;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (row < rows && blk < kblocks)
+        v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            src + (int64_t)row * ld_bytes + (int64_t)stage * 4 * L::kBlockSrc + piece * 16));
     }
+  };
+  u32x4 v[L::kCopies];
+  load(work, v);
+  for (;;) {
+    const int grp = work / stages, stage = work - grp * stages;
+    const int chunk = stage * groups + grp;
+#pragma unroll
+    for (int i = 0; i < L::kCopies; ++i) {
+      const int c = 64 * i + lane;
+      const int jr = c / L::kPieces, piece = c % L::kPieces;
+      *reinterpret_cast<u32x4*>(in + jr * L::kRow + piece * 16) = v[i];
+    }
+    const int next = work + nwaves;
+    if (next < nchunks) load(next, v);  // in flight while this chunk is converted
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    const int row = grp * 32 + j;
+    uint32_t q[2][kBits];
+    uint32_t sb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int qb = 2 * h + t;
+      const uint8_t* p = in + j * L::kRow + qb * L::kBlockSrc;
+      u32x4 w[F32 ? 8 : 4];
+#pragma unroll
+      for (int i = 0; i < (F32 ? 8 : 4); ++i) w[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
+      sb[t] = quantize_block<FMT, F32>(w, q[t]);
+      if (row >= rows || stage * 4 + qb >= kblocks) {  // padding
+#pragma unroll
+        for (int i = 0; i < kBits; ++i) q[t][i] = 0u;
+        sb[t] = 127u;
+      }
+    }
+    // every lane has read its blocks: the next chunk may overwrite the wave's LDS rows
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // the code bytes of row j in the planes of half h
+    uint8_t* half = codes + (int64_t)chunk * chunk_codes(kBits) + h * half_codes(kBits);
+    if constexpr (kBits == 6) {
+      *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
+      *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
+      *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
+      *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
+    } else if constexpr (kBits == 4) {
+      // 16-byte planes: block 2h, then block 2h+1
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<u32x4*>(half + t * kPlaneStride16 + j * 16) = u32x4{q[t][0], q[t][1], q[t][2], q[t][3]};
+    } else {
+      // 8 bits: block q = 2h + t goes to plane 2t + h of both halves, its bytes
+      // 0..15 in half 0 and 16..31 in half 1
+      uint8_t* chunk_base = codes + (int64_t)chunk * chunk_codes(kBits);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          *reinterpret_cast<u32x4*>(chunk_base + hh * half_codes(kBits) + (2 * t + h) * kPlaneStride16 + j * 16) =
+              u32x4{q[t][4 * hh], q[t][4 * hh + 1], q[t][4 * hh + 2], q[t][4 * hh + 3]};
+    }
+    *reinterpret_cast<uint16_t*>(scales + (int64_t)chunk * kChunkScales + j * 4 + 2 * h) =
+        (uint16_t)(sb[0] | (sb[1] << 8));
+    if (next >= nchunks) break;
+    work = next;
   }
-  // the code bytes of row j in the planes of half h
-  uint8_t* half = codes + (int64_t)chunk * chunk_codes(kBits) + h * half_codes(kBits);
-  if constexpr (kBits == 6) {
-    *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
-    *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
-    *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
-    *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
-  } else if constexpr (kBits == 4) {
-    // 16-byte planes: block 2h, then block 2h+1
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      *reinterpret_cast<u32x4*>(half + t * kPlaneStride16 + j * 16) = u32x4{q[t][0], q[t][1], q[t][2], q[t][3]};
-  } else {
-    // 8 bits: block q = 2h + t goes to plane 2t + h of both halves, its bytes
-    // 0..15 in half 0 and 16..31 in half 1
-    uint8_t* chunk_base = codes + (int64_t)chunk * chunk_codes(kBits);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        *reinterpret_cast<u32x4*>(chunk_base + hh * half_codes(kBits) + (2 * t + h) * kPlaneStride16 + j * 16) =
-            u32x4{q[t][4 * hh], q[t][4 * hh + 1], q[t][4 * hh + 2], q[t][4 * hh + 3]};
-  }
-  *reinterpret_cast<uint16_t*>(scales + (int64_t)chunk * kChunkScales + j * 4 + 2 * h) =
-      (uint16_t)(sb[0] | (sb[1] << 8));
 }
 
 template <int FMT>
@@ -315,7 +342,7 @@ hipError_t launch_quantize_tiled(const void* src, int src_type, int64_t rows, in
   const int64_t groups = ceil_div(rows, kTileGroupRows), stages = ceil_div(k, kTileStageK);
   const int64_t nchunks = groups * stages;
   if (nchunks == 0) return hipSuccess;
-  const dim3 g((unsigned)ceil_div(nchunks, kTWaves)), blk(kTWaves * 64);
+  const dim3 g((unsigned)std::min<int64_t>(ceil_div(nchunks, kTWaves), kTResident)), blk(kTWaves * 64);
   const uint8_t* s = static_cast<const uint8_t*>(src);
   const int64_t ldb = ld_src * (src_type == kSrcBf16 ? 2 : 4);
   const bool f32 = src_type == kSrcF32;

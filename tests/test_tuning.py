@@ -86,3 +86,21 @@ def test_tune_real_call_and_apply(tmp_path):
         mx.mx_gemm(a, w, out_kind="bf16", config=(4, 1, 64))
     with pytest.raises(mx.MXError):
         mx.mx_gemm(a, w, out_kind="bf16", config=(4, 1, 128, 8))
+
+
+def test_shipped_table_covers_the_workloads():
+    """The table shipped with the package loads, is keyed for gfx950, and holds
+    a valid configuration for every GEMM shape the bench runs."""
+    t = T.TuningTable(T.SHIPPED_TABLE)
+    dev = "gfx950/256cu"
+    calls = [dict(m=20480, n=12288, k=3072, epilogue="gelu_tanh", out_kind="mx"),
+             dict(m=20480, n=3072, k=12288),
+             dict(m=20480, n=16384, k=3072, epilogue="swiglu", out_kind="mx"),
+             dict(m=20480, n=3072, k=8192),
+             dict(m=4096, n=3072, k=3072)]
+    calls += [dict(m=20480, n=12288, k=3072, a_fmt=f, w_fmt=f) for f in ("e2m3", "e2m1", "e4m3")]
+    for c in calls:
+        cfg = t.lookup(device=dev, **c)
+        assert cfg is not None, c
+        af, wf, epi = c.get("a_fmt", "e2m3"), c.get("w_fmt", "e2m3"), c.get("epilogue", "none")
+        assert T.supports(cfg.key(), af, wf, epi), (c, cfg.key())
