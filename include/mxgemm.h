@@ -262,11 +262,12 @@ typedef struct {
   int32_t group_m;   /* m-tiles per group of the tile walk, 1 .. 16 (default 4)             */
   int32_t xcd_remap; /* 1: each XCD walks a contiguous range of the grouped order (default);
                         0: tiles in plain grouped order, dealt round-robin to the XCDs        */
-  int32_t tile_n;    /* output features per tile: 256 (default; 4 waves of 128 x 128, one
-                        workgroup per CU) or 128 (4 waves of 128 x 64 and a two-slot LDS
-                        ring, two workgroups per CU, so one's prologue, waits and epilogue
-                        overlap the other's matrix work; the 6-bit format pairs with
-                        MX_EPI_NONE or MX_EPI_GELU_TANH only, else MX_ERR_UNSUPPORTED)      */
+  int32_t tile_n;    /* weight rows per tile (output features; with MX_EPI_SWIGLU stacked
+                        gate/up rows, i.e. twice the output features): 256 (default; 4 waves
+                        of 128 x 128, one workgroup per CU) or 128 (4 waves of 128 x 64 and a
+                        two-slot LDS ring, two workgroups per CU, so one's prologue, waits and
+                        epilogue overlap the other's matrix work; the 6-bit format pairs
+                        only, else MX_ERR_UNSUPPORTED)                                      */
   int32_t waves;     /* waves per workgroup: 4 (default) or, with tile_n = 256, 8 (2 x 4 waves
                         of 128 x 64, two per SIMD, sharing the tile's operand ring; any format
                         pair, not MX_EPI_SWIGLU, else MX_ERR_UNSUPPORTED)                     */

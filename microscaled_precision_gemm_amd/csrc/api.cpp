@@ -217,8 +217,8 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   if (epilogue == MX_EPI_SWIGLU && n % 128 != 0) return MX_ERR_UNSUPPORTED;
   // the 4- and 8-bit operand formats have the plain product with fp32 / bf16 output
   if (!fp6_fmt(w_fmt) && (epilogue != MX_EPI_NONE || out_kind == MX_OUT_MX)) return MX_ERR_UNSUPPORTED;
-  // 128-feature tiles: the 6-bit pairs without the SwiGLU pairing
-  if (cfg.tile_n == 128 && (!fp6_fmt(w_fmt) || epilogue == MX_EPI_SWIGLU)) return MX_ERR_UNSUPPORTED;
+  // 128-feature tiles: the 6-bit pairs
+  if (cfg.tile_n == 128 && !fp6_fmt(w_fmt)) return MX_ERR_UNSUPPORTED;
   // eight waves: 256-feature tiles, not the SwiGLU pairing
   if (cfg.waves == 8 && (cfg.tile_n != 256 || epilogue == MX_EPI_SWIGLU)) return MX_ERR_UNSUPPORTED;
   const int64_t n_out = epilogue == MX_EPI_SWIGLU ? n / 2 : n;

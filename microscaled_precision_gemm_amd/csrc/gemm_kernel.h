@@ -66,11 +66,12 @@ static_assert(kStageScales == 4 * 64 * 4, "one 4-byte copy per lane per wave cov
 // free from the middle of stage ks on, and the copies have a whole stage of
 // matrix work to land).
 //
-// TN is the tile's width in output features: 256 (4 waves of 128 x 128, 256
-// accumulator registers each, one workgroup per CU) or 128 (4 waves of
-// 128 x 64, 128 accumulators, and a two-slot ring of 37.5 KB slots, so that
-// two workgroups share a CU and one's waits, prologue and epilogue overlap
-// the other's matrix work).  WV is the number of waves: 4 (2 x 2 waves over
+// TN is the tile's width in weight rows (output features, or for SwiGLU
+// stacked gate/up rows): 256 (4 waves of 128 x 128, 256 accumulator
+// registers each, one workgroup per CU) or 128 (4 waves of 128 x 64, 128
+// accumulators, and a two-slot ring of 37.5 KB slots, so that two workgroups
+// share a CU and one's waits, prologue and epilogue overlap the other's
+// matrix work).  WV is the number of waves: 4 (2 x 2 waves over
 // the tile) or, for TN = 256, 8 (2 x 4 waves of 128 x 64, two waves per
 // SIMD sharing the three-slot ring; each wave issues half the copies, and
 // its one scale copy is the activations' (waves 0-3) or the weights'
@@ -233,7 +234,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int WF, int XF, int OUT, int EPI, int OFMT, int TN = 256, int WV = 4>
 __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const GemmArgs g) {
   using R = Ring<WF, XF, TN, WV>;
-  static_assert((TN == 256 && WV == 4) || EPI != kEpiSwiglu, "the SwiGLU pairing needs 128 weight rows per wave");
+  static_assert(WV == 4 || EPI != kEpiSwiglu, "the SwiGLU pairing takes 4 waves");
+  constexpr bool kSwiglu = EPI == kEpiSwiglu;
+  // SwiGLU on 128-feature tiles: the tile's 128 weight rows are one run of 64
+  // gate rows and the 64 up rows of the same features, so wave wn takes gate
+  // group wn and up group 2 + wn as its two fragments (32 output features).
+  constexpr bool kSwNarrow = kSwiglu && TN == 128;
   __shared__ __attribute__((aligned(16))) uint8_t lds[R::kLds];
   constexpr int kLayout = OUT == kOutMx ? kLayoutMx : kLayoutContig;
 
@@ -314,11 +320,14 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
   const int h = lane >> 5, j = lane & 31;
   const int wrow = feature_of_row<kLayout>(j);
   constexpr int kFW = R::kFW, kMP = R::kMfmaPhase;
-  const int w16 = R::kOffW + wn * kFW * R::kChunkW + h * R::kHalfW + wrow * 16;
+  // chunk of the wave's first weight fragment (in units of kWaveChunksW) and
+  // the chunk stride between its fragments
+  constexpr int kWaveChunksW = kSwNarrow ? 1 : kFW, kFragChunksW = kSwNarrow ? 2 : 1;
+  const int w16 = R::kOffW + wn * kWaveChunksW * R::kChunkW + h * R::kHalfW + wrow * 16;
   const int x16 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 16;
-  const int w8 = R::kOffW + wn * kFW * R::kChunkW + h * R::kHalfW + wrow * 8;
+  const int w8 = R::kOffW + wn * kWaveChunksW * R::kChunkW + h * R::kHalfW + wrow * 8;
   const int x8 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 8;
-  const int wsc = R::kOffWs + wn * kFW * kChunkScales + wrow * 4 + 2 * h;
+  const int wsc = R::kOffWs + wn * kWaveChunksW * kChunkScales + wrow * 4 + 2 * h;
   const int xsc = R::kOffXs + wm * 4 * kChunkScales + j * 4 + 2 * h;
 
   v16f acc[kFW][4];
@@ -384,7 +393,8 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
     constexpr int I = decltype(i_tag)::value;
     constexpr int F = frag_index(I);
     if constexpr (frag_is_w(I))
-      r.w[F] = op(bw_t{}, sub_tag, so + w16 + F * R::kChunkW, so + w8 + F * R::kChunkW);
+      r.w[F] = op(bw_t{}, sub_tag, so + w16 + F * kFragChunksW * R::kChunkW,
+                  so + w8 + F * kFragChunksW * R::kChunkW);
     else
       r.x[F] = op(bx_t{}, sub_tag, so + x16 + F * R::kChunkX, so + x8 + F * R::kChunkX);
   };
@@ -401,7 +411,7 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
   auto read_scale = [&](Scales& c, int so, auto s_tag) {
     constexpr int S = decltype(s_tag)::value;
     if constexpr (S < kFW)
-      c.w[S] = scale_at(so, wsc, S);
+      c.w[S] = scale_at(so, wsc, S * kFragChunksW);
     else
       c.x[S - kFW] = scale_at(so, xsc, S - kFW);
   };
@@ -556,9 +566,9 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
 
   // ---- epilogue
   const int mw0 = m0 + wm * 128, nw0 = n0 + wn * (TN / R::kWN);
-  // SwiGLU: this wave's 128 stacked rows are the gate rows (fragments 0, 1)
-  // and the up rows (fragments 2, 3) of output features nw0/2 .. nw0/2 + 63.
-  constexpr bool kSwiglu = EPI == kEpiSwiglu;
+  // SwiGLU: the wave's weight fragments are its gate rows (the first kFW / 2)
+  // and the up rows of the same features (the rest), output features
+  // nw0/2 .. nw0/2 + 16 kFW - 1.
   const int n_out = kSwiglu ? g.N / 2 : g.N;
   auto act = [&](float x) { return EPI == kEpiGeluTanh ? gelu_tanh_f32(x) : x; };
   if constexpr (OUT == kOutMx) {
@@ -570,7 +580,9 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
     // one 32-value conversion covers it, and its 24 code bytes are one
     // 16-byte and one 8-byte run of the tiled layout.
     const int n_stages = (n_out + kTileStageK - 1) / kTileStageK;
-    auto emit_pair = [&](const v16f& va, const v16f& vb, int m, int gm, int stage, int pr) {
+    // the swap, block scale and conversion: lane half h ends with the 24 code
+    // bytes q and the scale byte of one whole block (va's for h = 0, vb's for h = 1)
+    auto convert_pair = [&](const v16f& va, const v16f& vb, v6u& q, uint32_t& sbyte) {
       // lo: features 0..15 of this lane's block (even ones in 0..7, odd in
       // 8..15), hi: features 16..31 in the same order
       v16f lo, hi;
@@ -605,26 +617,62 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
         od[i] = lo[8 + i];
         od[8 + i] = hi[8 + i];
       }
-      v6u q = cvt_f32x2x16<OFMT>(ev, od, sc.scale);
-      uint32_t sbyte = sc.byte;
+      q = cvt_f32x2x16<OFMT>(ev, od, sc.scale);
+      sbyte = sc.byte;
       if (sc.nonfinite) q = v6u{0, 0, 0, 0, 0, 0};
-      const int qb = 2 * pr + h;  // this lane's block within the stage
+    };
+    // block qb (0..3) of output stage `stage` for token row m of group gm:
+    // even block: plane A (bytes 0..15) + plane L (16..23); odd block: plane
+    // H (bytes 0..7) + plane B (8..23)
+    auto store_block = [&](v6u q, uint32_t sbyte, int m, int gm, int stage, int qb) {
       const int nb = stage * 4 + qb;
       if (gm < g.gx && stage < n_stages) {
         if (m >= g.M || nb >= n_out / 32) {  // layout padding
           q = v6u{0, 0, 0, 0, 0, 0};
           sbyte = 127u;
         }
-        // even block: plane A (bytes 0..15) + plane L (16..23);
-        // odd block: plane H (bytes 0..7) + plane B (8..23)
-        uint8_t* half = static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes + pr * kHalfBytes;
-        const u32x4 d16 = h == 0 ? u32x4{q[0], q[1], q[2], q[3]} : u32x4{q[2], q[3], q[4], q[5]};
-        const u32x2 d8 = h == 0 ? u32x2{q[4], q[5]} : u32x2{q[0], q[1]};
-        *reinterpret_cast<u32x4*>(half + (h == 0 ? kPlaneA : kPlaneB) + j * 16) = d16;
-        *reinterpret_cast<u32x2*>(half + (h == 0 ? kPlaneL : kPlaneH) + j * 8) = d8;
+        const bool odd = qb & 1;
+        uint8_t* half =
+            static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes + (qb >> 1) * kHalfBytes;
+        const u32x4 d16 = !odd ? u32x4{q[0], q[1], q[2], q[3]} : u32x4{q[2], q[3], q[4], q[5]};
+        const u32x2 d8 = !odd ? u32x2{q[4], q[5]} : u32x2{q[0], q[1]};
+        *reinterpret_cast<u32x4*>(half + (!odd ? kPlaneA : kPlaneB) + j * 16) = d16;
+        *reinterpret_cast<u32x2*>(half + (!odd ? kPlaneL : kPlaneH) + j * 8) = d8;
         g.out_scales[((int64_t)stage * g.gx + gm) * kChunkScales + j * 4 + qb] = (uint8_t)sbyte;
       }
     };
+    // two consecutive blocks 2pr, 2pr+1 of one token fragment (lane half h: block 2pr + h)
+    auto emit_pair = [&](const v16f& va, const v16f& vb, int m, int gm, int stage, int pr) {
+      v6u q;
+      uint32_t sbyte;
+      convert_pair(va, vb, q, sbyte);
+      store_block(q, sbyte, m, gm, stage, 2 * pr + h);
+    };
+    if constexpr (kSwNarrow) {
+      // SwiGLU on 128-feature tiles: the wave's 32 output features nw0/2 .. +31
+      // are one block; pair token fragments fp and fp + 1 instead (lane half h:
+      // the block of token fragment fp + h)
+      const int ob = nw0 / 2;
+      const int stage = ob / kTileStageK, qb = (ob % kTileStageK) / 32;
+#pragma unroll
+      for (int fp = 0; fp < 4; fp += 2) {
+        v16f va, vb;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          va[r] = silu_f32(acc[0][fp][r]) * acc[1][fp][r];
+          vb[r] = silu_f32(acc[0][fp + 1][r]) * acc[1][fp + 1][r];
+        }
+        v6u q;
+        uint32_t sbyte;
+        convert_pair(va, vb, q, sbyte);
+        const int mrow0 = mw0 + (fp + h) * 32;
+        store_block(q, sbyte, mrow0 + j, mrow0 / kTileGroupRows, stage, qb);
+        // the stage's other 64 features have no tile when the output ends here:
+        // write their layout padding (block index past n_out / 32)
+        if (qb < 2 && n0 / 2 + 64 >= n_out) store_block(q, sbyte, mrow0 + j, mrow0 / kTileGroupRows, stage, qb + 2);
+      }
+      return;
+    }
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
       const int m = mw0 + fm * 32 + j;
@@ -654,7 +702,7 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
     }
     return;
   }
-  constexpr int kOutFrags = kSwiglu ? 2 : kFW;
+  constexpr int kOutFrags = kSwiglu ? kFW / 2 : kFW;
 #pragma unroll
   for (int fn = 0; fn < kOutFrags; ++fn) {
 #pragma unroll
@@ -663,7 +711,7 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
       v16f v;
       if constexpr (kSwiglu) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = silu_f32(acc[fn][fm][r]) * acc[fn + 2][fm][r];
+        for (int r = 0; r < 16; ++r) v[r] = silu_f32(acc[fn][fm][r]) * acc[fn + kFW / 2][fm][r];
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] = act(acc[fn][fm][r]);
@@ -729,10 +777,10 @@ hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out
     if (a.waves != 4) return hipErrorInvalidValue;
     if (epilogue == kEpiGeluTanh)
       launch_epi<WF, XF, kEpiGeluTanh, 128>(a, out_kind, out_fmt, grid, stream);
-    else if (epilogue == kEpiNone)
-      launch_epi<WF, XF, kEpiNone, 128>(a, out_kind, out_fmt, grid, stream);
+    else if (epilogue == kEpiSwiglu)
+      launch_epi<WF, XF, kEpiSwiglu, 128>(a, out_kind, out_fmt, grid, stream);
     else
-      return hipErrorInvalidValue;  // SwiGLU needs 256-feature tiles (rejected before this point)
+      launch_epi<WF, XF, kEpiNone, 128>(a, out_kind, out_fmt, grid, stream);
     return hipGetLastError();
   }
   if (a.waves == 8) {

@@ -184,14 +184,13 @@ def test_gemm_config_validation(L):
     ok = B.MXGemmConfig(8, 0)
     assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(ok), NULL) == B.MX_OK
     assert L.mx_gemm_with_config(*dict(args, k=100).values(), ctypes.byref(ok), NULL) == B.MX_ERR_SHAPE
-    # 128-feature tiles: the 6-bit pairs without SwiGLU; other pairs and SwiGLU are refused
+    # 128-feature tiles: the 6-bit pairs (every epilogue); other pairs are refused
     narrow = B.MXGemmConfig(4, 1, 128)
     assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(narrow), NULL) == B.MX_OK
     assert L.mx_gemm_with_config(*dict(args, m=0, epi=1).values(), ctypes.byref(narrow), NULL) == B.MX_OK
     assert L.mx_gemm_with_config(*dict(args, m=0, out_kind=2, out_scales=FAKE).values(), ctypes.byref(narrow),
                                  NULL) == B.MX_OK
-    assert L.mx_gemm_with_config(*dict(args, epi=2, n=128).values(), ctypes.byref(narrow),
-                                 NULL) == B.MX_ERR_UNSUPPORTED
+    assert L.mx_gemm_with_config(*dict(args, epi=2, n=128, m=0).values(), ctypes.byref(narrow), NULL) == B.MX_OK
     assert L.mx_gemm_with_config(*dict(args, a_fmt=0, w_fmt=0).values(), ctypes.byref(narrow),
                                  NULL) == B.MX_ERR_UNSUPPORTED
     # eight waves: 256-feature tiles of every pair, not SwiGLU, not with 128-feature tiles

@@ -376,7 +376,11 @@ def test_swiglu_f32_and_bf16(a_fmt, w_fmt, m, h, k):
     wq = _gpu_weights(w, w_fmt, qw)
     o32 = mx.mx_gemm(a.cuda(), wq, out_kind="f32", epilogue="swiglu", a_fmt=a_fmt)
     o16 = mx.mx_gemm(a.cuda(), wq, out_kind="bf16", epilogue="swiglu", a_fmt=a_fmt)
+    # 128-row tiles (one gate/up run per tile): the same bytes
+    n32 = mx.mx_gemm(a.cuda(), wq, out_kind="f32", epilogue="swiglu", a_fmt=a_fmt, config=NARROW)
+    n16 = mx.mx_gemm(a.cuda(), wq, out_kind="bf16", epilogue="swiglu", a_fmt=a_fmt, config=NARROW)
     torch.cuda.synchronize()
+    assert torch.equal(n32, o32) and torch.equal(n16, o16)
     assert tuple(o32.shape) == (m, h)
     bound = swiglu_bound(gate, up, sg, su, out)
     got = to_np(o32).astype(np.float64)
@@ -388,17 +392,26 @@ def test_swiglu_f32_and_bf16(a_fmt, w_fmt, m, h, k):
     assert bad.size == 0, f"{len(bad)} bf16 SwiGLU outputs off; first {bad[0].tolist()}"
 
 
+@pytest.mark.parametrize("cfg", [None, NARROW], ids=["tile256", "tile128"])
 @pytest.mark.parametrize("out_fmt", ["e2m3", "e3m2"])
-@pytest.mark.parametrize("m,h,k", [(300, 320, 416), (64, 64, 128)])
-def test_swiglu_mx_out(out_fmt, m, h, k):
+@pytest.mark.parametrize("m,h,k", [(300, 320, 416), (64, 64, 128), (40, 192, 256)])
+def test_swiglu_mx_out(out_fmt, m, h, k, cfg):
     """SwiGLU -> MX re-quantization along the h output features, under the
-    boundary-aware rule; the padding of the tiled output is checked too."""
+    boundary-aware rule; the padding of the tiled output is checked too (the
+    output buffer starts filled with 0xA5, so padding left unwritten fails).
+    h = 320 and 192 end half-way through a 128-feature output stage: with
+    128-row tiles the last tile writes the stage's other half as padding."""
     from tests.parity import check_mx_values, swiglu_bound
     a, w, qa, qw, out, gate, up, sg, su = _swiglu_operands(m, h, k, seed=3 * m + h)
-    say(f"gemm swiglu mx-out {m}x{2 * h}x{k} out={out_fmt}")
+    say(f"gemm swiglu mx-out {m}x{2 * h}x{k} out={out_fmt} config={cfg}")
     wq = _gpu_weights(w, "e2m3", qw)
-    o = mx.mx_gemm(a.cuda(), wq, out_kind="mx", epilogue="swiglu", out_fmt=out_fmt)
+    o = mx.MXTensor.empty(m, h, out_fmt, "tiled", torch.device("cuda"))
+    o.codes.fill_(0xA5)
+    o.scales.fill_(0xA5)
+    mx.mx_gemm(a.cuda(), wq, out_kind="mx", epilogue="swiglu", out_fmt=out_fmt, out=o, config=cfg)
+    ref = mx.mx_gemm(a.cuda(), wq, out_kind="mx", epilogue="swiglu", out_fmt=out_fmt)
     torch.cuda.synchronize()
+    assert torch.equal(o.codes, ref.codes) and torch.equal(o.scales, ref.scales)
     assert o.rows == m and o.k == h
     oc, os_ = mx_rows_view(o)
     o32 = out.astype(np.float32).astype(np.float64)

@@ -32,10 +32,10 @@ def test_save_load_round_trip(tmp_path):
 
 
 def test_candidates_the_call_supports():
-    # 128-feature tiles exist for the 6-bit pairs without SwiGLU only; 8 waves
+    # 128-feature tiles exist for the 6-bit pairs (every epilogue); 8 waves
     # for 256-feature tiles of every pair, without SwiGLU
     assert T.supports((4, 1, 128, 4), "e2m3", "e3m2", "gelu_tanh")
-    assert not T.supports((4, 1, 128, 4), "e2m3", "e2m3", "swiglu")
+    assert T.supports((4, 1, 128, 4), "e2m3", "e2m3", "swiglu")
     assert not T.supports((4, 1, 128, 4), "e4m3", "e4m3", "none")
     assert not T.supports((4, 1, 128, 8), "e2m3", "e2m3", "none")
     assert T.supports((4, 1, 256, 4), "e2m1", "e2m1", "none")
