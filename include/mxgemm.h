@@ -249,14 +249,15 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
             int32_t out_fmt, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Launch configuration of mx_gemm: the output tile width, the waves per
- * workgroup and the order in which the tiles are handed to workgroups.  It changes the speed (which
- * operand stages the workgroups in flight share in each XCD's L2, how many
- * workgroups share a CU), never the result: every configuration computes each
- * output with the same arithmetic (the same MFMA sequence over K per output).  The Hedra
- * post (section "We tuned before writing custom kernels") keeps per-shape
- * choices found by timing candidates on real data; a table of such choices
- * (microscaled_precision_gemm_amd/tuning.py) passes them here.
+ * Launch configuration of mx_gemm: the tile width, the waves per workgroup
+ * and the order in which the tiles are handed to workgroups.  It changes the
+ * speed (which operand stages the workgroups in flight share in each XCD's
+ * L2, how many workgroups share a CU), never the result: every configuration
+ * computes each output with the same arithmetic (the same MFMA sequence over
+ * K per output).  The Hedra post (section "We tuned before writing custom
+ * kernels") keeps per-shape choices found by timing candidates on real data;
+ * a table of such choices (microscaled_precision_gemm_amd/tuning.py, with the
+ * one tuned on MI355X in tuned_gfx950.json) passes them here.
  */
 typedef struct {
   int32_t group_m;   /* m-tiles per group of the tile walk, 1 .. 16 (default 4)             */

@@ -8,7 +8,9 @@
 //  * Operands stay packed (24 bytes per 32-element block) from HBM to the
 //    matrix cores.  A workgroup computes a 256 x 256 tile of C with 4 waves of
 //    128 x 128 on V_MFMA_SCALE_F32_32X32X64_F8F6F4 (per lane 32 K-contiguous
-//    FP6 codes in 6 VGPRs and one E8M0 byte picked by op_sel).  The same
+//    FP6 codes in 6 VGPRs and one E8M0 byte picked by op_sel); the launch
+//    configuration can instead pick 256 x 128 tiles (two workgroups per CU)
+//    or 8 waves of 128 x 64 per 256 x 256 tile (see Ring).  The same
 //    kernel takes the instruction's other operand formats (FP4 E2M1 in 4
 //    VGPRs, FP8 E4M3 / E5M2 in 8), the layout's chunk size and the ring depth
 //    following the element width.
@@ -58,9 +60,9 @@ static_assert(kStageScales == 4 * 64 * 4, "one 4-byte copy per lane per wave cov
 // LDS ring and copy schedule for weight format WF and activation format XF.
 // A slot holds one stage of both operands (256 rows x 128 K each, 4 KB per
 // element bit) and their scales; three slots when they fit in the 160 KB of
-// LDS, else two.  Each wave copies 1 KB per instruction (16 bytes per lane):
-// bits(XF) activation copies, bits(WF) weight copies and one scale copy per
-// operand per stage.  With three slots, stage ks+3's copies go out half in
+// LDS, else two.  Each wave copies 1 KB per instruction (16 bytes per lane);
+// with 4 waves and 256 weight rows that is bits(XF) activation copies,
+// bits(WF) weight copies and one scale copy per operand per stage.  With three slots, stage ks+3's copies go out half in
 // phase 1 of stage ks and half in phase 0 of stage ks+1; with two, stage
 // ks+2's copies all go out in phase 1 of stage ks (the slot it refills is
 // free from the middle of stage ks on, and the copies have a whole stage of
