@@ -272,6 +272,54 @@ def bench_producer(iters: int = 50):
             "algorithmic_bytes": alg, "gb_s": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
+def bench_stacked_projection(table, iters: int = 10):
+    """Quantize once, then one GEMM for the stacked projections: the producer
+    (RMSNorm + modulation + E2M3) on 20480 x 3072 bf16, then one mx_gemm over
+    the stacked [Wq; Wk; Wv; Wgate] weights (12288 x 3072, bf16 out), against
+    the same four projections as four GEMMs of 3072 x 3072 on the same
+    quantized activations."""
+    w = syn.WORKLOADS["fc1"]
+    dev = torch.device("cuda:0")
+    x = syn.make_a(w).to(dev)
+    g = torch.ones(w.k, dtype=torch.float32, device=dev)
+    sh = torch.zeros((2, w.k), dtype=torch.float32, device=dev)
+    sc = torch.zeros((2, w.k), dtype=torch.float32, device=dev)
+    a = mx.MXTensor.empty(w.m, w.k, "e2m3", "tiled", dev)
+    wsrc = syn.make_w(w).to(dev)  # 12288 = 4 x 3072 rows: q, k, v, gate
+    w_stack = mx.mx_quantize(wsrc, "e2m3")
+    d = w.k
+    w_parts = [mx.mx_quantize(wsrc[i * d:(i + 1) * d].contiguous(), "e2m3") for i in range(4)]
+    del wsrc
+    out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty((w.m, d), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    cfg = table.lookup(w.m, w.n, w.k, epilogue="none", out_kind="bf16")
+
+    def fused():
+        mx.mx_rmsnorm_quantize(x, g, sh, sc, 10240, 1e-6, "e2m3", out=a)
+        mx.mx_gemm(a, w_stack, out_kind="bf16", out=out, config=cfg)
+
+    def separate():
+        mx.mx_rmsnorm_quantize(x, g, sh, sc, 10240, 1e-6, "e2m3", out=a)
+        for wp, o in zip(w_parts, outs):
+            mx.mx_gemm(a, wp, out_kind="bf16", out=o)
+
+    res = {"workload": "RMSNorm + modulation + E2M3 of 20480x3072 bf16, then stacked QKV + gate 20480x3072x12288 "
+                       "(bf16 out)"}
+    flops = 2.0 * w.m * w.n * w.k
+    for name, fn in (("one_stacked_gemm", fused), ("four_gemms", separate)):
+        settle(fn, 0.2)
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        res[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1)}
+    res["config"] = list(cfg.key()) if cfg is not None else None
+    return res
+
+
 def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
     w = syn.WORKLOADS["skinny"]
     dev = torch.device("cuda:0")
@@ -408,6 +456,7 @@ def main():
     skinny = [bench_skinny(16, 16, args.skinny_iters), bench_skinny(8, 16, args.skinny_iters)]
     swiglu = bench_swiglu_mlp(table if not args.no_tune else tuning.TuningTable(), args.steps, args.warmup)
     producer = bench_producer()
+    stacked = bench_stacked_projection(table if not args.no_tune else tuning.TuningTable())
     formats = bench_formats(table, tune=not args.no_tune)
     if args.save_tuning and not args.no_tune:
         table.save(args.save_tuning)
@@ -440,6 +489,7 @@ def main():
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in skinny],
         "swiglu_mlp": swiglu,
         "producer": producer,
+        "stacked_projection": stacked,
         "operand_formats": formats,
     }
     if args.copy_calibration:

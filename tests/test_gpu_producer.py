@@ -155,3 +155,32 @@ def test_producer_full_size():
     bound = rmsnorm_bound(x64, gamma, scale[cond_rows], 1, 1e-6, y32)
     stats = check_mx_values(gc[rows], gs[rows], y32, bound, "e2m3")
     assert stats["exact"] >= 0.999 * stats["elements"], stats
+
+
+def test_quantize_once_stacked_projection():
+    """Quantize once, one projection GEMM: the producer's single quantized
+    activation feeds one mx_gemm over the stacked [Wq; Wk; Wv; Wgate] weights.
+    Every output column depends only on its own weight row, so each slice of
+    the stacked result is bit-identical to the separate GEMM of that
+    projection, and the whole matches the oracle GEMM of the produced codes.
+    Ragged rows, K and stacked N."""
+    rows, d, outs = 300, 416, (160, 160, 96, 224)
+    xt, gamma, shift, scale = _inputs(rows, d, 1, 12, "bf16")
+    ws = [syn.random_like_workload(20 + i, rows, d, o)[1] for i, o in enumerate(outs)]
+    say("producer -> stacked projection")
+    a = mx.mx_rmsnorm_quantize(xt.cuda(), _t(gamma), _t(shift), _t(scale), 320)
+    w_stack = mx.mx_quantize(torch.cat(ws).cuda(), "e2m3")
+    c = mx.mx_gemm(a, w_stack, out_kind="bf16")
+    parts = [mx.mx_gemm(a, mx.mx_quantize(w.cuda(), "e2m3"), out_kind="bf16") for w in ws]
+    c32 = mx.mx_gemm(a, w_stack, out_kind="f32")
+    torch.cuda.synchronize()
+    assert tuple(c.shape) == (rows, sum(outs))
+    off = 0
+    for o, p in zip(outs, parts):
+        assert torch.equal(c[:, off:off + o], p)
+        off += o
+    gc, gs = mx_rows_view(a)
+    da = O.dequantize(O.unpack(gc, d), gs, "e2m3")
+    dw = O.dequantize(*O.quantize(torch.cat(ws).to(torch.float64).numpy(), "e2m3"), "e2m3")
+    ref, s = O.gemm_ref(da, dw)
+    assert O.check_fp32(c32.cpu().numpy().astype(np.float64), ref, s).all()
