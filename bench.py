@@ -5,10 +5,13 @@ A step is one forward pass of the MLP hot path over 20480 tokens:
   h = mx_gemm(x_mx, W1, GELU -> MX)  fc1 20480 x 3072 x 12288, E2M3 intermediate
   y = mx_gemm(h, W2, bf16 out)       fc2 20480 x 12288 x 3072
 with weights pre-quantized once (untimed) and inputs resident in HBM.  value =
-2*M*N*K summed over both GEMMs / step time.  The skinny split-K path
-(M in {16, 8} x 16384 x 13312, E3M2 weights) is measured beside it on rotating
-weight copies (the weights fit in the 256 MB last-level cache otherwise), and
-the CPU oracle is timed on a bounded sample of the same step.
+2*M*N*K summed over both GEMMs / step time.  The GEMMs' launch configurations
+come from the tuning table shipped with the package.  Measured beside it: the
+skinny split-K path (M in {16, 8} x 16384 x 13312, E3M2 weights) on rotating
+weight copies (the weights fit in the 256 MB last-level cache otherwise), the
+SwiGLU variant of the MLP, the quantize-once producer alone and feeding the
+stacked QKV + gate projection, and fc1's shape in each operand format; the
+CPU oracle is timed on a bounded sample of the MLP step.
 
 Prints one JSON line.
 """

@@ -21,7 +21,8 @@ weigh more), or 256 with 8 waves, two per SIMD.
 * ``TuningTable.lookup`` returns the recorded configuration for a call, or
   None (the library default) for shapes never tuned.
 * ``TuningTable.save`` / ``load`` persist the table as JSON; entries are keyed
-  by device name, so a table carried to other hardware is not applied there.
+  by the device's ISA name and compute-unit count, so a table carried to other
+  hardware is not applied there.
 * ``SHIPPED_TABLE`` is the table tuned on MI355X (gfx950, 256 CUs) for the
   workload shapes, shipped with the package so that a run uses the same
   configurations every time: several candidates are within run-to-run noise
