@@ -255,22 +255,23 @@ def test_chained_fc1_fc2_small():
     assert np.all(np.abs(got - c2) <= flip_bound + O.GEMM_RTOL * s2 + O.ulp_bf16(c2))
 
 
-def test_determinism_guard_bands_and_poison():
+@pytest.mark.parametrize("cfg", [None, NARROW, EIGHT], ids=["default", "tile128", "waves8"])
+def test_determinism_guard_bands_and_poison(cfg):
     """Run twice bit-identically; rows/columns outside [m, n] of a larger
     buffer untouched (guard bands); every element of the output written (NaN
-    poison gone)."""
+    poison gone); for every tile shape."""
     m, n, k = 300, 544, 416
     a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", "e2m3", seed=13)
     wq = _gpu_weights(w, "e2m3", qw)
     aq = mx.mx_quantize(a.cuda(), "e2m3")
-    say("determinism / guard bands")
+    say(f"determinism / guard bands {cfg}")
     big = torch.full((m + 8, n + 40), float("nan"), dtype=torch.float32, device="cuda")
     big[m:, :] = 12345.0
     big[:, n:] = 12345.0
     view = big[:m, :n]
-    mx.mx_gemm(aq, wq, out_kind="f32", out=view)
+    mx.mx_gemm(aq, wq, out_kind="f32", out=view, config=cfg)
     first = view.clone()
-    mx.mx_gemm(aq, wq, out_kind="f32", out=view)
+    mx.mx_gemm(aq, wq, out_kind="f32", out=view, config=cfg)
     torch.cuda.synchronize()
     assert torch.equal(first, view)
     assert not torch.isnan(view).any()
@@ -280,12 +281,23 @@ def test_determinism_guard_bands_and_poison():
     o = mx.MXTensor.empty(m, n, "e2m3", "tiled", "cuda")
     o.codes.fill_(0xFF)
     o.scales.fill_(0xFF)
-    mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", out=o)
+    mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh", out=o, config=cfg)
     o2 = mx.mx_gemm(aq, wq, out_kind="mx", epilogue="gelu_tanh")
     torch.cuda.synchronize()
     assert torch.equal(o.codes, o2.codes) and torch.equal(o.scales, o2.scales)
     assert not torch.any(o.scales == 0xFF)
     mx_rows_view(o)  # padding of the tiled output written as 0 codes / 127 scales
+    if cfg != EIGHT:
+        # SwiGLU (n = 544 stacked rows is not whole runs of 128: use 512) into a strided view
+        ws = mx.mx_quantize(w[:512].cuda(), "e2m3")
+        big = torch.full((m + 8, 256 + 24), float("nan"), dtype=torch.float32, device="cuda")
+        big[m:, :] = 12345.0
+        big[:, 256:] = 12345.0
+        mx.mx_gemm(aq, ws, out_kind="f32", epilogue="swiglu", out=big[:m, :256], config=cfg)
+        ref = mx.mx_gemm(aq, ws, out_kind="f32", epilogue="swiglu")
+        torch.cuda.synchronize()
+        assert torch.equal(big[:m, :256], ref)
+        assert torch.all(big[m:, :] == 12345.0) and torch.all(big[:, 256:] == 12345.0)
 
 
 def test_edge_shapes():
