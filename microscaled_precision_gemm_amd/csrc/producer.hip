@@ -13,6 +13,9 @@
 // Custom Kernels for the AMD MI300", section "Fused RMS Norm Kernel" (128-bit
 // coalesced loads, one block per row, a block-wide reduction); here:
 //
+//  * bf16 rows of up to 3072 elements (rmsnorm_quantize_rows_kernel): the rows
+//    stay in registers between the passes, so x is read from HBM once (see
+//    that kernel).  Wider rows and fp32 sources take the two-pass kernel:
 //  * one workgroup (4 waves) per 32-row group.  Pass 1: each wave reduces the
 //    sum of squares of 8 rows with 16-byte loads (consecutive lanes on
 //    consecutive bytes, up to eight loads in flight) and a wave-wide shuffle
@@ -68,6 +71,69 @@ __device__ __forceinline__ void piece_to_f32(const u32x4& w, float (&f)[4 * (F32
   }
 }
 
+// Conversion of one staged chunk (32 rows x 128 elements in LDS, rows
+// L::kRow bytes apart) and its store into the tiled layout: lane (h, j) takes
+// blocks 2h, 2h+1 of row j, y = x * inv * va[k] + vb[k] over the stage's
+// features k, then the MX rule.
+template <int FMT, bool F32>
+__device__ __forceinline__ void convert_store_chunk(const ProducerArgs& a, const uint8_t* in, const float* va,
+                                                    const float* vb, float inv, int grp, int stage, int lane) {
+  using L = PLayout<F32>;
+  const int j = lane & 31, h = lane >> 5;
+  const int row = grp * 32 + j;
+  const int kblocks = a.d / 32;
+  v6u q[2];
+  uint32_t sbyte[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int qb = 2 * h + t;
+    const uint8_t* p = in + j * L::kRow + qb * 32 * L::kEsize;
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 32 / (16 / L::kEsize); ++i) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * i);
+      float f[4 * (F32 ? 1 : 2)];
+      piece_to_f32<F32>(w, f);
+#pragma unroll
+      for (int e = 0; e < 4 * (F32 ? 1 : 2); ++e) {
+        const int kk = qb * 32 + i * (16 / L::kEsize) + e;  // element within the stage
+        y[i * (16 / L::kEsize) + e] = __builtin_fmaf(f[e] * inv, va[kk], vb[kk]);
+      }
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t m = __float_as_uint(y[e]) & 0x7fffffffu;
+      amax = m > amax ? m : amax;
+    }
+    const BlockScale s = scale_from_f32_bits<FMT>(amax);
+    v16f even, odd;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      even[i] = y[2 * i];
+      odd[i] = y[2 * i + 1];
+    }
+    v6u r = cvt_f32x2x16<FMT>(even, odd, s.scale);
+    uint32_t byte = s.byte;
+    if (s.nonfinite) r = v6u{0, 0, 0, 0, 0, 0};
+    if (row >= a.rows || stage * 4 + qb >= kblocks) {  // padding
+      r = v6u{0, 0, 0, 0, 0, 0};
+      byte = 127u;
+    }
+    q[t] = r;
+    sbyte[t] = byte;
+  }
+  // the 48 code bytes of row j in the planes of half h of chunk (stage, grp)
+  const int64_t chunk = (int64_t)stage * a.groups + grp;
+  uint8_t* half = a.codes + chunk * kChunkCodes + h * kHalfBytes;
+  *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
+  *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
+  *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
+  *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
+  *reinterpret_cast<uint16_t*>(a.scales + chunk * kChunkScales + j * 4 + 2 * h) =
+      (uint16_t)(sbyte[0] | (sbyte[1] << 8));
+}
+
 template <int FMT, bool F32>
 __global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const ProducerArgs a) {
   using L = PLayout<F32>;
@@ -77,7 +143,7 @@ __global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const Produ
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = blockIdx.x;
   const uint8_t* src = static_cast<const uint8_t*>(a.x);
-  const int d = a.d, kblocks = d / 32, stages = (d + kTileStageK - 1) / kTileStageK;
+  const int d = a.d, stages = (d + kTileStageK - 1) / kTileStageK;
 
   // ---- pass 1: 1 / rms of the group's rows, 8 rows per wave
   constexpr int kElemsPerLoad = 16 / L::kEsize;   // 8 bf16 or 4 fp32 per lane and load
@@ -117,9 +183,7 @@ __global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const Produ
   const int64_t cond = a.rows_per_cond > 0 ? (int64_t)grp * 32 / a.rows_per_cond : 0;
   const float* sh = a.shift ? a.shift + cond * d : nullptr;
   const float* sc = a.scale ? a.scale + cond * d : nullptr;
-  const int j = lane & 31, h = lane >> 5;
-  const int row = grp * 32 + j;
-  const float inv = lds_inv[j];
+  const float inv = lds_inv[lane & 31];
   // the chunk of 32 rows x 128 elements of stage `stage`, 16 bytes per lane and load
   auto load = [&](int stage, u32x4 (&v)[L::kCopies]) {
 #pragma unroll
@@ -159,23 +223,113 @@ __global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const Produ
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-    v6u q[2];
-    uint32_t sbyte[2];
+    convert_store_chunk<FMT, F32>(a, in, va, vb, inv, grp, stage, lane);
+    // the next stage reuses this wave's LDS rows
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+}
+
+// ---- bf16 rows of up to 3072 elements: the rows stay in registers between
+// the passes, so x is read from HBM once.  A workgroup takes half of a
+// 32-row group (16 rows; two workgroups fit a CU, so one's loads overlap the
+// other's conversion): eight waves of two whole rows each (piece p = 64 i +
+// lane of a row: elements 8p .. 8p+7, i = 0..5).  Pass 1 sums the squares
+// from the registers.  Pass 2 takes the stages eight at a time: every wave
+// writes its rows' pieces of the eight stages into eight LDS chunks (one
+// 16-byte write per register and row: the 64 lanes of register i cover stages
+// 4i .. 4i+3), and after a barrier wave w converts stage b + w, one block per
+// lane (row lane % 16, block lane / 16).
+constexpr int kRWaves = 8;
+constexpr int kRMaxD = 3072;
+constexpr int kRHalf = 16;                // rows per workgroup
+constexpr int kRRows = kRHalf / kRWaves;  // rows per wave
+constexpr int kRLoads = kRMaxD / 512;     // 16-byte pieces per lane and row
+constexpr int kRStages = kRMaxD / kTileStageK;
+
+template <int FMT>
+__global__ __launch_bounds__(64 * kRWaves, 2) void rmsnorm_quantize_rows_kernel(const ProducerArgs a) {
+  constexpr int kRow = 256 + 16;  // padded LDS row of a staged chunk
+  __shared__ __attribute__((aligned(16))) uint8_t lds_chunk[kRWaves][kRHalf * kRow];
+  __shared__ __attribute__((aligned(16))) float lds_ab[kRWaves][2][128];
+  __shared__ float lds_inv[kRHalf];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = blockIdx.x >> 1, r0 = (blockIdx.x & 1) * kRHalf;  // group, first row in it
+  const uint8_t* src = static_cast<const uint8_t*>(a.x);
+  const int d = a.d, kblocks = d / 32, stages = (d + kTileStageK - 1) / kTileStageK;
+
+  u32x4 v[kRRows][kRLoads];
+#pragma unroll
+  for (int rr = 0; rr < kRRows; ++rr) {
+    const int row = grp * 32 + r0 + wave * kRRows + rr;
+    const uint8_t* xr = src + (int64_t)(row < a.rows ? row : 0) * a.ld_bytes;
+#pragma unroll
+    for (int i = 0; i < kRLoads; ++i) {
+      const int e = (64 * i + lane) * 8;
+      v[rr][i] = row < a.rows && e < d ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + (int64_t)e * 2))
+                                       : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // ---- pass 1
+#pragma unroll
+  for (int rr = 0; rr < kRRows; ++rr) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRLoads; ++i) {
+      float f[8];
+      piece_to_f32<false>(v[rr][i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+    }
+    ss = wave_sum(ss);
+    const int jr = wave * kRRows + rr, row = grp * 32 + r0 + jr;
+    if (lane == 0) lds_inv[jr] = row < a.rows ? 1.0f / __builtin_sqrtf(ss / (float)d + a.eps) : 0.0f;
+  }
+  __syncthreads();
+
+  // ---- pass 2
+  const int j = lane & 15, q = lane >> 4;  // conversion: row j of the half-group, block q of the stage
+  const int row = grp * 32 + r0 + j;
+  const float inv = lds_inv[j];
+  const int64_t cond = a.rows_per_cond > 0 ? (int64_t)grp * 32 / a.rows_per_cond : 0;
+  const float* sh = a.shift ? a.shift + cond * d : nullptr;
+  const float* sc = a.scale ? a.scale + cond * d : nullptr;
+  const int sub = lane >> 4, piece = lane & 15;  // staging: stage 4i + sub of register i, its piece `piece`
+#pragma unroll
+  for (int b = 0; b < kRStages; b += kRWaves) {
+    if (b >= stages) break;
+#pragma unroll
+    for (int i = b / 4; i < (b + kRWaves) / 4; ++i)
+#pragma unroll
+      for (int rr = 0; rr < kRRows; ++rr)
+        *reinterpret_cast<u32x4*>(&lds_chunk[(4 * i + sub) % kRWaves][(wave * kRRows + rr) * kRow + piece * 16]) =
+            v[rr][i];
+    const int stage = b + wave;
+    float* va = lds_ab[wave][0];
+    float* vb = lds_ab[wave][1];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int qb = 2 * h + t;
-      const uint8_t* p = in + j * L::kRow + qb * 32 * L::kEsize;
+      const int k = stage * kTileStageK + 2 * lane + t;
+      float fa = 0.0f, fb = 0.0f;
+      if (stage < stages && k < d) {
+        fa = a.gamma ? a.gamma[k] : 1.0f;
+        if (sc) fa *= 1.0f + sc[k];
+        fb = sh ? sh[k] : 0.0f;
+      }
+      va[2 * lane + t] = fa;
+      vb[2 * lane + t] = fb;
+    }
+    __syncthreads();
+    if (stage < stages) {
+      const uint8_t* p = lds_chunk[wave] + j * kRow + q * 64;
       float y[32];
 #pragma unroll
-      for (int i = 0; i < 32 / (16 / L::kEsize); ++i) {
+      for (int i = 0; i < 4; ++i) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(p + 16 * i);
-        float f[4 * (F32 ? 1 : 2)];
-        piece_to_f32<F32>(w, f);
+        float f[8];
+        piece_to_f32<false>(w, f);
 #pragma unroll
-        for (int e = 0; e < 4 * (F32 ? 1 : 2); ++e) {
-          const int kk = qb * 32 + i * (16 / L::kEsize) + e;  // element within the stage
-          y[i * (16 / L::kEsize) + e] = __builtin_fmaf(f[e] * inv, va[kk], vb[kk]);
-        }
+        for (int e = 0; e < 8; ++e) y[8 * i + e] = __builtin_fmaf(f[e] * inv, va[q * 32 + 8 * i + e], vb[q * 32 + 8 * i + e]);
       }
       uint32_t amax = 0;
 #pragma unroll
@@ -193,32 +347,35 @@ __global__ __launch_bounds__(kPThreads) void rmsnorm_quantize_kernel(const Produ
       v6u r = cvt_f32x2x16<FMT>(even, odd, s.scale);
       uint32_t byte = s.byte;
       if (s.nonfinite) r = v6u{0, 0, 0, 0, 0, 0};
-      if (row >= a.rows || stage * 4 + qb >= kblocks) {  // padding
+      if (row >= a.rows || stage * 4 + q >= kblocks) {  // padding
         r = v6u{0, 0, 0, 0, 0, 0};
         byte = 127u;
       }
-      q[t] = r;
-      sbyte[t] = byte;
+      // block q of row r0 + j: even blocks in planes A + L, odd ones in H + B, of half q / 2
+      const int jj = r0 + j;
+      const int64_t chunk = (int64_t)stage * a.groups + grp;
+      uint8_t* half = a.codes + chunk * kChunkCodes + (q >> 1) * kHalfBytes;
+      if ((q & 1) == 0) {
+        *reinterpret_cast<u32x4*>(half + kPlaneA + jj * 16) = u32x4{r[0], r[1], r[2], r[3]};
+        *reinterpret_cast<u32x2*>(half + kPlaneL + jj * 8) = u32x2{r[4], r[5]};
+      } else {
+        *reinterpret_cast<u32x2*>(half + kPlaneH + jj * 8) = u32x2{r[0], r[1]};
+        *reinterpret_cast<u32x4*>(half + kPlaneB + jj * 16) = u32x4{r[2], r[3], r[4], r[5]};
+      }
+      a.scales[chunk * kChunkScales + jj * 4 + q] = (uint8_t)byte;
     }
-    // the 48 code bytes of row j in the planes of half h of chunk (stage, grp)
-    const int64_t chunk = (int64_t)stage * a.groups + grp;
-    uint8_t* half = a.codes + chunk * kChunkCodes + h * kHalfBytes;
-    *reinterpret_cast<u32x4*>(half + kPlaneA + j * 16) = u32x4{q[0][0], q[0][1], q[0][2], q[0][3]};
-    *reinterpret_cast<u32x2*>(half + kPlaneL + j * 8) = u32x2{q[0][4], q[0][5]};
-    *reinterpret_cast<u32x2*>(half + kPlaneH + j * 8) = u32x2{q[1][0], q[1][1]};
-    *reinterpret_cast<u32x4*>(half + kPlaneB + j * 16) = u32x4{q[1][2], q[1][3], q[1][4], q[1][5]};
-    *reinterpret_cast<uint16_t*>(a.scales + chunk * kChunkScales + j * 4 + 2 * h) =
-        (uint16_t)(sbyte[0] | (sbyte[1] << 8));
-    // the next stage reuses this wave's LDS rows
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // every wave has converted its chunk: the next batch may overwrite them
+    __syncthreads();
   }
 }
 
 template <int FMT>
 void launch_fmt(const ProducerArgs& a, bool f32, hipStream_t stream) {
   const dim3 grid((unsigned)a.groups), block(kPThreads);
-  if (f32)
+  if (!f32 && a.d <= kRMaxD)
+    hipLaunchKernelGGL((rmsnorm_quantize_rows_kernel<FMT>), dim3(2 * (unsigned)a.groups), dim3(64 * kRWaves), 0,
+                       stream, a);
+  else if (f32)
     hipLaunchKernelGGL((rmsnorm_quantize_kernel<FMT, true>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((rmsnorm_quantize_kernel<FMT, false>), grid, block, 0, stream, a);
