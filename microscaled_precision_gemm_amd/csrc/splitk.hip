@@ -23,6 +23,23 @@
 //  * V_MFMA_SCALE_F32_32X32X64_F8F6F4 with the weights as the A operand and
 //    the tokens as the B operand; token rows 16..31 are layout padding (zero
 //    codes), so M = 8 or 16 costs no extra weight bytes and no branches.
+//  * The scale bytes a wave needs for all of its stages (both groups' weight
+//    scales and the tokens' activation scales, 320 B per stage) are loaded
+//    with a handful of 16-byte loads ahead of the first stages and kept in
+//    the wave's own LDS slice, then read per stage from LDS.  That takes
+//    three small loads per stage out of the in-order memory queue the weight
+//    stream uses.
+//  * The window only works if each MFMA waits for its own stage's loads and
+//    not for all of them (vmcnt counts loads in issue order).  The compiler
+//    inserts those waits; it can count exactly only when: a slot is consumed
+//    in place before it is refilled (a copy of a register with a load
+//    pending waits for every load), the per-wave bounds are uniform values,
+//    every refill is unconditional (past the last stage it reads one line,
+//    never used), and no direct global-to-LDS copy is pending (those make
+//    every later LDS read wait for all loads).  The LDS-scale path meets all
+//    four: every wave streams a multiple of kWindow stages, at most
+//    kLdsStages.  Other shapes take the per-stage-scale path with
+//    conditional refills.
 //  * When a chunk ends, its fp32 partials go to LDS; after one barrier the
 //    workgroup adds the S partials in the fixed order 0 .. S-1 (deterministic)
 //    and rounds once into the output.  No partials touch HBM and no second
@@ -40,6 +57,9 @@ constexpr int kSkWaves = 8;
 constexpr int kSkThreads = 64 * kSkWaves;
 constexpr int kSkGroups = 2;  // 32-feature weight groups per workgroup (and per wave)
 constexpr int kWindow = 4;    // stages of loads in flight per wave (two waves per SIMD fit)
+constexpr int kLdsStages = 16;  // stages per wave whose scales fit the wave's LDS slice
+constexpr int kRecW = 2 * kChunkScales;  // per stage: both groups' weight scales (2 x 128 B)
+constexpr int kRecX = kChunkScales / 2;  // per stage: token rows 0..15's activation scales
 
 // One operand pair of a stage as loaded: the lane's entries of planes A, L,
 // H and B of half h (block 2h = A + L, block 2h+1 = H + B).  The window keeps
@@ -83,11 +103,17 @@ __device__ __forceinline__ v8i op1(const Pieces& p) {
 }
 
 // grid: one workgroup per pair of 32-feature groups.
-template <int WF, int XF, int OUT>
+// LDS_SCALES: every wave streams at most kLdsStages stages.
+template <int WF, int XF, int OUT, bool LDS_SCALES>
 __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) {
   // partial sums [split][token][feature], tokens 0..15, features of both groups
   __shared__ __attribute__((aligned(16))) float part[kMaxSplits][16][32 * kSkGroups];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // per wave: the scale bytes of its stages, in stage order
+  __shared__ __attribute__((aligned(16))) uint8_t scw[LDS_SCALES ? kSkWaves : 1][LDS_SCALES ? kLdsStages : 1][kRecW];
+  __shared__ __attribute__((aligned(16))) uint8_t scx[LDS_SCALES ? kSkWaves : 1][LDS_SCALES ? kLdsStages : 1][kRecX];
+  // the wave index as a uniform value: every per-wave bound and refill
+  // condition below is then scalar, not an exec-masked branch
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, j = lane & 31;
   const int grp = blockIdx.x * kSkGroups;                 // first of the workgroup's groups
   const bool has1 = grp + 1 < g.gw;                      // the second group exists
@@ -109,7 +135,6 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
   const uint8_t* wc = g.w_codes + (int64_t)grp * kChunkCodes + lane_off;
   const uint8_t* ws = g.w_scales + (int64_t)grp * kChunkScales + scale_off;
   const uint8_t* xc = g.x_codes + lane_off;  // activations: one 32-row group
-  const uint8_t* xs = g.x_scales + scale_off;
   const int64_t w_step = (int64_t)g.gw * kChunkCodes, ws_step = (int64_t)g.gw * kChunkScales;
   const bool token = j < 16;  // rows 16..31 of the activation group are zero padding
 
@@ -126,26 +151,51 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
     }
     return (c0 + c) * sps + t;
   };
+  const int s_first = c0 * sps;  // the wave's stages are s_first .. s_first + nst - 1
+  // Loads are branch-free, so that the compiler can count the window's
+  // loads exactly and wait for one stage at a time: padding lanes 16..31
+  // re-read token rows 0..15 (the same lines, no extra requests) and a
+  // missing second group re-reads the first; neither result is ever stored.
+  const int jx = j & 15;
+  const int64_t w1_off = has1 ? kChunkCodes : 0;
+  const int64_t ws1_off = has1 ? kChunkScales : 0;
+  const int xs_off = jx * 4 + 2 * h;
+  auto load_codes = [&](int st, StageOps& o) {
+    o.w0 = load_pieces<true>(wc + st * w_step, j);
+    o.w1 = load_pieces<true>(wc + st * w_step + w1_off, j);
+    o.x = load_pieces<false>(xc + (int64_t)st * kChunkCodes, jx);
+  };
+  auto load_scales_global = [&](int st, StageOps& o) {
+    o.ws0 = *reinterpret_cast<const uint16_t*>(ws + st * ws_step);
+    o.ws1 = *reinterpret_cast<const uint16_t*>(ws + st * ws_step + ws1_off);
+    o.xs = *reinterpret_cast<const uint16_t*>(g.x_scales + (int64_t)st * kChunkScales + xs_off);
+  };
+  auto load_scales = [&](int st, StageOps& o) {
+    if constexpr (LDS_SCALES) {
+      const uint8_t* r = &scw[wave][st - s_first][scale_off];
+      o.ws0 = *reinterpret_cast<const uint16_t*>(r);
+      o.ws1 = *reinterpret_cast<const uint16_t*>(r + kChunkScales);
+      o.xs = *reinterpret_cast<const uint16_t*>(&scx[wave][st - s_first][xs_off]);
+    } else {
+      load_scales_global(st, o);
+    }
+  };
+  // LDS path refill, unconditional so that the compiler counts the loads in
+  // flight exactly: past the wave's last stage (more == false) every lane
+  // reads the same few lines at the start of the weights; never consumed.
+  auto refill = [&](int st, bool more, StageOps& o) {
+    const uint8_t* w = more ? wc + st * w_step : g.w_codes;
+    const uint8_t* x = more ? xc + (int64_t)st * kChunkCodes : g.w_codes;
+    const int jw = more ? j : 0, jt = more ? jx : 0;
+    o.w0 = load_pieces<true>(w, jw);
+    o.w1 = load_pieces<true>(more ? w + w1_off : w, jw);
+    o.x = load_pieces<false>(x, jt);
+    load_scales(more ? st : s_first, o);
+  };
   auto load = [&](int st) {
     StageOps o;
-    o.w0 = load_pieces<true>(wc + st * w_step, j);
-    o.ws0 = *reinterpret_cast<const uint16_t*>(ws + st * ws_step);
-    if (has1) {  // the next group's chunk follows in memory
-      o.w1 = load_pieces<true>(wc + st * w_step + kChunkCodes, j);
-      o.ws1 = *reinterpret_cast<const uint16_t*>(ws + st * ws_step + kChunkScales);
-    } else {
-      o.w1.a = o.w1.b = u32x4{0u, 0u, 0u, 0u};
-      o.w1.l = o.w1.hh = u32x2{0u, 0u};
-      o.ws1 = 0x7f7f;
-    }
-    if (token) {
-      o.x = load_pieces<false>(xc + (int64_t)st * kChunkCodes, j);
-      o.xs = *reinterpret_cast<const uint16_t*>(xs + (int64_t)st * kChunkScales);
-    } else {
-      o.x.a = o.x.b = u32x4{0u, 0u, 0u, 0u};
-      o.x.l = o.x.hh = u32x2{0u, 0u};
-      o.xs = 0x7f7f;
-    }
+    load_codes(st, o);
+    load_scales(st, o);
     return o;
   };
 
@@ -153,16 +203,51 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
   StageOps win[kWindow];
+  if constexpr (LDS_SCALES) {
+    if (nst > 0) {  // then nst >= kWindow (launch condition)
+      // The scale bytes of the wave's stages are loaded first (weight scales
+      // 16 lanes x 16 B per stage, 4 stages per load, a missing second group
+      // repeating the first; activation scales 4 lanes x 16 B per stage, 16
+      // stages per load; lanes past the wave's last stage repeat it), then
+      // the window's code loads, then the scales are written to the wave's
+      // LDS slice: the wait for them is not a wait for the window.
+      const uint8_t* wsb = g.w_scales + (int64_t)grp * kChunkScales + (has1 ? lane & 15 : lane & 7) * 16;
+      u32x4 rw[kLdsStages / 4];
 #pragma unroll
-  for (int i = 0; i < kWindow; ++i)
-    if (i < nst) win[i] = load(next_stage());
+      for (int r = 0; r < kLdsStages / 4; ++r)
+        rw[r] = *reinterpret_cast<const u32x4*>(wsb + (int64_t)(s_first + min(4 * r + (lane >> 4), nst - 1)) * ws_step);
+      const u32x4 rx = *reinterpret_cast<const u32x4*>(
+          g.x_scales + (int64_t)(s_first + min(lane >> 2, nst - 1)) * kChunkScales + (lane & 3) * 16);
+      int wst[kWindow];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kWindow; ++k) {
+        wst[k] = next_stage();
+        load_codes(wst[k], win[k]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < kLdsStages / 4; ++r)
+        *reinterpret_cast<u32x4*>(&scw[wave][4 * r + (lane >> 4)][(lane & 15) * 16]) = rw[r];
+      *reinterpret_cast<u32x4*>(&scx[wave][lane >> 2][(lane & 3) * 16]) = rx;
+#pragma unroll
+      for (int k = 0; k < kWindow; ++k) load_scales(wst[k], win[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kWindow; ++k)
+      if (k < nst) win[k] = load(next_stage());
+  }
   int cc = 0, left = sps;  // chunk position being accumulated, its stages still to come
   for (int i = 0; i < nst; i += kWindow) {
 #pragma unroll
     for (int k = 0; k < kWindow; ++k) {
-      if (i + k < nst) {
-        const StageOps o = win[k];
-        if (i + k + kWindow < nst) win[k] = load(next_stage());
+      // LDS path: nst is a multiple of kWindow (launch condition)
+      if (LDS_SCALES || i + k < nst) {
+        // consume the slot in place, then refill it: the refill can reuse
+        // the slot's registers, so the window rotates without copies (a copy
+        // of a register with a load pending would wait for every load)
+        const StageOps& o = win[k];
         const v8i x0 = op0(o.x), x1 = op1(o.x);
         acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op0(o.w0), x0, acc0, WF, XF, 0, o.ws0, 0, o.xs);
         acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op0(o.w1), x0, acc1, WF, XF, 0, o.ws1, 0, o.xs);
@@ -185,6 +270,12 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
           for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
           ++cc;
           left = sps;
+        }
+        if constexpr (LDS_SCALES) {
+          const bool more = i + k + kWindow < nst;
+          refill(next_stage(), more, win[k]);  // the cursor may run past the end: unused then
+        } else if (i + k + kWindow < nst) {
+          win[k] = load(next_stage());
         }
       }
     }
@@ -209,18 +300,28 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
   }
 }
 
-template <int OUT>
-hipError_t launch_out(const SplitKArgs& a, int x_fmt, int w_fmt, hipStream_t stream) {
+template <int OUT, bool LDS_SCALES>
+hipError_t launch_fmt(const SplitKArgs& a, int x_fmt, int w_fmt, hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(a.gw, kSkGroups)), block(kSkThreads);
   if (w_fmt == kFmtE2M3 && x_fmt == kFmtE2M3)
-    hipLaunchKernelGGL((splitk_kernel<kFmtE2M3, kFmtE2M3, OUT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((splitk_kernel<kFmtE2M3, kFmtE2M3, OUT, LDS_SCALES>), grid, block, 0, stream, a);
   else if (w_fmt == kFmtE3M2 && x_fmt == kFmtE2M3)
-    hipLaunchKernelGGL((splitk_kernel<kFmtE3M2, kFmtE2M3, OUT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((splitk_kernel<kFmtE3M2, kFmtE2M3, OUT, LDS_SCALES>), grid, block, 0, stream, a);
   else if (w_fmt == kFmtE2M3 && x_fmt == kFmtE3M2)
-    hipLaunchKernelGGL((splitk_kernel<kFmtE2M3, kFmtE3M2, OUT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((splitk_kernel<kFmtE2M3, kFmtE3M2, OUT, LDS_SCALES>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_out(const SplitKArgs& a, int x_fmt, int w_fmt, hipStream_t stream) {
+  // A wave streams 0 or 1 .. ceil(S / waves) chunks of K / 128 / S stages.
+  // The LDS scale path needs every streaming wave to fill the window and to
+  // fit its records in its slice.
+  const int64_t sps = a.K / kTileStageK / a.splits;
+  const bool lds = sps > 0 && sps % kWindow == 0 && ceil_div(a.splits, kSkWaves) * sps <= kLdsStages;
+  return lds ? launch_fmt<OUT, true>(a, x_fmt, w_fmt, stream) : launch_fmt<OUT, false>(a, x_fmt, w_fmt, stream);
 }
 
 }  // namespace
