@@ -8,7 +8,8 @@ with weights pre-quantized once (untimed) and inputs resident in HBM.  value =
 2*M*N*K summed over both GEMMs / step time.  The GEMMs' launch configurations
 come from the tuning table shipped with the package.  Measured beside it: the
 skinny split-K path (M in {16, 8} x 16384 x 13312, E3M2 weights) on rotating
-weight copies (the weights fit in the 256 MB last-level cache otherwise), the
+weight copies (the weights fit in the 256 MB last-level cache otherwise), per
+call and for the split-K kernel alone on activations quantized beforehand, the
 SwiGLU variant of the MLP, the quantize-once producer alone and feeding the
 stacked QKV + gate projection, and fc1's shape in each operand format; the
 CPU oracle is timed on a bounded sample of the MLP step.
@@ -361,10 +362,23 @@ def bench_skinny(m: int, splits: int, iters: int, copies: int = 3):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
+    # the split-K kernel alone: activations quantized beforehand (one launch per call)
+    aq = mx.mx_quantize(a, "e2m3", "tiled")
+    for i in range(10):
+        mx.mx_gemm_splitk(aq, ws[i % copies], splits, out=out)
+    e0.record()
+    for i in range(iters):
+        mx.mx_gemm_splitk(aq, ws[i % copies], splits, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    kms = e0.elapsed_time(e1) / iters
     wbytes = w.n * w.k * 3 // 4 + w.n * w.k // 32
     alg = wbytes + m * w.k * 2 + m * w.n * 2
+    kalg = wbytes + m * w.k * 3 // 4 + m * w.k // 32 + m * w.n * 2
     return {"m": m, "splits": splits, "ms": ms, "algorithmic_bytes": alg, "gb_s": alg / ms / 1e6,
-            "hbm_frac": alg / ms / 1e6 / PEAK_HBM_GBS, "tflops": 2.0 * m * w.n * w.k / ms / 1e9}
+            "hbm_frac": alg / ms / 1e6 / PEAK_HBM_GBS, "tflops": 2.0 * m * w.n * w.k / ms / 1e9,
+            "kernel_ms": kms, "kernel_algorithmic_bytes": kalg, "kernel_gb_s": kalg / kms / 1e6,
+            "kernel_hbm_frac": kalg / kms / 1e6 / PEAK_HBM_GBS}
 
 
 def gemm_sources_sha256() -> str:
