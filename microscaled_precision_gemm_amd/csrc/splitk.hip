@@ -7,14 +7,14 @@
 // stream of packed weights from HBM (0.78 bytes per weight), so the kernel is
 // built for memory-level parallelism, not for the matrix cores:
 //
-//  * One workgroup per pair of 32-feature weight groups, 8 waves.  Wave w
-//    streams the K-chunks w*spw .. w*spw+spw-1 (spw = ceil(S/8)) of both
+//  * One workgroup per pair of 32-feature weight groups, 4 waves.  Wave w
+//    streams the K-chunks w*spw .. w*spw+spw-1 (spw = ceil(S/4)) of both
 //    groups, stage after stage, with kWindow stages of loads in flight across
 //    chunk boundaries.  Each stage's activation operand is loaded once and
 //    used by the MFMAs of both groups: the activations are the same few
 //    hundred KB for every workgroup and come from L2, so sharing them halves
 //    those load instructions per weight byte (they measured a fifth of the
-//    kernel's time with one group per wave).  208 workgroups of 8 waves for
+//    kernel's time with one group per wave).  208 workgroups of 4 waves for
 //    N = 13312 fit the GPU in one round.
 //  * Both operands are in the tiled MX layout.  Per 128-element stage each
 //    lane loads its row's entries of the four planes of half h (16 + 8 + 8 +
@@ -53,13 +53,15 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kSkWaves = 8;
+constexpr int kSkWaves = 4;  // 32 stages per wave at K = 16384, S = 16: 8 waves of 16 stages
+                              // spend a larger share of each stream filling and draining the window
 constexpr int kSkThreads = 64 * kSkWaves;
 constexpr int kSkGroups = 2;  // 32-feature weight groups per workgroup (and per wave)
-constexpr int kWindow = 4;    // stages of loads in flight per wave (two waves per SIMD fit)
-constexpr int kLdsStages = 16;  // stages per wave whose scales fit the wave's LDS slice
+constexpr int kWindow = 4;    // stages of loads in flight per wave
+constexpr int kLdsStages = 32;  // stages per wave whose scales fit the wave's LDS slice
 constexpr int kRecW = 2 * kChunkScales;  // per stage: both groups' weight scales (2 x 128 B)
 constexpr int kRecX = kChunkScales / 2;  // per stage: token rows 0..15's activation scales
+static_assert(kLdsStages % 16 == 0, "scale records load 4 (weights) and 16 (activations) stages per load");
 
 // One operand pair of a stage as loaded: the lane's entries of planes A, L,
 // H and B of half h (block 2h = A + L, block 2h+1 = H + B).  The window keeps
@@ -216,8 +218,11 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
 #pragma unroll
       for (int r = 0; r < kLdsStages / 4; ++r)
         rw[r] = *reinterpret_cast<const u32x4*>(wsb + (int64_t)(s_first + min(4 * r + (lane >> 4), nst - 1)) * ws_step);
-      const u32x4 rx = *reinterpret_cast<const u32x4*>(
-          g.x_scales + (int64_t)(s_first + min(lane >> 2, nst - 1)) * kChunkScales + (lane & 3) * 16);
+      u32x4 rx[kLdsStages / 16];
+#pragma unroll
+      for (int r = 0; r < kLdsStages / 16; ++r)
+        rx[r] = *reinterpret_cast<const u32x4*>(
+            g.x_scales + (int64_t)(s_first + min(16 * r + (lane >> 2), nst - 1)) * kChunkScales + (lane & 3) * 16);
       int wst[kWindow];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -229,7 +234,9 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
 #pragma unroll
       for (int r = 0; r < kLdsStages / 4; ++r)
         *reinterpret_cast<u32x4*>(&scw[wave][4 * r + (lane >> 4)][(lane & 15) * 16]) = rw[r];
-      *reinterpret_cast<u32x4*>(&scx[wave][lane >> 2][(lane & 3) * 16]) = rx;
+#pragma unroll
+      for (int r = 0; r < kLdsStages / 16; ++r)
+        *reinterpret_cast<u32x4*>(&scx[wave][16 * r + (lane >> 2)][(lane & 3) * 16]) = rx[r];
 #pragma unroll
       for (int k = 0; k < kWindow; ++k) load_scales(wst[k], win[k]);
     }

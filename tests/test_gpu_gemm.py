@@ -339,9 +339,9 @@ def test_splitk_small(m, splits, w_fmt):
 
 @pytest.mark.parametrize("splits", [6, 12])
 def test_splitk_uneven_chunks_per_wave(splits):
-    """24 stages in 6 or 12 chunks of 4 or 2 stages: with eight waves per
-    workgroup, waves 0..5 get one or two chunks and waves 6 and 7 none (S = 6
-    takes the LDS-scale path, S = 12 the per-stage-scale path)."""
+    """24 stages in 6 or 12 chunks of 4 or 2 stages: with four waves per
+    workgroup, waves 0..2 get two chunks and wave 3 none (S = 6, the LDS-scale
+    path), or every wave three (S = 12, the per-stage-scale path)."""
     m, n, k = 16, 96, 3072
     a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", "e3m2", seed=43)
     wq = _gpu_weights(w, "e3m2", qw)
