@@ -189,7 +189,7 @@ def _src_type(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported source dtype {t.dtype}; expected bfloat16 or float32")
 
 
-def _require_cuda(*ts: torch.Tensor) -> torch.device:
+def _require_cuda(*ts: torch.Tensor | None) -> torch.device:
     dev = None
     for t in ts:
         if t is None:
@@ -200,6 +200,22 @@ def _require_cuda(*ts: torch.Tensor) -> torch.device:
         if t.device != dev:
             raise ValueError("all tensors must be on the same device")
     return dev
+
+
+def _mx_parts(x: MXTensor | None) -> tuple[torch.Tensor | None, torch.Tensor | None]:
+    return (x.codes, x.scales) if x is not None else (None, None)
+
+
+def _check_workspace(workspace: torch.Tensor | None) -> None:
+    """A caller-supplied workspace is a contiguous uint8 buffer: its numel()
+    is the byte count handed to the library."""
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+
+
+def _check_plain_out(out: torch.Tensor, dtype: torch.dtype, m: int, n: int) -> None:
+    if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be a [{m}, {n}] {dtype} tensor with unit stride along its rows")
 
 
 def _check_mx(x: MXTensor, name: str, layout: str | None = None) -> None:
@@ -293,21 +309,30 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
             raise ValueError("a must be [m, k] with unit stride along K")
         a_src, a_codes, a_scales, af, lda, m = a, None, None, _fmt(a_fmt), a.stride(0), a.shape[0]
         src_type = _src_type(a)
-    dev = _require_cuda(a_src, a_codes, w.codes)
     kind = OUT_KINDS[out_kind]
+    if kind == MX_OUT_MX and out is not None and not isinstance(out, MXTensor):
+        raise ValueError("out_kind='mx' needs an MXTensor out")
+    if kind != MX_OUT_MX and isinstance(out, MXTensor):
+        raise ValueError(f"out_kind={out_kind!r} needs a tensor out")
+    # every shape / dtype check first, then one device check over every buffer
+    _check_workspace(workspace)
+    dtype = torch.float32 if kind == MX_OUT_F32 else torch.bfloat16
+    if out is not None:
+        if kind == MX_OUT_MX:
+            _check_mx(out, "out", "tiled")
+            if out.rows != m or out.k != n_out or out.fmt != out_fmt:
+                raise ValueError(f"out must be an [m, n_out] {out_fmt} MX matrix")
+        else:
+            _check_plain_out(out, dtype, m, n_out)
+    dev = _require_cuda(a_src, a_codes, a_scales, w.codes, w.scales, *_mx_parts(out if kind == MX_OUT_MX else None),
+                        out if kind != MX_OUT_MX else None, workspace)
     if kind == MX_OUT_MX:
         if out is None:
             out = MXTensor.empty(m, n_out, out_fmt, "tiled", dev)
-        _check_mx(out, "out", "tiled")
-        if out.rows != m or out.k != n_out:
-            raise ValueError("out must be an [m, n_out] MX matrix")
         out_data, out_scales, ldo = out.codes, out.scales, 0
     else:
-        dtype = torch.float32 if kind == MX_OUT_F32 else torch.bfloat16
         if out is None:
             out = torch.empty((m, n_out), dtype=dtype, device=dev)
-        if out.dtype != dtype or out.dim() != 2 or out.stride(1) != 1 or tuple(out.shape) != (m, n_out):
-            raise ValueError("out must be [m, n_out] of the output dtype with unit stride")
         out_data, out_scales, ldo = out, None, out.stride(0)
     need = mx_gemm_workspace_size(m, n, k, a_src is not None, 0)
     if workspace is None and need > 0:
@@ -335,15 +360,22 @@ def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kin
     if isinstance(a, MXTensor):
         _check_mx(a, "a", "tiled")
         a_src, a_codes, a_scales, af, lda, m = None, a.codes, a.scales, _fmt(a.fmt), 0, a.rows
+        if a.k != k:
+            raise ValueError("A and W disagree on K")
         src_type = MX_SRC_BF16
     else:
         if a.dim() != 2 or a.stride(1) != 1 or a.shape[1] != k:
             raise ValueError("a must be [m, k] with unit stride along K")
         a_src, a_codes, a_scales, af, lda, m = a, None, None, _fmt(a_fmt), a.stride(0), a.shape[0]
         src_type = _src_type(a)
-    dev = _require_cuda(a_src, a_codes, w.codes)
     kind = OUT_KINDS[out_kind]
+    if kind == MX_OUT_MX:
+        raise ValueError("mx_gemm_splitk writes fp32 or bf16 output")
+    _check_workspace(workspace)
     dtype = torch.float32 if kind == MX_OUT_F32 else torch.bfloat16
+    if out is not None:
+        _check_plain_out(out, dtype, m, n)
+    dev = _require_cuda(a_src, a_codes, a_scales, w.codes, w.scales, out, workspace)
     if out is None:
         out = torch.empty((m, n), dtype=dtype, device=dev)
     need = mx_gemm_workspace_size(m, n, k, a_src is not None, splits)

@@ -89,6 +89,53 @@ int check_gemm_common(const void* a_src, int32_t a_src_type, int64_t lda, const 
   return MX_OK;
 }
 
+// mx_gemm_splitk's host-side checks (everything but the workspace).
+int check_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
+                 int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n,
+                 int64_t k, int32_t splits, int32_t out_kind, const void* out, int64_t ldo) {
+  int st = check_gemm_common(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k);
+  if (st != MX_OK) return st;
+  if (m > 16) return MX_ERR_SHAPE;
+  if (splits < 1) return MX_ERR_SHAPE;
+  if (!fp6_fmt(a_fmt) || !fp6_fmt(w_fmt)) return MX_ERR_UNSUPPORTED;
+  if (out_kind != MX_OUT_F32 && out_kind != MX_OUT_BF16) return MX_ERR_FORMAT;
+  if (!out) return MX_ERR_NULL;
+  if (ldo < n) return MX_ERR_SHAPE;
+  if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
+  if (splits > kMaxSplits || k % (kTileStageK * (int64_t)splits) != 0) return MX_ERR_UNSUPPORTED;
+  return MX_OK;
+}
+
+// The split-K launch after validation: in-call quantization into ws (when
+// a_src is given), then the split-K kernel.
+int run_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
+               int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n,
+               int64_t k, int32_t splits, int32_t out_kind, void* out, int64_t ldo, uint8_t* ws, hipStream_t stream) {
+  const uint8_t* xc = static_cast<const uint8_t*>(a_codes);
+  const uint8_t* xs = a_scales;
+  if (a_src && k > 0) {
+    const TiledWs w = tiled_ws(m, k, 6);
+    const hipError_t e =
+        launch_quantize_tiled(a_src, a_src_type, m, k, lda, a_fmt, ws + w.codes_off, ws + w.scales_off, stream);
+    if (e != hipSuccess) return MX_ERR_HIP;
+    xc = ws + w.codes_off;
+    xs = ws + w.scales_off;
+  }
+  SplitKArgs g;
+  g.x_codes = xc;
+  g.x_scales = xs;
+  g.w_codes = static_cast<const uint8_t*>(w_codes);
+  g.w_scales = w_scales;
+  g.out = out;
+  g.ldo = ldo;
+  g.M = (int32_t)m;
+  g.N = (int32_t)n;
+  g.K = (int32_t)k;
+  g.splits = splits;
+  g.gw = (int32_t)ceil_div(n, kTileGroupRows);
+  return hip_status(launch_gemm_splitk(g, a_fmt, w_fmt, out_kind, stream));
+}
+
 }  // namespace
 
 namespace mxg {
@@ -282,45 +329,15 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
                    int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n,
                    int64_t k, int32_t splits, int32_t out_kind, void* out, int64_t ldo, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
-  int st = check_gemm_common(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k);
+  int st = check_splitk(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k, splits,
+                        out_kind, out, ldo);
   if (st != MX_OK) return st;
-  if (m > 16) return MX_ERR_SHAPE;
-  if (splits < 1) return MX_ERR_SHAPE;
-  if (!fp6_fmt(a_fmt) || !fp6_fmt(w_fmt)) return MX_ERR_UNSUPPORTED;
-  if (out_kind != MX_OUT_F32 && out_kind != MX_OUT_BF16) return MX_ERR_FORMAT;
-  if (!out) return MX_ERR_NULL;
-  if (ldo < n) return MX_ERR_SHAPE;
-  if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
-  if (splits > kMaxSplits || k % (kTileStageK * (int64_t)splits) != 0) return MX_ERR_UNSUPPORTED;
   const size_t need = mx_gemm_workspace_size(m, n, k, a_src != nullptr, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MX_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, kWsAlign)) return MX_ERR_ALIGN;
   if (m == 0 || n == 0) return MX_OK;
-
-  uint8_t* base = static_cast<uint8_t*>(workspace);
-  const uint8_t* xc = static_cast<const uint8_t*>(a_codes);
-  const uint8_t* xs = a_scales;
-  if (a_src && k > 0) {
-    const TiledWs w = tiled_ws(m, k, 6);
-    const hipError_t e = launch_quantize_tiled(a_src, a_src_type, m, k, lda, a_fmt, base + w.codes_off,
-                                               base + w.scales_off, stream);
-    if (e != hipSuccess) return MX_ERR_HIP;
-    xc = base + w.codes_off;
-    xs = base + w.scales_off;
-  }
-  SplitKArgs g;
-  g.x_codes = xc;
-  g.x_scales = xs;
-  g.w_codes = static_cast<const uint8_t*>(w_codes);
-  g.w_scales = w_scales;
-  g.out = out;
-  g.ldo = ldo;
-  g.M = (int32_t)m;
-  g.N = (int32_t)n;
-  g.K = (int32_t)k;
-  g.splits = splits;
-  g.gw = (int32_t)ceil_div(n, kTileGroupRows);
-  return hip_status(launch_gemm_splitk(g, a_fmt, w_fmt, out_kind, stream));
+  return run_splitk(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k, splits,
+                    out_kind, out, ldo, static_cast<uint8_t*>(workspace), stream);
 }
 
 }  // extern "C"

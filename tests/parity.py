@@ -183,10 +183,17 @@ def check_mx_epilogue(gpu_codes: np.ndarray, gpu_scales: np.ndarray, c: np.ndarr
     of a power of two, the scale byte may differ by one.  Everything else must
     match exactly.  Returns counts of exact and tolerated differences.
     """
+    g32, delta = mx_epilogue_target(c, s, gelu)
+    return check_mx_values(gpu_codes, gpu_scales, g32, delta, fmt)
+
+
+def mx_epilogue_target(c: np.ndarray, s: np.ndarray, gelu: bool) -> tuple[np.ndarray, np.ndarray]:
+    """The oracle's fp32 epilogue value fp32(GELU(C)) (or fp32(C)) and the
+    distance delta the device's fp32 value may lie from it."""
     g64 = O.gelu_tanh(c) if gelu else c
     g32 = g64.astype(np.float32).astype(np.float64)
     delta = O.GEMM_RTOL * s * (GELU_DERIV_MAX if gelu else 1.0) + (gelu_eval_slack(c, g32) if gelu else 0.0)
-    return check_mx_values(gpu_codes, gpu_scales, g32, delta, fmt)
+    return g32, delta
 
 
 def check_mx_values(gpu_codes: np.ndarray, gpu_scales: np.ndarray, g32: np.ndarray, delta: np.ndarray,
@@ -307,3 +314,35 @@ def assert_close_window(gpu: np.ndarray, c: np.ndarray, s: np.ndarray, wb: np.nd
         raise AssertionError(f"{what}: {len(bad)} of {ok.size} outputs outside the bound; first {i}: gpu {gpu[i]!r} "
                              f"oracle {c[i]!r} S {s[i]!r} window {wb[i]!r}")
     return int(np.count_nonzero(d > base))
+
+
+def check_chain_fc2(got: np.ndarray, gpu_h_codes: np.ndarray, gpu_h_scales: np.ndarray, codes_o: np.ndarray,
+                    scales_o: np.ndarray, g32: np.ndarray, delta: np.ndarray, dw2: np.ndarray, what: str,
+                    fmt: str = "e2m3") -> dict:
+    """The second GEMM of an MLP chain, held to the full GEMM bar on every
+    checked output.
+
+    1. The GPU's intermediate rows (packed codes and scales, as the first GEMM
+       wrote them) must pass the boundary-aware rule against the oracle's
+       fp32 intermediate g32 with its allowed distance delta: an element may
+       differ from the oracle's code only by one step across a rounding
+       midpoint within delta, a scale byte by one at a power of two.
+    2. fc2's expected value is the exact product (float64) of that verified
+       intermediate with the weights: the oracle's own intermediate plus the
+       exact effect of the legitimately different elements.  Every output
+       must meet the bf16 bar against it; no fraction of outputs is excused.
+    Returns the intermediate's statistics and how many outputs needed the
+    bf16 cancellation clause."""
+    stats = check_mx_values(gpu_h_codes, gpu_h_scales, g32, delta, fmt)
+    n = codes_o.shape[1]
+    dh_o = O.dequantize(codes_o, scales_o, fmt)
+    dh_g = O.dequantize(O.unpack(gpu_h_codes, n, fmt), gpu_h_scales, fmt)
+    c2, s2 = O.gemm_ref(dh_o, dw2)
+    diff = dh_g - dh_o
+    rows = np.nonzero(diff.any(axis=1))[0]
+    if rows.size:
+        c2[rows] += diff[rows] @ dw2.T          # = dh_g @ dw2.T on those rows, exactly in float64
+        s2[rows] = np.abs(dh_g[rows]) @ np.abs(dw2).T
+    stats["fc2_second_clause"] = assert_bf16_close(got, c2, s2, what)
+    stats["rows_with_flips"] = int(rows.size)
+    return stats

@@ -264,3 +264,55 @@ def test_binding_refuses_cpu_tensors(L):
     import torch
     with pytest.raises(ValueError):
         mx.mx_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
+def _cpu_mx(rows, k, fmt="e2m3"):
+    import torch
+    return B.MXTensor(torch.zeros(mx.mx_packed_bytes(rows, k, "tiled", 0, fmt), dtype=torch.uint8),
+                      torch.zeros(mx.mx_packed_bytes(rows, k, "tiled", 1, fmt), dtype=torch.uint8), fmt, rows, k)
+
+
+@pytest.mark.parametrize("fn", ["gemm", "splitk"])
+def test_binding_checks_out_workspace_and_k_before_launch(L, fn):
+    """Every malformed argument of the Python wrappers is refused with a
+    ValueError naming it, before any pointer reaches the library: a wrong
+    out dtype, rank, shape or stride (which would be written out of bounds),
+    a K mismatch between MX operands (read past A), a non-uint8 workspace
+    (its numel would not be its byte count), and CPU buffers anywhere."""
+    import torch
+    m, n, k = 16, 64, 256
+    w = _cpu_mx(n, k)
+    a = _cpu_mx(m, k)
+    call = (lambda **kw: mx.mx_gemm(a, w, out_kind="f32", **kw)) if fn == "gemm" else \
+        (lambda **kw: mx.mx_gemm_splitk(a, w, 2, out_kind="f32", **kw))
+    bad_outs = [torch.zeros(m, n, dtype=torch.bfloat16),          # bf16 buffer for fp32 output
+                torch.zeros(m, n - 1, dtype=torch.float32),       # too narrow
+                torch.zeros(m - 1, n, dtype=torch.float32),       # too few rows
+                torch.zeros(n, m, dtype=torch.float32).t(),       # column stride
+                torch.zeros(m * n, dtype=torch.float32)]          # 1-D
+    for o in bad_outs:
+        with pytest.raises(ValueError, match="out must be"):
+            call(out=o)
+    with pytest.raises(ValueError, match="workspace"):
+        call(workspace=torch.zeros(64, dtype=torch.float32))
+    # right shapes, CPU buffers: refused by the device check
+    with pytest.raises(ValueError, match="GPU"):
+        call(out=torch.zeros(m, n, dtype=torch.float32))
+    # K mismatch between the MX activations and the weights
+    a_short = _cpu_mx(m, k - 128)
+    with pytest.raises(ValueError, match="disagree on K"):
+        if fn == "gemm":
+            mx.mx_gemm(a_short, w, out_kind="f32")
+        else:
+            mx.mx_gemm_splitk(a_short, w, 2, out_kind="f32")
+    if fn == "splitk":
+        with pytest.raises(ValueError, match="fp32 or bf16"):
+            mx.mx_gemm_splitk(a, w, 2, out_kind="mx")
+    else:
+        # MX output: an out of the wrong kind or element format
+        with pytest.raises(ValueError):
+            mx.mx_gemm(a, w, out_kind="mx", out=torch.zeros(m, n, dtype=torch.float32))
+        with pytest.raises(ValueError, match="MX matrix"):
+            mx.mx_gemm(a, w, out_kind="mx", out_fmt="e2m3", out=_cpu_mx(m, n, "e3m2"))
+        with pytest.raises(ValueError, match="MX matrix"):
+            mx.mx_gemm(a, w, out_kind="mx", out=_cpu_mx(m, n - 32))

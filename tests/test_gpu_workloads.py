@@ -19,7 +19,8 @@ import microscaled_precision_gemm_amd as mx
 from microscaled_precision_gemm_amd import synthetic as syn
 from oracle import mx_oracle as O
 from tests.parity import (assert_bf16_close, assert_close_window, assert_fp32_close, bf16_tensor_to_f64,
-                          check_mx_epilogue, mfma_window_bound, mx_rows_view, say, to_np)
+                          check_chain_fc2, check_mx_epilogue, mfma_window_bound, mx_epilogue_target, mx_rows_view,
+                          say, swiglu_bound, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -141,8 +142,9 @@ def test_mlp_chain_full_size():
     """The bench's whole step (quantize x, fc1 GELU -> E2M3, fc2 bf16) at full
     size.  fc2's output on sampled tokens is checked against the oracle's own
     chain: the oracle computes those tokens' whole E2M3 intermediate itself.
-    An intermediate element that legitimately rounds one step the other way
-    moves an output by at most that step times |w|."""
+    The GPU's own intermediate on those tokens must pass the boundary-aware
+    rule, and every sampled output meets the bf16 bar against the exact
+    product of that verified intermediate."""
     fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
     x, w1, w2 = syn.make_a(fc1), syn.make_w(fc1), syn.make_w(fc2)
     rng = np.random.default_rng([79, fc1.index])
@@ -159,16 +161,13 @@ def test_mlp_chain_full_size():
     mx.mx_gemm(h, w2q, out_kind="bf16", out=y)
     torch.cuda.synchronize()
     got = bf16_tensor_to_f64(y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)])
+    gc, gs = mx_rows_view(h)
     dw1 = _deq_rows(w1, np.arange(fc1.n), "e2m3")
-    codes_o, scales_o, *_ = O.fc1_gelu_mx_ref(_deq_rows(x, rows, "e2m3"), dw1)
-    dh = O.dequantize(codes_o, scales_o, "e2m3")
-    dw2 = _deq_rows(w2, cols, "e2m3")
-    c2, s2 = O.gemm_ref(dh, dw2)
-    step = np.ldexp(1.0, scales_o.astype(np.int64) - 127 - 2)  # one E2M3 step is at most 2^(shared - 2)
-    flip_bound = np.repeat(step, 32, axis=1) @ np.abs(dw2).T
-    ok, _ = O.check_bf16(got, c2, s2)
-    assert ok.mean() > 0.99, ok.mean()
-    assert np.all(np.abs(got - c2) <= flip_bound + O.GEMM_RTOL * s2 + O.ulp_bf16(c2))
+    codes_o, scales_o, c1, s1, _ = O.fc1_gelu_mx_ref(_deq_rows(x, rows, "e2m3"), dw1)
+    g32, delta = mx_epilogue_target(c1, s1, True)
+    stats = check_chain_fc2(got, gc[rows], gs[rows], codes_o, scales_o, g32, delta, _deq_rows(w2, cols, "e2m3"),
+                            "MLP chain fc2")
+    print("MLP chain", stats)
 
 
 @pytest.mark.parametrize("m", [16, 8])
@@ -242,7 +241,7 @@ def test_swiglu_fc1_full_size_mx():
 def test_swiglu_mlp_chain_full_size():
     """The SwiGLU MLP step: quantize x, stacked gate/up GEMM with SwiGLU -> E2M3
     (8192 features), down projection to bf16, at full size; sampled tokens of the
-    output against the oracle's own chain (as for the GELU chain)."""
+    output against the oracle's chain under the same rule as the GELU chain."""
     w1w, w2w = syn.WORKLOADS["sw_fc1"], syn.WORKLOADS["sw_fc2"]
     h = w1w.n // 2
     x, w1, w2 = syn.make_a(w1w), syn.make_w(w1w), syn.make_w(w2w)
@@ -257,12 +256,10 @@ def test_swiglu_mlp_chain_full_size():
     y = mx.mx_gemm(hq, w2q, out_kind="bf16")
     torch.cuda.synchronize()
     got = bf16_tensor_to_f64(y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(dev)])
-    codes_o, scales_o, *_ = O.fc1_swiglu_mx_ref(_deq_rows(x, rows, "e2m3"), _deq_rows(w1, np.arange(w1w.n), "e2m3"))
-    dh = O.dequantize(codes_o, scales_o, "e2m3")
-    dw2 = _deq_rows(w2, cols, "e2m3")
-    c2, s2 = O.gemm_ref(dh, dw2)
-    step = np.ldexp(1.0, scales_o.astype(np.int64) - 127 - 2)
-    flip_bound = np.repeat(step, 32, axis=1) @ np.abs(dw2).T
-    ok, _ = O.check_bf16(got, c2, s2)
-    assert ok.mean() > 0.99, ok.mean()
-    assert np.all(np.abs(got - c2) <= flip_bound + O.GEMM_RTOL * s2 + O.ulp_bf16(c2))
+    gc, gs = mx_rows_view(hq)
+    codes_o, scales_o, out, g, u, sg, su = O.fc1_swiglu_mx_ref(_deq_rows(x, rows, "e2m3"),
+                                                              _deq_rows(w1, np.arange(w1w.n), "e2m3"))
+    o32 = out.astype(np.float32).astype(np.float64)
+    stats = check_chain_fc2(got, gc[rows], gs[rows], codes_o, scales_o, o32, swiglu_bound(g, u, sg, su, o32),
+                            _deq_rows(w2, cols, "e2m3"), "SwiGLU MLP chain down projection")
+    print("SwiGLU MLP chain", stats)
