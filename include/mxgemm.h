@@ -85,7 +85,9 @@
  *   - every call is asynchronous on the given HIP stream; the library never
  *     allocates, frees or synchronizes device memory, and keeps no mutable
  *     global state, so calls on different streams may run concurrently as
- *     long as their buffers do not overlap;
+ *     long as their buffers do not overlap.  The one exception is
+ *     mx_gemm_splitk_noalloc, whose calls on one GPU share a static device
+ *     scratch array (see there);
  *   - argument errors are detected on the host before anything is launched
  *     and return a negative status; nothing is written in that case;
  *   - MX_ERR_HIP reports a failed launch (hipGetLastError); a fault inside a
@@ -113,6 +115,7 @@ extern "C" {
 #define MX_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than required           */
 #define MX_ERR_UNSUPPORTED (-6) /* valid request with no kernel variant              */
 #define MX_ERR_HIP (-7)         /* a kernel launch failed                            */
+#define MX_ERR_SCRATCH (-8)     /* larger than mx_gemm_splitk_noalloc's static scratch */
 
 /* Element formats.  The values equal the format codes of the gfx950 scaled
  * f8f6f4 MFMA instructions. */
@@ -307,6 +310,31 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
                    const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
                    int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t splits, int32_t out_kind, void* out,
                    int64_t ldo, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mx_gemm_splitk_noalloc - mx_gemm_splitk for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It takes no workspace and allocates
+ * nothing (no hipMalloc / hipFree, no allocating library routine).  The
+ * activations it quantizes inside the call go to a file-scope device array
+ * of the library (1.5625 MiB: one 32-row group of k <= MX_NOALLOC_MAX_K
+ * 6-bit codes and their scales), which each GPU the library runs on holds
+ * until the process ends; its address is looked up once per device, on the
+ * first call with that device current.  The caller still owns a_src / the
+ * quantized operands, the weights and out.
+ *
+ * Arguments, results and errors as mx_gemm_splitk without the workspace
+ * (the results are bit-identical to it), plus MX_ERR_SCRATCH when
+ * k > MX_NOALLOC_MAX_K.  Every call on one GPU shares that GPU's array and
+ * leaves its last contents there: calls that overlap in time on one GPU
+ * (different streams, or host threads without ordering) race on it and must
+ * be serialized by the caller; calls on one stream are ordered.
+ */
+#define MX_NOALLOC_MAX_K 65536
+int mx_gemm_splitk_noalloc(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+                           const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
+                           int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t splits, int32_t out_kind,
+                           void* out, int64_t ldo, hipStream_t stream);
 
 /*
  * mx_gemm_workspace_size - bytes of workspace needed by mx_gemm (splits == 0)

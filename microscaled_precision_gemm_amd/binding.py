@@ -26,6 +26,8 @@ MX_ERR_ALIGN = -4
 MX_ERR_WORKSPACE = -5
 MX_ERR_UNSUPPORTED = -6
 MX_ERR_HIP = -7
+MX_ERR_SCRATCH = -8
+MX_NOALLOC_MAX_K = 65536
 
 MX_FMT_E4M3 = 0
 MX_FMT_E5M2 = 1
@@ -51,7 +53,8 @@ EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH, "swiglu": MX_EP
 LAYOUTS = {"rows": MX_LAYOUT_ROWS, "tiled": MX_LAYOUT_TILED}
 
 EXPORTED = ("mx_quantize", "mx_rmsnorm_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_default_config",
-            "mx_gemm_with_config", "mx_gemm_splitk", "mx_gemm_workspace_size", "mx_status_string", "mx_version")
+            "mx_gemm_with_config", "mx_gemm_splitk", "mx_gemm_splitk_noalloc", "mx_gemm_workspace_size",
+            "mx_status_string", "mx_version")
 
 
 class MXGemmConfig(ctypes.Structure):
@@ -106,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.mx_gemm_splitk.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32,
                                  c_i32, c_p, c_i64, c_p, c_sz, c_p]
     L.mx_gemm_splitk.restype = ctypes.c_int
+    L.mx_gemm_splitk_noalloc.argtypes = L.mx_gemm_splitk.argtypes[:16] + [c_p]
+    L.mx_gemm_splitk_noalloc.restype = ctypes.c_int
     L.mx_gemm_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i32]
     L.mx_gemm_workspace_size.restype = c_sz
     L.mx_status_string.argtypes = [ctypes.c_int]
@@ -352,9 +357,13 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
 
 
 def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kind: str = "bf16",
-                   a_fmt: str = "e2m3", out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                   a_fmt: str = "e2m3", out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   noalloc: bool = False):
     """Skinny C = A W^T (m <= 16) with K split into ``splits`` chunks, fp32
-    partials summed in a fixed order."""
+    partials summed in a fixed order.  noalloc=True calls
+    mx_gemm_splitk_noalloc instead (no workspace: the library's static
+    scratch; ``out`` must then be given for the call itself to allocate
+    nothing)."""
     _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
     if isinstance(a, MXTensor):
@@ -378,6 +387,14 @@ def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kin
     dev = _require_cuda(a_src, a_codes, a_scales, w.codes, w.scales, out, workspace)
     if out is None:
         out = torch.empty((m, n), dtype=dtype, device=dev)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("mx_gemm_splitk_noalloc takes no workspace")
+        st = lib().mx_gemm_splitk_noalloc(_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af,
+                                          _ptr(w.codes), _ptr(w.scales), _fmt(w.fmt), m, n, k, splits, kind, _ptr(out),
+                                          out.stride(0), _stream(dev))
+        _check(st, "mx_gemm_splitk_noalloc")
+        return out
     need = mx_gemm_workspace_size(m, n, k, a_src is not None, splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

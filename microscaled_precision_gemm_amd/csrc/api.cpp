@@ -4,8 +4,25 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "mx_device.h"
+
+// ---- the allocation-free split-K entry point's scratch.  The activations
+// that mx_gemm_splitk_noalloc quantizes inside the call go to this
+// file-scope device array instead of a caller workspace: at most 16 rows
+// (one 32-row group of the tiled layout) of k <= MX_NOALLOC_MAX_K 6-bit
+// codes and their scales.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code the array's name only stands in for
+// the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and that pointer is what
+// the kernels receive.  The quantizer rewrites every byte the GEMM reads
+// (padding included) on each call, so nothing needs clearing between calls.
+constexpr size_t kNoAllocScratchBytes =
+    (size_t)(MX_NOALLOC_MAX_K / 128) * 3072 + (size_t)(MX_NOALLOC_MAX_K / 128) * 128;  // codes, then scales
+static_assert((MX_NOALLOC_MAX_K / 128) * 3072 % 256 == 0, "the scales start 256-byte aligned, as in a workspace");
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -136,6 +153,24 @@ int run_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void* a
   return hip_status(launch_gemm_splitk(g, a_fmt, w_fmt, out_kind, stream));
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MX_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MX_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MX_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MX_OK;
+}
+
 }  // namespace
 
 namespace mxg {
@@ -167,6 +202,8 @@ const char* mx_status_string(int status) {
     case MX_ERR_WORKSPACE: return "workspace missing or smaller than mx_gemm_workspace_size()";
     case MX_ERR_UNSUPPORTED: return "valid request without a kernel variant";
     case MX_ERR_HIP: return "HIP kernel launch failed";
+    case MX_ERR_SCRATCH:
+      return "request larger than the static scratch of mx_gemm_splitk_noalloc (k > MX_NOALLOC_MAX_K)";
     default: return "unknown status";
   }
 }
@@ -338,6 +375,26 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
   if (m == 0 || n == 0) return MX_OK;
   return run_splitk(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k, splits,
                     out_kind, out, ldo, static_cast<uint8_t*>(workspace), stream);
+}
+
+int mx_gemm_splitk_noalloc(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+                           const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
+                           int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t splits, int32_t out_kind,
+                           void* out, int64_t ldo, hipStream_t stream) {
+  int st = check_splitk(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k, splits,
+                        out_kind, out, ldo);
+  if (st != MX_OK) return st;
+  if (k > MX_NOALLOC_MAX_K) return MX_ERR_SCRATCH;
+  // what run_splitk writes: one 32-row group of 6-bit codes, then scales
+  if (a_src && tiled_ws(m, k, 6).end > kNoAllocScratchBytes) return MX_ERR_SCRATCH;
+  if (m == 0 || n == 0) return MX_OK;
+  uint8_t* ws = nullptr;
+  if (a_src && k > 0) {
+    st = noalloc_scratch(&ws);
+    if (st != MX_OK) return st;
+  }
+  return run_splitk(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k, splits,
+                    out_kind, out, ldo, ws, stream);
 }
 
 }  // extern "C"

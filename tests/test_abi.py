@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert mx.mx_version() == 400
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert mx.mx_status_string(st) and mx.mx_status_string(st) != "unknown status"
     assert mx.mx_status_string(-99) == "unknown status"
 
@@ -228,6 +228,31 @@ def test_splitk_validation(L):
     assert sk(a_fmt=3) == B.MX_ERR_UNSUPPORTED
     assert sk(a_fmt=0, w_fmt=0) == B.MX_ERR_UNSUPPORTED  # 6-bit types only
     assert sk(m=0) == B.MX_OK
+
+
+def sk_noalloc(**kw):
+    a = dict(a_src=FAKE, a_src_type=0, lda=1 << 17, a_codes=NULL, a_scales=NULL, a_fmt=2, w_codes=FAKE,
+             w_scales=FAKE, w_fmt=3, m=16, n=64, k=4096, splits=8, out_kind=1, out=FAKE, ldo=64, stream=NULL)
+    a.update(kw)
+    return mx.lib().mx_gemm_splitk_noalloc(*a.values())
+
+
+@host_only
+def test_splitk_noalloc_validation(L):
+    """The allocation-free split-K entry point validates like mx_gemm_splitk
+    (on the host, before any HIP call) and refuses a K beyond its static
+    scratch with its own status."""
+    assert B.MX_NOALLOC_MAX_K == 65536
+    assert sk_noalloc(k=B.MX_NOALLOC_MAX_K + 1024) == B.MX_ERR_SCRATCH
+    assert sk_noalloc(k=1 << 20, lda=1 << 20, splits=16) == B.MX_ERR_SCRATCH
+    assert "scratch" in mx.mx_status_string(B.MX_ERR_SCRATCH)
+    assert sk_noalloc(m=17) == B.MX_ERR_SHAPE
+    assert sk_noalloc(splits=3) == B.MX_ERR_UNSUPPORTED
+    assert sk_noalloc(out_kind=2) == B.MX_ERR_FORMAT
+    assert sk_noalloc(out=NULL) == B.MX_ERR_NULL
+    assert sk_noalloc(a_src=FAKE + 8) == B.MX_ERR_ALIGN
+    assert sk_noalloc(a_fmt=3) == B.MX_ERR_UNSUPPORTED
+    assert sk_noalloc(m=0) == B.MX_OK  # nothing to do: no HIP call
 
 
 def test_packed_bytes(L):
