@@ -277,13 +277,33 @@ typedef struct {
                         pair, not MX_EPI_SWIGLU, else MX_ERR_UNSUPPORTED)                     */
 } mx_gemm_config;
 
-/* mx_gemm_default_config - fill *config with the defaults mx_gemm uses. */
+/* mx_gemm_default_config - fill *config with the generic configuration
+ * (group_m 4, xcd_remap 1, tile_n 256, 4 waves): the one every format pair and
+ * epilogue takes. */
 void mx_gemm_default_config(mx_gemm_config* config);
 
 /*
+ * mx_gemm_select_config - fill *config with the configuration mx_gemm uses
+ * for a call of this shape when it is given none (a shape rule, so that a
+ * shape missing from a tuning table does not fall back to the generic
+ * configuration; the Hedra post, section "We tuned before writing custom
+ * kernels", found library GEMMs doing exactly that).  The rule, from timings
+ * of every candidate on the workload shapes on MI355X:
+ *   - FP8 operands, or MX_EPI_SWIGLU: the generic configuration;
+ *   - 6-bit operands with MX_OUT_MX and k <= 4096: tile_n 128, group_m 8;
+ *   - otherwise (4- and 6-bit operands, f32 / bf16 output, or MX output with
+ *     long K): 8 waves, group_m 4.
+ * Arguments as mx_gemm's; nothing is validated (an invalid call still fails
+ * in mx_gemm).
+ */
+void mx_gemm_select_config(int64_t m, int64_t n, int64_t k, int32_t a_fmt, int32_t w_fmt, int32_t epilogue,
+                           int32_t out_kind, mx_gemm_config* config);
+
+/*
  * mx_gemm_with_config - mx_gemm with an explicit launch configuration
- * (NULL = the defaults).  Same arguments, results and errors as mx_gemm,
- * plus MX_ERR_FORMAT for a configuration outside the ranges above.
+ * (NULL = mx_gemm_select_config's choice, which is what mx_gemm uses).  Same
+ * arguments, results and errors as mx_gemm, plus MX_ERR_FORMAT for a
+ * configuration outside the ranges above.
  */
 int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
                         const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     lib,
     mx_gemm,
     mx_gemm_default_config,
+    mx_gemm_select_config,
     mx_gemm_splitk,
     mx_gemm_workspace_size,
     mx_packed_bytes,

@@ -53,7 +53,7 @@ EPILOGUES = {"none": MX_EPI_NONE, "gelu_tanh": MX_EPI_GELU_TANH, "swiglu": MX_EP
 LAYOUTS = {"rows": MX_LAYOUT_ROWS, "tiled": MX_LAYOUT_TILED}
 
 EXPORTED = ("mx_quantize", "mx_rmsnorm_quantize", "mx_packed_bytes", "mx_gemm", "mx_gemm_default_config",
-            "mx_gemm_with_config", "mx_gemm_splitk", "mx_gemm_splitk_noalloc", "mx_gemm_workspace_size",
+            "mx_gemm_select_config", "mx_gemm_with_config", "mx_gemm_splitk", "mx_gemm_splitk_noalloc", "mx_gemm_workspace_size",
             "mx_status_string", "mx_version")
 
 
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.mx_gemm_with_config.restype = ctypes.c_int
     L.mx_gemm_default_config.argtypes = [ctypes.POINTER(MXGemmConfig)]
     L.mx_gemm_default_config.restype = None
+    L.mx_gemm_select_config.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(MXGemmConfig)]
+    L.mx_gemm_select_config.restype = None
     L.mx_gemm_splitk.argtypes = [c_p, c_i32, c_i64, c_p, c_p, c_i32, c_p, c_p, c_i32, c_i64, c_i64, c_i64, c_i32,
                                  c_i32, c_p, c_i64, c_p, c_sz, c_p]
     L.mx_gemm_splitk.restype = ctypes.c_int
@@ -286,8 +288,19 @@ def mx_rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor | None = None, shif
 
 
 def mx_gemm_default_config() -> MXGemmConfig:
+    """The generic launch configuration (every format pair and epilogue)."""
     c = MXGemmConfig()
     lib().mx_gemm_default_config(ctypes.byref(c))
+    return c
+
+
+def mx_gemm_select_config(m: int, n: int, k: int, a_fmt: str = "e2m3", w_fmt: str = "e2m3", epilogue: str = "none",
+                          out_kind: str = "bf16") -> MXGemmConfig:
+    """The configuration mx_gemm uses for this call shape when given none
+    (the library's shape rule)."""
+    c = MXGemmConfig()
+    lib().mx_gemm_select_config(m, n, k, _fmt(a_fmt), _fmt(w_fmt), EPILOGUES[epilogue], OUT_KINDS[out_kind],
+                                ctypes.byref(c))
     return c
 
 
@@ -299,7 +312,7 @@ def mx_gemm(a: torch.Tensor | MXTensor, w: MXTensor, out_kind: str = "bf16", epi
     out_kind="mx"; n_out = n, or n / 2 for epilogue="swiglu" (``w`` then holds
     stacked gate/up rows, see include/mxgemm.h).  ``config``: the tile order
     and shape (an MXGemmConfig or (group_m, xcd_remap[, tile_n[, waves]]));
-    None = the library default."""
+    None = the library's shape rule (mx_gemm_select_config)."""
     _check_mx(w, "w", "tiled")
     n, k = w.rows, w.k
     n_out = n // 2 if epilogue == "swiglu" else n

@@ -21,6 +21,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmxgemm.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# measurement only (bench.py): the matrix-instruction rate with nothing else in the loop
+PROBE_SOURCE = "mfma_ceiling.hip"
+PROBE_PATH = os.path.join(PKG, "libmxprobe.so")
 
 SOURCES = ["api.cpp", "quantize.hip", "gemm_we2m3_e2m3.hip", "gemm_we3m2_e2m3.hip", "gemm_we2m3_e3m2.hip",
            "gemm_we2m1_e2m1.hip", "gemm_wfp8_fp8.hip", "splitk.hip", "producer.hip"]
@@ -59,17 +62,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libmxgemm.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs: list[str], path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950, link libmxgemm.so (and the
+    measurement probe libmxprobe.so); returns the library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + [PROBE_SOURCE]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], PROBE_PATH)
     return LIB_PATH
 
 

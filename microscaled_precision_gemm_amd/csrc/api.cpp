@@ -271,6 +271,27 @@ void mx_gemm_default_config(mx_gemm_config* config) {
   config->waves = 4;
 }
 
+void mx_gemm_select_config(int64_t m, int64_t n, int64_t k, int32_t a_fmt, int32_t w_fmt, int32_t epilogue,
+                           int32_t out_kind, mx_gemm_config* config) {
+  if (!config) return;
+  mx_gemm_default_config(config);
+  (void)m;
+  (void)n;
+  const bool fp8 = fmt_bits(a_fmt) == 8 || fmt_bits(w_fmt) == 8;
+  if (fp8 || epilogue == MX_EPI_SWIGLU) return;  // 8 waves slow FP8 down; the SwiGLU pairing takes 4 waves
+  if (out_kind == MX_OUT_MX && fp6_fmt(a_fmt) && fp6_fmt(w_fmt) && k <= 4096) {
+    // short K with the MX epilogue: the per-tile cost (first stages' fill,
+    // GELU / MX conversion, stores) weighs most; two 128-feature workgroups
+    // per CU overlap it with each other's matrix work
+    config->group_m = 8;
+    config->tile_n = 128;
+    return;
+  }
+  // plain outputs of the 4- and 6-bit types: two waves per SIMD hide the
+  // operand reads from LDS behind the other wave's matrix work
+  config->waves = 8;
+}
+
 int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
             int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n, int64_t k,
             int32_t epilogue, int32_t out_kind, void* out, int64_t ldo, uint8_t* out_scales, int32_t out_fmt,
@@ -286,7 +307,7 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
                         int64_t ldo, uint8_t* out_scales, int32_t out_fmt, void* workspace, size_t workspace_bytes,
                         const mx_gemm_config* config, hipStream_t stream) {
   mx_gemm_config cfg;
-  mx_gemm_default_config(&cfg);
+  mx_gemm_select_config(m, n, k, a_fmt, w_fmt, epilogue, out_kind, &cfg);
   if (config) {
     if (config->group_m < 1 || config->group_m > 16 || (config->xcd_remap != 0 && config->xcd_remap != 1) ||
         (config->tile_n != 256 && config->tile_n != 128) || (config->waves != 4 && config->waves != 8))

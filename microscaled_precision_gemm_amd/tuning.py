@@ -18,8 +18,17 @@ weigh more), or 256 with 8 waves, two per SIMD.
   sequence over K; the check holds the library to that on the real data), and
   records the fastest, keeping the default unless a candidate beats
   it by more than ``margin``.
-* ``TuningTable.lookup`` returns the recorded configuration for a call, or
-  None (the library default) for shapes never tuned.
+* ``TuningTable.lookup`` returns the recorded configuration for a call; for
+  a shape never tuned, the configuration of the nearest tuned shape of the
+  same GEMM (same device, K, element formats, epilogue and output kind; the
+  closest M x N); with no such entry, None, and mx_gemm then applies the
+  library's shape rule (``mx_gemm_select_config``), never the generic
+  configuration blindly.
+* ``tune_gemm`` warm-starts by default: the search starts from that nearest
+  entry (the post tunes a new request size starting from the earlier
+  optimizations of the same GEMM), or from the shape rule, and times that
+  seed, the rule's pick, the generic configuration and the candidates one
+  knob away from the seed, instead of every candidate.
 * ``TuningTable.save`` / ``load`` persist the table as JSON; entries are keyed
   by the device's ISA name and compute-unit count, so a table carried to other
   hardware is not applied there.
@@ -32,12 +41,13 @@ weigh more), or 256 with 8 waves, two per SIMD.
 from __future__ import annotations
 
 import json
+import math
 import os
 import tempfile
 
 import torch
 
-from .binding import MXGemmConfig, MXTensor, mx_gemm, mx_gemm_default_config
+from .binding import MXGemmConfig, MXTensor, mx_gemm, mx_gemm_default_config, mx_gemm_select_config
 
 # (group_m, xcd_remap, tile_n, waves)
 CANDIDATES = ((4, 1, 256, 4), (2, 1, 256, 4), (8, 1, 256, 4), (16, 1, 256, 4), (1, 1, 256, 4), (4, 0, 256, 4),
@@ -75,6 +85,23 @@ def gemm_key(m: int, n: int, k: int, a_fmt: str, w_fmt: str, epilogue: str, out_
     return f"{device}|{m}x{n}x{k}|a={a_fmt}|w={w_fmt}|epi={epilogue}|out={out_kind}:{of}"
 
 
+def split_key(key: str) -> tuple[str, int, int, int, str]:
+    """(device, m, n, k, the rest of the key) of a table key."""
+    device, shape, rest = key.split("|", 2)
+    m, n, k = (int(v) for v in shape.split("x"))
+    return device, m, n, k, rest
+
+
+def neighbours(config: tuple[int, int, int, int], a_fmt: str, w_fmt: str, epilogue: str) -> list:
+    """The candidates one knob away from ``config``: the tile walk's group
+    width halved or doubled, the XCD remapping flipped, or the other tile
+    shapes with the same walk."""
+    g, x, t, wv = config
+    out = [(max(1, g // 2), x, t, wv), (min(16, g * 2), x, t, wv), (g, 1 - x, t, wv)]
+    out += [(g, x, tt, ww) for tt, ww in ((256, 4), (128, 4), (256, 8)) if (tt, ww) != (t, wv)]
+    return [c for c in dict.fromkeys(out) if c != config and supports(c, a_fmt, w_fmt, epilogue)]
+
+
 class TuningTable:
     """Per-shape launch configurations of mx_gemm."""
 
@@ -86,8 +113,31 @@ class TuningTable:
 
     def lookup(self, m, n, k, a_fmt="e2m3", w_fmt="e2m3", epilogue="none", out_kind="bf16", out_fmt="e2m3",
                device: str | None = None) -> MXGemmConfig | None:
-        e = self.entries.get(gemm_key(m, n, k, a_fmt, w_fmt, epilogue, out_kind, out_fmt, device or device_name()))
-        return None if e is None else MXGemmConfig(*e["config"])
+        """The configuration for this call: its own entry, else the nearest
+        tuned shape of the same GEMM, else None (the library's shape rule)."""
+        key = self.source(m, n, k, a_fmt, w_fmt, epilogue, out_kind, out_fmt, device)
+        return None if key is None else MXGemmConfig(*self.entries[key]["config"])
+
+    def source(self, m, n, k, a_fmt="e2m3", w_fmt="e2m3", epilogue="none", out_kind="bf16", out_fmt="e2m3",
+               device: str | None = None) -> str | None:
+        """Key of the entry lookup() takes its configuration from: the call's
+        own key, or the entry of the same device, K, formats, epilogue and
+        output kind whose M x N is closest in log scale (ties: the closer N,
+        then the key order), or None."""
+        device = device or device_name()
+        key = gemm_key(m, n, k, a_fmt, w_fmt, epilogue, out_kind, out_fmt, device)
+        if key in self.entries:
+            return key
+        rest = split_key(key)[4]
+        best, best_d = None, None
+        for other in sorted(self.entries):
+            dv, om, on, ok, orest = split_key(other)
+            if dv != device or ok != k or orest != rest:
+                continue
+            d = (abs(math.log2(om * on) - math.log2(max(1, m * n))), abs(math.log2(on) - math.log2(max(1, n))))
+            if best_d is None or d < best_d:
+                best, best_d = other, d
+        return best
 
     def record(self, key: str, entry: dict) -> None:
         self.entries[key] = entry
@@ -143,14 +193,24 @@ def _time_us(fn, iters: int) -> float:
 
 
 def tune_gemm(table: TuningTable, a: MXTensor, w: MXTensor, out_kind: str = "bf16", epilogue: str = "none",
-              out_fmt: str = "e2m3", candidates=CANDIDATES, iters: int = 10, rounds: int = 3,
-              margin: float = 0.01) -> dict:
+              out_fmt: str = "e2m3", candidates=None, iters: int = 10, rounds: int = 3,
+              margin: float = 0.01, warm_start: bool = True) -> dict:
     """Time the candidate configurations this call supports on these operands
-    and record the fastest in ``table`` (see the module docstring).  Returns
-    the recorded entry; raises if a candidate's output differs from the
-    default's."""
+    and record the fastest in ``table`` (see the module docstring).  With
+    ``candidates`` None: a warm-started search (the seed, its neighbours, the
+    shape rule's pick and the generic configuration) when ``warm_start``,
+    else every candidate.  Returns the recorded entry; raises if a
+    candidate's output differs from the generic configuration's."""
     default = mx_gemm_default_config().key()
-    cands = [default] + [c for c in candidates if c != default and supports(c, a.fmt, w.fmt, epilogue)]
+    rule = mx_gemm_select_config(a.rows, w.rows, w.k, a.fmt, w.fmt, epilogue, out_kind).key()
+    seed_key = table.source(a.rows, w.rows, w.k, a.fmt, w.fmt, epilogue, out_kind, out_fmt)
+    if candidates is None and warm_start:
+        seed = tuple(table.entries[seed_key]["config"]) if seed_key is not None else rule
+        candidates = [seed, rule] + neighbours(seed, a.fmt, w.fmt, epilogue)
+    elif candidates is None:
+        candidates = CANDIDATES
+    cands = [default] + [c for c in dict.fromkeys(map(tuple, candidates))
+                         if c != default and supports(c, a.fmt, w.fmt, epilogue)]
     ref = mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, config=default)
     outs = {c: mx_gemm(a, w, out_kind=out_kind, epilogue=epilogue, out_fmt=out_fmt, config=c) for c in cands}
     torch.cuda.synchronize()
@@ -171,7 +231,8 @@ def tune_gemm(table: TuningTable, a: MXTensor, w: MXTensor, out_kind: str = "bf1
     if best[pick] > best[default] * (1.0 - margin):
         pick = default
     entry = {"config": list(pick), "us": round(best[pick], 2), "default_us": round(best[default], 2),
-             "candidates": {",".join(map(str, c)): round(t, 2) for c, t in best.items()}}
+             "candidates": {",".join(map(str, c)): round(t, 2) for c, t in best.items()},
+             "seeded_from": seed_key if warm_start else None}
     key = gemm_key(a.rows, w.rows, w.k, a.fmt, w.fmt, epilogue, out_kind, out_fmt, device_name())
     table.record(key, entry)
     return entry

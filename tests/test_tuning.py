@@ -31,6 +31,65 @@ def test_save_load_round_trip(tmp_path):
     assert u.lookup(256, 512, 2048, device="devX") is None  # untuned shape: library default
 
 
+def test_untuned_shape_takes_the_nearest_entry_of_the_same_gemm():
+    """A call shape missing from the table takes the configuration of the
+    tuned shape of the same GEMM (device, K, formats, epilogue, output) with
+    the closest M x N, never one of another GEMM; with none, the library's
+    shape rule applies (lookup returns None)."""
+    t = T.TuningTable()
+    dev = "devX"
+    fc1 = dict(k=3072, epilogue="gelu_tanh", out_kind="mx")
+    t.record(T.gemm_key(20480, 12288, 3072, "e2m3", "e2m3", "gelu_tanh", "mx", "e2m3", dev),
+             {"config": [8, 1, 128, 4], "us": 1.0, "default_us": 1.0, "candidates": {}})
+    t.record(T.gemm_key(512, 12288, 3072, "e2m3", "e2m3", "gelu_tanh", "mx", "e2m3", dev),
+             {"config": [2, 1, 256, 8], "us": 1.0, "default_us": 1.0, "candidates": {}})
+    t.record(T.gemm_key(2560, 12288, 3072, "e2m3", "e2m3", "none", "bf16", "e2m3", dev),
+             {"config": [16, 0, 256, 4], "us": 1.0, "default_us": 1.0, "candidates": {}})
+    # 2560 tokens: log2 distance 3 to 20480, 2.3 to 512 -> the 512 entry; 8192: the 20480 one
+    assert t.source(2560, 12288, device=dev, **fc1).startswith(f"{dev}|512x")
+    assert t.lookup(2560, 12288, device=dev, **fc1).key() == (2, 1, 256, 8)
+    assert t.lookup(8192, 12288, device=dev, **fc1).key() == (8, 1, 128, 4)
+    assert t.lookup(20480, 12288, device=dev, **fc1).key() == (8, 1, 128, 4)  # its own entry
+    # another GEMM at the same M x N is never borrowed
+    assert t.lookup(2560, 12288, 6144, epilogue="gelu_tanh", out_kind="mx", device=dev) is None  # other K
+    assert t.lookup(2560, 12288, 3072, epilogue="gelu_tanh", out_kind="mx", out_fmt="e3m2", device=dev) is None
+    assert t.lookup(2560, 12288, 3072, a_fmt="e3m2", epilogue="gelu_tanh", out_kind="mx", device=dev) is None
+    assert t.lookup(2560, 12288, 3072, device=dev).key() == (16, 0, 256, 4)  # the bf16 GEMM's own entry
+    assert t.lookup(2560, 12288, 3072, epilogue="gelu_tanh", out_kind="mx", device="devY") is None
+
+
+def test_neighbours_change_one_knob():
+    n = T.neighbours((8, 1, 128, 4), "e2m3", "e2m3", "gelu_tanh")
+    assert set(n) == {(4, 1, 128, 4), (16, 1, 128, 4), (8, 0, 128, 4), (8, 1, 256, 4), (8, 1, 256, 8)}
+    # FP8 operands have no 128-feature tiles; SwiGLU no 8-wave tiles
+    assert all(c[2] == 256 for c in T.neighbours((4, 1, 256, 4), "e4m3", "e4m3", "none"))
+    assert all(c[3] == 4 for c in T.neighbours((4, 1, 256, 4), "e2m3", "e2m3", "swiglu"))
+    assert (1, 1, 256, 4) not in T.neighbours((1, 1, 256, 4), "e2m3", "e2m3", "none")
+
+
+def test_library_shape_rule():
+    """mx_gemm_select_config (what mx_gemm uses when given no configuration)
+    picks the choices tuned on the workload shapes, and only configurations
+    the call supports."""
+    sel = mx.mx_gemm_select_config
+    assert sel(20480, 12288, 3072, epilogue="gelu_tanh", out_kind="mx").key() == (8, 1, 128, 4)
+    assert sel(2560, 12288, 3072, epilogue="none", out_kind="mx").key() == (8, 1, 128, 4)
+    assert sel(20480, 3072, 12288, epilogue="none", out_kind="bf16").key() == (4, 1, 256, 8)
+    assert sel(4096, 3072, 3072).key() == (4, 1, 256, 8)
+    assert sel(20480, 12288, 3072, "e2m1", "e2m1").key() == (4, 1, 256, 8)
+    assert sel(20480, 12288, 3072, "e4m3", "e4m3").key() == (4, 1, 256, 4)
+    assert sel(20480, 16384, 3072, epilogue="swiglu", out_kind="mx").key() == (4, 1, 256, 4)
+    assert sel(20480, 12288, 8192, epilogue="gelu_tanh", out_kind="mx").key() == (4, 1, 256, 8)
+    assert mx.mx_gemm_default_config().key() == (4, 1, 256, 4)
+    for af, wf in (("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e2m1", "e2m1"), ("e5m2", "e4m3")):
+        for epi, out in (("none", "bf16"), ("none", "f32"), ("gelu_tanh", "mx"), ("swiglu", "mx"), ("none", "mx")):
+            for k in (128, 3072, 16384):
+                if epi != "none" or out == "mx":
+                    if af not in ("e2m3", "e3m2"):
+                        continue
+                assert T.supports(sel(4096, 4096, k, af, wf, epi, out).key(), af, wf, epi), (af, wf, epi, out, k)
+
+
 def test_candidates_the_call_supports():
     # 128-feature tiles exist for the 6-bit pairs (every epilogue); 8 waves
     # for 256-feature tiles of every pair, without SwiGLU
@@ -66,7 +125,7 @@ def test_tune_real_call_and_apply(tmp_path):
     w = mx.mx_quantize((torch.randn(n, k, device="cuda") * 0.05).to(torch.bfloat16), "e2m3")
     say("tuning 2048x512x2048 gelu->mx")
     table = T.TuningTable(str(tmp_path / "t.json"))
-    entry = T.tune_gemm(table, a, w, out_kind="mx", epilogue="gelu_tanh", iters=3, rounds=2)
+    entry = T.tune_gemm(table, a, w, out_kind="mx", epilogue="gelu_tanh", iters=3, rounds=2, warm_start=False)
     assert set(entry["candidates"]) >= {"4,1,256,4", "8,1,256,4", "1,1,256,4", "4,0,256,4", "4,1,128,4",
                                         "4,1,256,8"}
     cfg = table.lookup(m, n, k, epilogue="gelu_tanh", out_kind="mx")
@@ -104,3 +163,40 @@ def test_shipped_table_covers_the_workloads():
         assert cfg is not None, c
         af, wf, epi = c.get("a_fmt", "e2m3"), c.get("w_fmt", "e2m3"), c.get("epilogue", "none")
         assert T.supports(cfg.key(), af, wf, epi), (c, cfg.key())
+
+
+@pytest.mark.gpu
+def test_warm_start_for_an_untuned_token_count():
+    """2560 tokens (one GPU's share of the 20480 when the tokens are split
+    eight ways) is not in the shipped table.  lookup() gives it the fc1
+    entry's configuration (not the generic one), whose output is
+    bit-identical to the generic configuration's and to the shape rule's; a
+    warm-started tune starts from that entry and keeps a configuration no
+    slower than the generic one."""
+    from tests.parity import say
+    torch.manual_seed(1)
+    m, k, n = 2560, 3072, 12288
+    shipped = T.TuningTable(T.SHIPPED_TABLE)
+    dev = T.device_name()
+    src = shipped.source(m, n, k, epilogue="gelu_tanh", out_kind="mx")
+    if not dev.startswith("gfx950/"):
+        pytest.skip(f"the shipped table is for gfx950, this is {dev}")
+    assert src == T.gemm_key(20480, n, k, "e2m3", "e2m3", "gelu_tanh", "mx", "e2m3", dev)
+    cfg = shipped.lookup(m, n, k, epilogue="gelu_tanh", out_kind="mx")
+    assert cfg.key() != mx.mx_gemm_default_config().key()
+    a = mx.mx_quantize(torch.randn(m, k, device="cuda").to(torch.bfloat16), "e2m3")
+    w = mx.mx_quantize((torch.randn(n, k, device="cuda") * 0.02).to(torch.bfloat16), "e2m3")
+    say("warm-started tuning 2560x3072x12288 gelu->mx")
+    outs = [mx.mx_gemm(a, w, out_kind="mx", epilogue="gelu_tanh", config=c)
+            for c in (cfg, mx.mx_gemm_default_config(), None)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.codes, outs[0].codes) and torch.equal(o.scales, outs[0].scales)
+    entry = T.tune_gemm(shipped, a, w, out_kind="mx", epilogue="gelu_tanh", iters=5, rounds=3)
+    print("warm start", {k_: v for k_, v in entry.items()})
+    assert entry["seeded_from"] == src
+    assert ",".join(map(str, cfg.key())) in entry["candidates"]
+    assert len(entry["candidates"]) < len(T.CANDIDATES)
+    assert entry["us"] <= entry["default_us"]
+    # the table-derived configuration itself is no slower than the generic one (5 % timing noise)
+    assert entry["candidates"][",".join(map(str, cfg.key()))] <= 1.05 * entry["default_us"]
