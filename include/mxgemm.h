@@ -7,9 +7,10 @@
  * (section "Quality set the precision limit": 6-bit floating-point elements
  * that share one scale per block) and replaces the library GEMM with a custom
  * MXFP6 GEMM (section "We built a faster MXFP6 kernel": packed 6-bit storage,
- * no re-reads by neighbouring workgroups, Figure 1 timings).  Its section
- * "Fusion cut intermediate memory traffic" has the down projection read the
- * quantized intermediate directly.  The pages fix no element variant, block
+ * no re-reads by neighbouring workgroups, Figure 1 timings).  In its section
+ * "Fusion cut intermediate memory traffic" the MLP's second GEMM takes the
+ * first one's output already in MXFP6, with no bf16 copy written and
+ * re-quantized in between.  The pages fix no element variant, block
  * size or rounding; this library follows the OCP Microscaling (MX) v1.0
  * definition:
  *
@@ -153,6 +154,12 @@ extern "C" {
 /*
  * mx_quantize - MX-quantize a [rows, k] matrix along its rows.
  *
+ * This is the activation quantizer of the Hedra post's section "Fusion cut
+ * intermediate memory traffic" (an activation is quantized once and every
+ * GEMM that consumes it reads the packed result), with the block, scale and
+ * rounding rule of the header comment.  It also quantizes weights once,
+ * ahead of the GEMMs that read them.
+ *
  *   src       device pointer to bf16 (src_type MX_SRC_BF16) or fp32
  *             (MX_SRC_F32) values, row r starting at src + r * ld_src
  *             elements; 16-byte aligned, ld_src * element size a multiple of 16.
@@ -240,8 +247,9 @@ size_t mx_packed_bytes(int64_t rows, int64_t k, int32_t fmt, int32_t layout, int
  *   MX_OUT_MX: the epilogue result is MX-quantized along N in blocks of 32
  *     (n_out % 32 == 0) into out / out_scales as an [m, n_out] matrix in
  *     MX_LAYOUT_TILED (padding written too), element format out_fmt
- *     (MX_FMT_E2M3 or MX_FMT_E3M2); ldo is ignored.  This output is directly the a_codes / a_scales of a
- *     following GEMM (the down projection reads the quantized intermediate).
+ *     (MX_FMT_E2M3 or MX_FMT_E3M2); ldo is ignored.  This output is directly the
+ *     a_codes / a_scales of a following GEMM, which reads it with no bf16
+ *     round trip.
  * workspace: device memory of at least mx_gemm_workspace_size(m, n, k, a_src
  *   != NULL, 0) bytes (may be NULL when that size is 0).  That size holds the
  *   quantized activations in any element format.
@@ -315,6 +323,10 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
  * mx_gemm_splitk - the same product for skinny m (0 <= m <= 16), split along
  * K into `splits` contiguous chunks whose fp32 partial sums are added in the
  * fixed order 0, 1, ..., splits-1 (deterministic) before the output rounding.
+ * This is the split-K scheme of "Creating Custom Kernels for the AMD MI300",
+ * section "Skinny GEMM Kernel": with few rows there are too few output tiles
+ * to occupy every compute unit, so the reduction dimension is divided among
+ * workgroups instead.
  *
  * Arguments as mx_gemm (operands in MX_LAYOUT_TILED), with:
  *   splits    1 .. 16 and k % (128 * splits) == 0, i.e. each chunk is whole

@@ -19,9 +19,10 @@ computes, in float64 with numpy:
   an fp64 sum; ``S = |A| @ |W|.T`` is the scale used by the tolerance.
 * The fused fc1 epilogue is GELU with the tanh approximation (Hendrycks and
   Gimpel, "Gaussian Error Linear Units", 2016) followed by the same MX
-  quantization, with blocks of 32 consecutive output columns.  The Hedra post
-  (section "Fusion cut intermediate memory traffic") has the down projection
-  read the quantized intermediate directly; this is that intermediate.
+  quantization, with blocks of 32 consecutive output columns.  In the Hedra
+  post (section "Fusion cut intermediate memory traffic") fc2 takes fc1's
+  output already in MXFP6, with no bf16 copy written and re-quantized in
+  between; this function defines that MXFP6 operand.
 * The SwiGLU variant of that epilogue (the MLP activation the same section
   names for Krea 3): the gate and up projections are one GEMM over stacked
   weights, and each output is silu(gate) * up (Shazeer, "GLU Variants Improve
