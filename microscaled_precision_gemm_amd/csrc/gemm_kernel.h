@@ -584,6 +584,8 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
     const int n_stages = (n_out + kTileStageK - 1) / kTileStageK;
     // the swap, block scale and conversion: lane half h ends with the 24 code
     // bytes q and the scale byte of one whole block (va's for h = 0, vb's for h = 1)
+    // A non-finite block comes back with scale byte 0xFF and its codes are
+    // zeroed when it is stored (together with the layout padding).
     auto convert_pair = [&](const v16f& va, const v16f& vb, v6u& q, uint32_t& sbyte) {
       // lo: features 0..15 of this lane's block (even ones in 0..7, odd in
       // 8..15), hi: features 16..31 in the same order
@@ -603,14 +605,10 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
           hi[8 * half8 + i] = __uint_as_float(y[i]);
         }
       }
-      uint32_t amax = 0;
+      float amax = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t x = __float_as_uint(lo[r]) & 0x7fffffffu, y = __float_as_uint(hi[r]) & 0x7fffffffu;
-        const uint32_t xy = x > y ? x : y;
-        amax = xy > amax ? xy : amax;
-      }
-      const BlockScale sc = scale_from_f32_bits<OFMT>(amax);
+      for (int r = 0; r < 16; ++r) amax = absmax2(amax, lo[r], hi[r]);
+      const BlockScale sc = scale_from_f32_bits<OFMT>(__float_as_uint(amax));
       v16f ev, od;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -621,7 +619,6 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
       }
       q = cvt_f32x2x16<OFMT>(ev, od, sc.scale);
       sbyte = sc.byte;
-      if (sc.nonfinite) q = v6u{0, 0, 0, 0, 0, 0};
     };
     // block qb (0..3) of output stage `stage` for token row m of group gm:
     // even block: plane A (bytes 0..15) + plane L (16..23); odd block: plane
@@ -629,10 +626,9 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
     auto store_block = [&](v6u q, uint32_t sbyte, int m, int gm, int stage, int qb) {
       const int nb = stage * 4 + qb;
       if (gm < g.gx && stage < n_stages) {
-        if (m >= g.M || nb >= n_out / 32) {  // layout padding
-          q = v6u{0, 0, 0, 0, 0, 0};
-          sbyte = 127u;
-        }
+        const bool pad = m >= g.M || nb >= n_out / 32;  // layout padding: codes 0, scale 127
+        if (pad || sbyte == 0xFFu) q = v6u{0, 0, 0, 0, 0, 0};  // padding or a non-finite block
+        if (pad) sbyte = 127u;
         const bool odd = qb & 1;
         uint8_t* half =
             static_cast<uint8_t*>(g.out) + ((int64_t)stage * g.gx + gm) * kChunkCodes + (qb >> 1) * kHalfBytes;

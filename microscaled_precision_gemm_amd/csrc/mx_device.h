@@ -81,6 +81,15 @@ __device__ __forceinline__ BlockScale scale_from_f32_bits(uint32_t amax_bits) {
   return make_scale(shared);
 }
 
+// Running block amax of fp32 values: max(m, |a|, |b|) in one v_maximum3_f32.
+// Unlike v_max3 it propagates a NaN, so the bits of the result order exactly
+// as the integer maximum of the magnitude bits would: a block holding a NaN or
+// an infinity ends at bits >= 0x7f800000 (the non-finite scale), any other
+// block at its largest magnitude.
+__device__ __forceinline__ float absmax2(float m, float a, float b) {
+  return __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)));
+}
+
 // Scale rule from the magnitude bits of a bf16 amax (sign bit clear, in the low 16 bits).
 template <int FMT>
 __device__ __forceinline__ BlockScale scale_from_bf16_bits(uint32_t amax_bits) {

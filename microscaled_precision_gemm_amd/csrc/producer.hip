@@ -100,13 +100,10 @@ __device__ __forceinline__ void convert_store_chunk(const ProducerArgs& a, const
         y[i * (16 / L::kEsize) + e] = __builtin_fmaf(f[e] * inv, va[kk], vb[kk]);
       }
     }
-    uint32_t amax = 0;
+    float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const uint32_t m = __float_as_uint(y[e]) & 0x7fffffffu;
-      amax = m > amax ? m : amax;
-    }
-    const BlockScale s = scale_from_f32_bits<FMT>(amax);
+    for (int e = 0; e < 32; e += 2) amax = absmax2(amax, y[e], y[e + 1]);
+    const BlockScale s = scale_from_f32_bits<FMT>(__float_as_uint(amax));
     v16f even, odd;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -331,13 +328,10 @@ __global__ __launch_bounds__(64 * kRWaves, 2) void rmsnorm_quantize_rows_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[8 * i + e] = __builtin_fmaf(f[e] * inv, va[q * 32 + 8 * i + e], vb[q * 32 + 8 * i + e]);
       }
-      uint32_t amax = 0;
+      float amax = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const uint32_t m = __float_as_uint(y[e]) & 0x7fffffffu;
-        amax = m > amax ? m : amax;
-      }
-      const BlockScale s = scale_from_f32_bits<FMT>(amax);
+      for (int e = 0; e < 32; e += 2) amax = absmax2(amax, y[e], y[e + 1]);
+      const BlockScale s = scale_from_f32_bits<FMT>(__float_as_uint(amax));
       v16f even, odd;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {

@@ -69,15 +69,12 @@ __device__ __forceinline__ uint32_t quantize_block(const u32x4* w, uint32_t (&q)
       }
     s = scale_from_bf16_bits<FMT>(m2[0] > m2[1] ? m2[0] : m2[1]);
   } else {
-    uint32_t amax = 0;
+    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = w[i][j] & 0x7fffffffu;
-        amax = a > amax ? a : amax;
-      }
-    s = scale_from_f32_bits<FMT>(amax);
+      for (int j = 0; j < 4; j += 2) amax = absmax2(amax, __uint_as_float(w[i][j]), __uint_as_float(w[i][j + 1]));
+    s = scale_from_f32_bits<FMT>(__float_as_uint(amax));
   }
   if constexpr (!F32 && fmt_bits(FMT) == 6) {
     v32bf x;

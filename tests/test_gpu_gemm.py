@@ -405,6 +405,57 @@ def test_splitk_matches_plain_gemm_property():
         assert_fp32_close(to_np(o).astype(np.float64), c, s, "split count")
 
 
+@pytest.mark.parametrize("m", [16, 5, 1])
+@pytest.mark.parametrize("splits", [1, 4, 8, 16])
+@pytest.mark.parametrize("a_fmt,w_fmt", FORMAT_PAIRS)
+def test_splitk_in_call_quantization_bit_identical(m, splits, a_fmt, w_fmt):
+    """bf16 activations given to mx_gemm_splitk are quantized inside the call
+    (S = 1, 4, 8 take the LDS-scale path of the split-K kernel, S = 16 the
+    per-stage-scale path).  The output must be bit-identical to the call on
+    activations quantized beforehand with mx_quantize, for both output kinds,
+    with a row stride wider than K, and within the GEMM bar of the oracle."""
+    n, k = 400, 4096
+    a, w, qa, qw, c, s = _operands(m, n, k, a_fmt, w_fmt, seed=61 + m + splits)
+    say(f"splitk in-call quantization m={m} S={splits} a={a_fmt} w={w_fmt}")
+    wq = _gpu_weights(w, w_fmt, qw)
+    wide = torch.zeros((m, k + 64), dtype=torch.bfloat16, device="cuda")
+    wide[:, :k] = a.cuda()
+    a_view = wide[:, :k]  # row stride k + 64 elements
+    aq = mx.mx_quantize(a.cuda(), a_fmt)
+    for out_kind in ("bf16", "f32"):
+        got = mx.mx_gemm_splitk(a_view, wq, splits, out_kind=out_kind, a_fmt=a_fmt)
+        want = mx.mx_gemm_splitk(aq, wq, splits, out_kind=out_kind)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16) if out_kind == "bf16" else got.view(torch.int32),
+                           want.view(torch.int16) if out_kind == "bf16" else want.view(torch.int32)), out_kind
+        if out_kind == "f32":
+            assert_fp32_close(to_np(got).astype(np.float64), c, s, "splitk in-call quantization")
+
+
+def test_splitk_in_call_quantization_special_blocks():
+    """Blocks the quantizer treats specially, quantized inside the split-K
+    call: an all-zero block (scale byte 0), a block with a NaN (scale 0xFF,
+    codes 0: its products make that token's outputs NaN), tiny values, values
+    near the bf16 maximum (saturation) and negative zeros.  Bit-identical to
+    the call on pre-quantized activations, NaN outputs included, and only the
+    NaN token's outputs are NaN."""
+    m, n, k, splits = 16, 64, 4096, 4
+    a, w, qa, qw, c, s = _operands(m, n, k, "e2m3", "e3m2", seed=67)
+    a = a.clone()
+    a[0, 0:32] = 0.0
+    a[1, 64:96] = float("nan")
+    a[2, 128:160] = torch.tensor([1e-38] * 32, dtype=torch.bfloat16)
+    a[3, 3000:3032] = 3.0e38
+    a[4, 4064:4096] = -0.0
+    say("splitk in-call quantization, special blocks")
+    wq = _gpu_weights(w, "e3m2", qw)
+    got = mx.mx_gemm_splitk(a.cuda(), wq, splits, out_kind="f32")
+    want = mx.mx_gemm_splitk(mx.mx_quantize(a.cuda(), "e2m3"), wq, splits, out_kind="f32")
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+    assert torch.isnan(got[1]).all() and not torch.isnan(got[[0, 2, 3, 4]]).any()
+
+
 # ---------------------------------------------------------------- SwiGLU epilogue
 
 def _swiglu_operands(m, h, k, a_fmt="e2m3", w_fmt="e2m3", seed=0):

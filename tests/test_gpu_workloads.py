@@ -175,7 +175,8 @@ def test_skinny_full_size_splitk(m):
     """M x 16384 x 13312 with E3M2 weights, 16 splits, activations quantized
     inside the call (as the bench runs it): sampled features, all tokens, bf16
     and fp32 outputs; one split must agree with sixteen within the fp32
-    bound."""
+    bound, and the call must give the bits of the same split-K call on
+    activations quantized beforehand (every output)."""
     w = syn.WORKLOADS["skinny"]
     a, wt = syn.make_a(w, m=m), syn.make_w(w)
     rng = np.random.default_rng([80, m])
@@ -188,7 +189,9 @@ def test_skinny_full_size_splitk(m):
     mx.mx_gemm_splitk(a.to(dev), wq, w.splits, out=out, workspace=work)
     o32 = mx.mx_gemm_splitk(a.to(dev), wq, w.splits, out_kind="f32")
     o32_one = mx.mx_gemm_splitk(a.to(dev), wq, 1, out_kind="f32")
+    pre = mx.mx_gemm_splitk(mx.mx_quantize(a.to(dev), "e2m3"), wq, w.splits, out_kind="bf16")
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), pre.view(torch.int16))
     ci = torch.from_numpy(cols).to(dev)
     c, s = O.gemm_ref(_deq_rows(a, np.arange(m), "e2m3"), _deq_rows(wt, cols, w.w_fmt))
     assert_bf16_close(bf16_tensor_to_f64(out[:, ci]), c, s, "skinny bf16")
