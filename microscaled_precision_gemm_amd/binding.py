@@ -246,13 +246,15 @@ def mx_quantize(src: torch.Tensor, fmt: str = "e2m3", layout: str = "tiled", out
     """MX-quantize a 2-D bf16/fp32 GPU tensor along its rows (blocks of 32)."""
     if src.dim() != 2 or src.stride(1) != 1:
         raise ValueError("src must be 2-D with unit stride along K")
-    dev = _require_cuda(src)
     rows, k = src.shape
+    if out is not None:
+        # the kernel writes `fmt` codes: an out sized for another element width would overflow
+        if out.rows != rows or out.k != k or out.layout != layout or out.fmt != fmt:
+            raise ValueError("out does not match the source shape / layout / element format")
+        _check_mx(out, "out")
+    dev = _require_cuda(src, *_mx_parts(out))
     if out is None:
         out = MXTensor.empty(rows, k, fmt, layout, dev)
-    if out.rows != rows or out.k != k or out.layout != layout:
-        raise ValueError("out does not match the source shape / layout")
-    _check_mx(out, "out")
     st = lib().mx_quantize(_ptr(src), _src_type(src), rows, k, src.stride(0), _fmt(fmt), LAYOUTS[layout],
                            _ptr(out.codes), _ptr(out.scales), _stream(dev))
     _check(st, "mx_quantize")
@@ -267,19 +269,20 @@ def mx_rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor | None = None, shif
     [n_cond, d] with rows_per_cond rows per conditioning row (a multiple of 32)."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be [rows, d] with unit stride along d")
-    dev = _require_cuda(x)
     rows, d = x.shape
     for name, v in (("gamma", gamma), ("shift", shift), ("scale", scale)):
         if v is not None:
-            if v.dtype != torch.float32 or not v.is_contiguous() or v.device != dev:
-                raise ValueError(f"{name} must be a contiguous fp32 tensor on {dev}")
+            if v.dtype != torch.float32 or not v.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous fp32 tensor")
             if v.shape[-1] != d:
                 raise ValueError(f"{name} must have d = {d} features")
+    if out is not None:
+        if out.rows != rows or out.k != d or out.layout != "tiled" or out.fmt != fmt:
+            raise ValueError(f"out must be a tiled [rows, d] {fmt} MX matrix")
+        _check_mx(out, "out")
+    dev = _require_cuda(x, gamma, shift, scale, *_mx_parts(out))
     if out is None:
         out = MXTensor.empty(rows, d, fmt, "tiled", dev)
-    if out.rows != rows or out.k != d or out.layout != "tiled":
-        raise ValueError("out must be a tiled [rows, d] MX matrix")
-    _check_mx(out, "out")
     st = lib().mx_rmsnorm_quantize(_ptr(x), _src_type(x), rows, d, x.stride(0), _ptr(gamma), _ptr(shift), _ptr(scale),
                                    rows_per_cond, float(eps), _fmt(fmt), _ptr(out.codes), _ptr(out.scales),
                                    _stream(dev))

@@ -291,6 +291,29 @@ def test_binding_refuses_cpu_tensors(L):
         mx.mx_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
 
 
+def test_quantize_and_producer_bindings_check_out_before_launch(L):
+    """A caller-supplied out of the quantizer and of the producer must match
+    the call's element format (codes of another width would be written past
+    its buffers), shape and layout, and live on the GPU like the inputs;
+    the producer's vectors must be contiguous fp32 of d features."""
+    import torch
+    x = torch.zeros(32, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="element format"):
+        mx.mx_quantize(x, "e4m3", "tiled", out=_cpu_mx(32, 128, "e2m1"))   # 8-bit codes into a 4-bit buffer
+    with pytest.raises(ValueError, match="shape"):
+        mx.mx_quantize(x, "e2m3", "tiled", out=_cpu_mx(32, 96))
+    with pytest.raises(ValueError, match="GPU"):
+        mx.mx_quantize(x, "e2m3", "tiled", out=_cpu_mx(32, 128))
+    with pytest.raises(ValueError, match="MX matrix"):
+        mx.mx_rmsnorm_quantize(x, fmt="e3m2", out=_cpu_mx(32, 128, "e2m3"))
+    with pytest.raises(ValueError, match="fp32"):
+        mx.mx_rmsnorm_quantize(x, gamma=torch.ones(128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="features"):
+        mx.mx_rmsnorm_quantize(x, gamma=torch.ones(64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU"):
+        mx.mx_rmsnorm_quantize(x, gamma=torch.ones(128, dtype=torch.float32), out=_cpu_mx(32, 128))
+
+
 def _cpu_mx(rows, k, fmt="e2m3"):
     import torch
     return B.MXTensor(torch.zeros(mx.mx_packed_bytes(rows, k, "tiled", 0, fmt), dtype=torch.uint8),
