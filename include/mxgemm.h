@@ -93,7 +93,13 @@
  *     and return a negative status; nothing is written in that case;
  *   - MX_ERR_HIP reports a failed launch (hipGetLastError); a fault inside a
  *     kernel surfaces at the caller's next synchronization instead;
- *   - device pointers must be 16-byte aligned unless stated otherwise.
+ *   - device pointers must be 16-byte aligned unless stated otherwise;
+ *   - launch log: with the environment variable MXGEMM_LOG=1 (read once, at
+ *     the first call), every call of mx_quantize, mx_rmsnorm_quantize,
+ *     mx_gemm, mx_gemm_with_config, mx_gemm_splitk and
+ *     mx_gemm_splitk_noalloc writes one line to stderr: the call, its sizes,
+ *     formats and options (for mx_gemm the launch configuration and whether
+ *     the shape rule chose it) and the status returned.  Off otherwise.
  */
 #ifndef MXGEMM_H
 #define MXGEMM_H

@@ -2,7 +2,10 @@
 // workspace layout and kernel dispatch.  See include/mxgemm.h for the contract.
 #include "mxgemm.h"
 
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -42,6 +45,29 @@ bool valid_fmt(int32_t f) {
 bool fp6_fmt(int32_t f) { return f == MX_FMT_E2M3 || f == MX_FMT_E3M2; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+// Launch log: with MXGEMM_LOG=1 in the environment (read once), every call of
+// a computing entry point writes one line to stderr: the call, its sizes,
+// formats and options, and the status it returns.  Off by default.
+bool log_on() {
+  static const bool on = [] {
+    const char* e = getenv("MXGEMM_LOG");
+    return e != nullptr && e[0] == '1' && e[1] == '\0';
+  }();
+  return on;
+}
+
+__attribute__((format(printf, 2, 3))) int logged(int status, const char* fmt, ...) {
+  if (log_on()) {
+    char line[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(line, sizeof line, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "mxgemm: %s -> %d (%s)\n", line, status, mx_status_string(status));
+  }
+  return status;
+}
 
 bool valid_layout(int32_t l) { return l == MX_LAYOUT_ROWS || l == MX_LAYOUT_TILED; }
 
@@ -208,7 +234,7 @@ const char* mx_status_string(int status) {
   }
 }
 
-int mx_rmsnorm_quantize(const void* x, int32_t src_type, int64_t rows, int64_t d, int64_t ld_x, const float* gamma,
+static int rmsnorm_quantize_call(const void* x, int32_t src_type, int64_t rows, int64_t d, int64_t ld_x, const float* gamma,
                         const float* shift, const float* scale, int64_t rows_per_cond, float eps, int32_t fmt,
                         void* codes, uint8_t* scales, hipStream_t stream) {
   int st = check_quantize_args(x, src_type, rows, d, ld_x, fmt, MX_LAYOUT_TILED, codes, scales);
@@ -251,7 +277,7 @@ size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t a_is_src,
   return a_is_src ? tiled_ws(m, k, 8).end : 0;
 }
 
-int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
+static int quantize_call(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
                 int32_t layout, void* codes, uint8_t* scales, hipStream_t stream) {
   const int st = check_quantize_args(src, src_type, rows, k, ld_src, fmt, layout, codes, scales);
   if (st != MX_OK || rows == 0 || k == 0) return st;
@@ -301,7 +327,7 @@ int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_co
                              stream);
 }
 
-int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+static int gemm_call(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
                         const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
                         int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t epilogue, int32_t out_kind, void* out,
                         int64_t ldo, uint8_t* out_scales, int32_t out_fmt, void* workspace, size_t workspace_bytes,
@@ -383,7 +409,7 @@ int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, cons
   return hip_status(launch_gemm(g, a_fmt, w_fmt, epilogue, out_kind, out_fmt, stream));
 }
 
-int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
+static int splitk_call(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
                    int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n,
                    int64_t k, int32_t splits, int32_t out_kind, void* out, int64_t ldo, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
@@ -398,7 +424,7 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
                     out_kind, out, ldo, static_cast<uint8_t*>(workspace), stream);
 }
 
-int mx_gemm_splitk_noalloc(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+static int splitk_noalloc_call(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
                            const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
                            int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t splits, int32_t out_kind,
                            void* out, int64_t ldo, hipStream_t stream) {
@@ -416,6 +442,65 @@ int mx_gemm_splitk_noalloc(const void* a_src, int32_t a_src_type, int64_t lda, c
   }
   return run_splitk(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k, splits,
                     out_kind, out, ldo, ws, stream);
+}
+
+// ---- the computing entry points: the calls above plus the launch log
+
+int mx_quantize(const void* src, int32_t src_type, int64_t rows, int64_t k, int64_t ld_src, int32_t fmt,
+                int32_t layout, void* codes, uint8_t* scales, hipStream_t stream) {
+  return logged(quantize_call(src, src_type, rows, k, ld_src, fmt, layout, codes, scales, stream),
+                "mx_quantize rows=%lld k=%lld ld=%lld src_type=%d fmt=%d layout=%d", (long long)rows, (long long)k,
+                (long long)ld_src, src_type, fmt, layout);
+}
+
+int mx_rmsnorm_quantize(const void* x, int32_t src_type, int64_t rows, int64_t d, int64_t ld_x, const float* gamma,
+                        const float* shift, const float* scale, int64_t rows_per_cond, float eps, int32_t fmt,
+                        void* codes, uint8_t* scales, hipStream_t stream) {
+  return logged(rmsnorm_quantize_call(x, src_type, rows, d, ld_x, gamma, shift, scale, rows_per_cond, eps, fmt, codes,
+                                      scales, stream),
+                "mx_rmsnorm_quantize rows=%lld d=%lld ld=%lld src_type=%d fmt=%d gamma=%d shift=%d scale=%d "
+                "rows_per_cond=%lld eps=%g",
+                (long long)rows, (long long)d, (long long)ld_x, src_type, fmt, gamma != nullptr, shift != nullptr,
+                scale != nullptr, (long long)rows_per_cond, (double)eps);
+}
+
+int mx_gemm_with_config(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+                        const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
+                        int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t epilogue, int32_t out_kind, void* out,
+                        int64_t ldo, uint8_t* out_scales, int32_t out_fmt, void* workspace, size_t workspace_bytes,
+                        const mx_gemm_config* config, hipStream_t stream) {
+  mx_gemm_config used;
+  if (config)
+    used = *config;
+  else
+    mx_gemm_select_config(m, n, k, a_fmt, w_fmt, epilogue, out_kind, &used);
+  return logged(gemm_call(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k,
+                          epilogue, out_kind, out, ldo, out_scales, out_fmt, workspace, workspace_bytes, config,
+                          stream),
+                "mx_gemm m=%lld n=%lld k=%lld a=%s fmt=%d w_fmt=%d epilogue=%d out_kind=%d out_fmt=%d "
+                "config=(%d,%d,%d,%d)%s",
+                (long long)m, (long long)n, (long long)k, a_src ? "src" : "mx", a_fmt, w_fmt, epilogue, out_kind,
+                out_fmt, used.group_m, used.xcd_remap, used.tile_n, used.waves, config ? "" : " by shape rule");
+}
+
+int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,
+                   int32_t a_fmt, const void* w_codes, const uint8_t* w_scales, int32_t w_fmt, int64_t m, int64_t n,
+                   int64_t k, int32_t splits, int32_t out_kind, void* out, int64_t ldo, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  return logged(splitk_call(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n, k,
+                            splits, out_kind, out, ldo, workspace, workspace_bytes, stream),
+                "mx_gemm_splitk m=%lld n=%lld k=%lld a=%s fmt=%d w_fmt=%d splits=%d out_kind=%d", (long long)m,
+                (long long)n, (long long)k, a_src ? "src" : "mx", a_fmt, w_fmt, splits, out_kind);
+}
+
+int mx_gemm_splitk_noalloc(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes,
+                           const uint8_t* a_scales, int32_t a_fmt, const void* w_codes, const uint8_t* w_scales,
+                           int32_t w_fmt, int64_t m, int64_t n, int64_t k, int32_t splits, int32_t out_kind,
+                           void* out, int64_t ldo, hipStream_t stream) {
+  return logged(splitk_noalloc_call(a_src, a_src_type, lda, a_codes, a_scales, a_fmt, w_codes, w_scales, w_fmt, m, n,
+                                    k, splits, out_kind, out, ldo, stream),
+                "mx_gemm_splitk_noalloc m=%lld n=%lld k=%lld a=%s fmt=%d w_fmt=%d splits=%d out_kind=%d",
+                (long long)m, (long long)n, (long long)k, a_src ? "src" : "mx", a_fmt, w_fmt, splits, out_kind);
 }
 
 }  // extern "C"

@@ -364,3 +364,33 @@ def test_binding_checks_out_workspace_and_k_before_launch(L, fn):
             mx.mx_gemm(a, w, out_kind="mx", out_fmt="e2m3", out=_cpu_mx(m, n, "e3m2"))
         with pytest.raises(ValueError, match="MX matrix"):
             mx.mx_gemm(a, w, out_kind="mx", out=_cpu_mx(m, n - 32))
+
+
+def test_launch_log(L):
+    """MXGEMM_LOG=1 makes every computing call write one line to stderr with
+    its sizes and status (checked in a child process, on calls that fail
+    validation, so nothing is launched); without it the library is silent."""
+    import subprocess
+    import sys
+    code = (
+        "import microscaled_precision_gemm_amd as mx, ctypes\n"
+        "L = mx.lib()\n"
+        "print(L.mx_quantize(None, 0, 4, 48, 48, 2, 1, None, None, None))\n"       # k % 32 != 0
+        "print(L.mx_gemm(None, 0, 0, None, None, 3, None, None, 3, 4, 64, 128, 0, 1, None, 64, None, 2, None, 0,"
+        " None))\n"                                                                   # E3M2 x E3M2
+        "print(L.mx_gemm_splitk(None, 0, 0, None, None, 2, None, None, 3, 17, 64, 0, 1, 1, None, 64, None, 0,"
+        " None))\n")                                                                  # m > 16
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MXGEMM_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == [str(B.MX_ERR_SHAPE), str(B.MX_ERR_UNSUPPORTED), str(B.MX_ERR_SHAPE)]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("mxgemm: ")]
+    assert len(lines) == 3, r.stderr
+    assert lines[0].startswith("mxgemm: mx_quantize rows=4 k=48 ") and lines[0].endswith(f"-> {B.MX_ERR_SHAPE} "
+                                                                                          f"({mx.mx_status_string(B.MX_ERR_SHAPE)})")
+    assert lines[1].startswith("mxgemm: mx_gemm m=4 n=64 k=128 a=mx fmt=3 w_fmt=3") and "by shape rule" in lines[1]
+    assert lines[2].startswith("mxgemm: mx_gemm_splitk m=17 ")
+    env.pop("MXGEMM_LOG")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "mxgemm:" not in r.stderr
