@@ -72,14 +72,14 @@ def test_library_shape_rule():
     picks the choices tuned on the workload shapes, and only configurations
     the call supports."""
     sel = mx.mx_gemm_select_config
-    assert sel(20480, 12288, 3072, epilogue="gelu_tanh", out_kind="mx").key() == (8, 1, 128, 4)
-    assert sel(2560, 12288, 3072, epilogue="none", out_kind="mx").key() == (8, 1, 128, 4)
+    assert sel(20480, 12288, 3072, epilogue="gelu_tanh", out_kind="mx").key() == (8, 1, 256, 8)
+    assert sel(2560, 12288, 3072, epilogue="none", out_kind="mx").key() == (8, 1, 256, 8)
     assert sel(20480, 3072, 12288, epilogue="none", out_kind="bf16").key() == (4, 1, 256, 8)
     assert sel(4096, 3072, 3072).key() == (4, 1, 256, 8)
     assert sel(20480, 12288, 3072, "e2m1", "e2m1").key() == (4, 1, 256, 8)
     assert sel(20480, 12288, 3072, "e4m3", "e4m3").key() == (4, 1, 256, 4)
     assert sel(20480, 16384, 3072, epilogue="swiglu", out_kind="mx").key() == (4, 1, 256, 4)
-    assert sel(20480, 12288, 8192, epilogue="gelu_tanh", out_kind="mx").key() == (4, 1, 256, 8)
+    assert sel(20480, 12288, 8192, epilogue="gelu_tanh", out_kind="mx").key() == (8, 1, 256, 8)
     assert mx.mx_gemm_default_config().key() == (4, 1, 256, 4)
     for af, wf in (("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e2m1", "e2m1"), ("e5m2", "e4m3")):
         for epi, out in (("none", "bf16"), ("none", "f32"), ("gelu_tanh", "mx"), ("swiglu", "mx"), ("none", "mx")):
