@@ -94,6 +94,13 @@
  *   - MX_ERR_HIP reports a failed launch (hipGetLastError); a fault inside a
  *     kernel surfaces at the caller's next synchronization instead;
  *   - device pointers must be 16-byte aligned unless stated otherwise;
+ *   - size limits: every dimension is at most 2^30 (else MX_ERR_SHAPE).
+ *     Beyond that a request returns MX_ERR_UNSUPPORTED, before anything is
+ *     launched, when a tiled MX matrix would hold 2^40 code bytes or more,
+ *     when one 128-element stage of a GEMM operand (all its rows) would reach
+ *     4 GiB, or when a kernel would need 2^32 lanes or more (a dispatch holds
+ *     its grid size in 32 bits).  Inside those limits every byte offset is
+ *     computed in 64 bits, so buffers may be far larger than 4 GiB;
  *   - launch log: with the environment variable MXGEMM_LOG=1 (read once, at
  *     the first call), every call of mx_quantize, mx_rmsnorm_quantize,
  *     mx_gemm, mx_gemm_with_config, mx_gemm_splitk and

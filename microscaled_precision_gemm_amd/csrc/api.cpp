@@ -9,6 +9,7 @@
 
 #include <mutex>
 
+#include "grid_limits.h"
 #include "internal.h"
 #include "mx_device.h"
 
@@ -146,6 +147,7 @@ int check_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void*
   if (ldo < n) return MX_ERR_SHAPE;
   if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
   if (splits > kMaxSplits || k % (kTileStageK * (int64_t)splits) != 0) return MX_ERR_UNSUPPORTED;
+  if (splitk_grid_items(n) > kMaxGridItems) return MX_ERR_UNSUPPORTED;
   return MX_OK;
 }
 
@@ -246,6 +248,8 @@ static int rmsnorm_quantize_call(const void* x, int32_t src_type, int64_t rows, 
   if (rows == 0 || d == 0) return MX_OK;
   if (!aligned(gamma, 4) || !aligned(shift, 4) || !aligned(scale, 4)) return MX_ERR_ALIGN;
   if (tiled_codes_bytes(rows, d, 6) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
+  if (rmsnorm_quantize_grid_items(rows, d, src_type == MX_SRC_F32 ? kSrcF32 : kSrcBf16) > kMaxGridItems)
+    return MX_ERR_UNSUPPORTED;
   ProducerArgs a;
   a.x = x;
   a.ld_bytes = ld_x * (src_type == MX_SRC_BF16 ? 2 : 4);
@@ -281,6 +285,8 @@ static int quantize_call(const void* src, int32_t src_type, int64_t rows, int64_
                 int32_t layout, void* codes, uint8_t* scales, hipStream_t stream) {
   const int st = check_quantize_args(src, src_type, rows, k, ld_src, fmt, layout, codes, scales);
   if (st != MX_OK || rows == 0 || k == 0) return st;
+  if (quantize_grid_items(rows, k, layout == MX_LAYOUT_TILED ? kLayoutTiled : kLayoutRows) > kMaxGridItems)
+    return MX_ERR_UNSUPPORTED;
   if (layout == MX_LAYOUT_TILED) {
     if (tiled_codes_bytes(rows, k, fmt_bits(fmt)) >= ((int64_t)1 << 40)) return MX_ERR_UNSUPPORTED;
     return hip_status(
@@ -362,6 +368,14 @@ static int gemm_call(const void* a_src, int32_t a_src_type, int64_t lda, const v
   if (need > 0 && (!workspace || workspace_bytes < need)) return MX_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, kWsAlign)) return MX_ERR_ALIGN;
   if (m == 0 || n == 0) return MX_OK;
+  // launch limits, checked before anything is launched
+  const int64_t tiles_m = ceil_div(m, kTileM), tiles_n = ceil_div(n, cfg.tile_n);
+  if (tiles_m * tiles_n > INT32_MAX) return MX_ERR_SHAPE;
+  if (gemm_grid_items(tiles_m, tiles_n, cfg.waves) > kMaxGridItems) return MX_ERR_UNSUPPORTED;
+  // the kernel addresses one stage of an operand with 32-bit offsets
+  const int64_t chunk = chunk_codes(fmt_bits(w_fmt));
+  if (ceil_div(m, kTileGroupRows) * chunk >= ((int64_t)1 << 32) || ceil_div(n, kTileGroupRows) * chunk >= ((int64_t)1 << 32))
+    return MX_ERR_UNSUPPORTED;
 
   const uint8_t* xc = static_cast<const uint8_t*>(a_codes);
   const uint8_t* xs = a_scales;
@@ -385,8 +399,8 @@ static int gemm_call(const void* a_src, int32_t a_src_type, int64_t lda, const v
   g.M = (int32_t)m;
   g.N = (int32_t)n;
   g.K = (int32_t)k;
-  g.tiles_m = (int32_t)ceil_div(m, kTileM);
-  g.tiles_n = (int32_t)ceil_div(n, cfg.tile_n);
+  g.tiles_m = (int32_t)tiles_m;
+  g.tiles_n = (int32_t)tiles_n;
   g.tile_n = cfg.tile_n;
   g.waves = cfg.waves;
   g.gx = (int32_t)ceil_div(m, kTileGroupRows);
@@ -395,11 +409,6 @@ static int gemm_call(const void* a_src, int32_t a_src_type, int64_t lda, const v
   g.vec_store = out_kind != MX_OUT_MX && aligned(out, 16) && (ldo * esize) % 16 == 0;
   g.group_m = cfg.group_m;
   g.xcd_remap = cfg.xcd_remap;
-  if ((int64_t)g.tiles_m * g.tiles_n > INT32_MAX) return MX_ERR_SHAPE;
-  // the kernel addresses one stage of an operand with 32-bit offsets
-  const int64_t chunk = chunk_codes(fmt_bits(w_fmt));
-  if ((int64_t)g.gx * chunk >= ((int64_t)1 << 32) || (int64_t)g.gw * chunk >= ((int64_t)1 << 32))
-    return MX_ERR_UNSUPPORTED;
   return hip_status(launch_gemm(g, a_fmt, w_fmt, epilogue, out_kind, out_fmt, stream));
 }
 

@@ -30,6 +30,7 @@
 //  * all rows of a group share one conditioning row (rows_per_cond is a
 //    multiple of 32), so the stage's gain and modulation vectors are folded
 //    into one (a, b) pair per feature in LDS.
+#include "grid_limits.h"
 #include "internal.h"
 #include "mx_device.h"
 
@@ -363,10 +364,14 @@ __global__ __launch_bounds__(64 * kRWaves, 2) void rmsnorm_quantize_rows_kernel(
   }
 }
 
+// bf16 rows of up to kRMaxD features take the register-resident kernel (two
+// workgroups per 32-row group), the rest the two-pass kernel (one per group)
+bool rows_kernel(int64_t d, bool f32) { return !f32 && d <= kRMaxD; }
+
 template <int FMT>
 void launch_fmt(const ProducerArgs& a, bool f32, hipStream_t stream) {
   const dim3 grid((unsigned)a.groups), block(kPThreads);
-  if (!f32 && a.d <= kRMaxD)
+  if (rows_kernel(a.d, f32))
     hipLaunchKernelGGL((rmsnorm_quantize_rows_kernel<FMT>), dim3(2 * (unsigned)a.groups), dim3(64 * kRWaves), 0,
                        stream, a);
   else if (f32)
@@ -377,8 +382,14 @@ void launch_fmt(const ProducerArgs& a, bool f32, hipStream_t stream) {
 
 }  // namespace
 
+int64_t rmsnorm_quantize_grid_items(int64_t rows, int64_t d, int src_type) {
+  const int64_t groups = ceil_div(rows, kTileGroupRows);
+  return rows_kernel(d, src_type == kSrcF32) ? 2 * groups * 64 * kRWaves : groups * kPThreads;
+}
+
 hipError_t launch_rmsnorm_quantize(const ProducerArgs& a, int src_type, int fmt, hipStream_t stream) {
   if (a.groups == 0 || a.d == 0) return hipSuccess;
+  if (rmsnorm_quantize_grid_items(a.rows, a.d, src_type) > kMaxGridItems) return hipErrorInvalidConfiguration;
   if (fmt == kFmtE2M3)
     launch_fmt<kFmtE2M3>(a, src_type == kSrcF32, stream);
   else

@@ -19,6 +19,7 @@
 //    lanes.
 #include <algorithm>
 
+#include "grid_limits.h"
 #include "internal.h"
 #include "mx_device.h"
 
@@ -312,12 +313,21 @@ void launch_tiled_fmt(const uint8_t* s, bool f32, int64_t ldb, int rows, int k, 
 
 }  // namespace
 
+// rows layout: one lane per block; tiled layout: the resident workgroups walk the chunks
+int64_t quantize_grid_items(int64_t rows, int64_t k, int layout) {
+  if (layout == kLayoutTiled)
+    return std::min<int64_t>(ceil_div(ceil_div(rows, kTileGroupRows) * ceil_div(k, kTileStageK), kTWaves),
+                             kTResident) * kTWaves * 64;
+  return ceil_div(rows * (k / 32), kQThreads) * kQThreads;
+}
+
 hipError_t launch_quantize(const void* src, int src_type, int64_t rows, int64_t k, int64_t ld_src, int fmt,
                            uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   const int64_t kblocks = k / 32;
   const int64_t total = rows * kblocks;
   if (total == 0) return hipSuccess;
-  const int64_t grid = (total + 64 * kQWaves - 1) / (64 * kQWaves);
+  if (quantize_grid_items(rows, k, kLayoutRows) > kMaxGridItems) return hipErrorInvalidConfiguration;
+  const int64_t grid = quantize_grid_items(rows, k, kLayoutRows) / kQThreads;
   const uint8_t* s = static_cast<const uint8_t*>(src);
   const int vec_out = ((uintptr_t)codes % 16) == 0;
   const int64_t ldb = ld_src * (src_type == kSrcBf16 ? 2 : 4);
@@ -339,7 +349,7 @@ hipError_t launch_quantize_tiled(const void* src, int src_type, int64_t rows, in
   const int64_t groups = ceil_div(rows, kTileGroupRows), stages = ceil_div(k, kTileStageK);
   const int64_t nchunks = groups * stages;
   if (nchunks == 0) return hipSuccess;
-  const dim3 g((unsigned)std::min<int64_t>(ceil_div(nchunks, kTWaves), kTResident)), blk(kTWaves * 64);
+  const dim3 g((unsigned)(quantize_grid_items(rows, k, kLayoutTiled) / (kTWaves * 64))), blk(kTWaves * 64);
   const uint8_t* s = static_cast<const uint8_t*>(src);
   const int64_t ldb = ld_src * (src_type == kSrcBf16 ? 2 : 4);
   const bool f32 = src_type == kSrcF32;

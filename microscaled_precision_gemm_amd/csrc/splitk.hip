@@ -44,6 +44,7 @@
 //    workgroup adds the S partials in the fixed order 0 .. S-1 (deterministic)
 //    and rounds once into the output.  No partials touch HBM and no second
 //    kernel is launched.
+#include "grid_limits.h"
 #include "internal.h"
 #include "mx_device.h"
 
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) 
 
 template <int OUT, bool LDS_SCALES>
 hipError_t launch_fmt(const SplitKArgs& a, int x_fmt, int w_fmt, hipStream_t stream) {
-  const dim3 grid((unsigned)ceil_div(a.gw, kSkGroups)), block(kSkThreads);
+  const dim3 grid((unsigned)(splitk_grid_items(a.N) / kSkThreads)), block(kSkThreads);
   if (w_fmt == kFmtE2M3 && x_fmt == kFmtE2M3)
     hipLaunchKernelGGL((splitk_kernel<kFmtE2M3, kFmtE2M3, OUT, LDS_SCALES>), grid, block, 0, stream, a);
   else if (w_fmt == kFmtE3M2 && x_fmt == kFmtE2M3)
@@ -333,8 +334,12 @@ hipError_t launch_out(const SplitKArgs& a, int x_fmt, int w_fmt, hipStream_t str
 
 }  // namespace
 
+// one workgroup per kSkGroups 32-feature weight groups
+int64_t splitk_grid_items(int64_t n) { return ceil_div(ceil_div(n, kTileGroupRows), kSkGroups) * kSkThreads; }
+
 hipError_t launch_gemm_splitk(const SplitKArgs& a, int x_fmt, int w_fmt, int out_kind, hipStream_t stream) {
   if (a.splits < 1 || a.splits > kMaxSplits || a.M > 16) return hipErrorInvalidValue;
+  if (splitk_grid_items(a.N) > kMaxGridItems) return hipErrorInvalidConfiguration;
   return out_kind == kOutBf16 ? launch_out<kOutBf16>(a, x_fmt, w_fmt, stream)
                               : launch_out<kOutF32>(a, x_fmt, w_fmt, stream);
 }

@@ -106,6 +106,23 @@ def make_w(w: Workload, n: int | None = None, k: int | None = None) -> torch.Ten
     return to_bf16(x)
 
 
+def device_normal_bf16(rows: int, cols: int, seed: int, std: float, device) -> torch.Tensor:
+    """Seeded N(0, std^2) matrix [rows, cols] drawn on the device, for inputs of
+    many GiB that are too large to draw on the host: torch's generator on that
+    device seeded with `seed`, fp32 draws in slabs of at most 2^28 values (so
+    the fp32 draw never holds more than one slab), each scaled and rounded to
+    bf16.  Checks read the rows they sample back from the device."""
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=device)
+    slab_rows = max(1, (1 << 28) // max(cols, 1))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    for r0 in range(0, rows, slab_rows):
+        r1 = min(rows, r0 + slab_rows)
+        slab = torch.randn((r1 - r0, cols), generator=gen, dtype=torch.float32, device=device)
+        out[r0:r1] = (slab * std).to(torch.bfloat16)
+    return out
+
+
 def as_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a bf16/fp32 CPU tensor, for the CPU oracle."""
     return t.detach().cpu().to(torch.float64).numpy()

@@ -79,6 +79,27 @@ def tiled_to_rows(codes_t: np.ndarray, scales_t: np.ndarray, rows: int, k: int, 
     return c[:rows, :kb], s[:rows, :k // 32], pad_c, pad_s
 
 
+def mx_rows_gather(gpu_mx, rows) -> tuple[np.ndarray, np.ndarray]:
+    """Row-major packed codes [len(rows), bits*k/8] and scales [len(rows), k/32]
+    of the given rows of an MXTensor in the tiled layout, gathered where the
+    tensor lives: only those rows' bytes are copied to the host (for matrices
+    of many GiB).  Same result as tiled_to_rows on the whole tensor, then
+    [rows]."""
+    bits = O.element_bits(gpu_mx.fmt)
+    stages, groups = -(-gpu_mx.k // 128), -(-gpu_mx.rows // 32)
+    rows = np.asarray(rows, dtype=np.int64)
+    grp, j = rows // 32, rows % 32
+    chunk = np.arange(stages, dtype=np.int64)[None, :] * groups + grp[:, None]          # [R, stages]
+    cidx = chunk[:, :, None] * (512 * bits) + _CHUNK_OFFSETS[bits][j][:, None, :]       # [R, stages, 16 bits]
+    sidx = (chunk[:, :, None] * 32 + j[:, None, None]) * 4 + np.arange(4)               # [R, stages, 4]
+    dev = gpu_mx.codes.device
+    c = gpu_mx.codes.reshape(-1)[torch.from_numpy(cidx.reshape(-1)).to(dev)]
+    sc = gpu_mx.scales.reshape(-1)[torch.from_numpy(sidx.reshape(-1)).to(dev)]
+    c = to_np(c).reshape(len(rows), stages * 16 * bits)
+    sc = to_np(sc).reshape(len(rows), stages * 4)
+    return c[:, :bits * gpu_mx.k // 8], sc[:, :gpu_mx.k // 32]
+
+
 def mx_rows_view(gpu_mx):
     """Row-major (codes, scales) of a GPU MXTensor, checking tiled padding."""
     gc, gs = to_np(gpu_mx.codes), to_np(gpu_mx.scales)

@@ -255,6 +255,31 @@ def test_splitk_noalloc_validation(L):
     assert sk_noalloc(m=0) == B.MX_OK  # nothing to do: no HIP call
 
 
+@host_only
+def test_size_limits_rejected_before_launch(L):
+    """Requests past the launch limits (a kernel of 2^32 lanes or more, one
+    GEMM operand stage of 4 GiB or more, a tiled matrix of 2^40 code bytes or
+    more) return MX_ERR_UNSUPPORTED on the host, before anything is launched;
+    a dimension above 2^30 is MX_ERR_SHAPE."""
+    s = NULL
+    # rows layout: one lane per 32-element block; 2^27 rows x 32 blocks = 2^32 lanes
+    assert q(FAKE, 0, 1 << 27, 1024, 1024, 2, 0, FAKE, FAKE, s) == B.MX_ERR_UNSUPPORTED
+    # tiled layout: 2^23 stages x 2^25 groups of 3072 bytes
+    assert q(FAKE, 0, 1 << 30, 1 << 30, 1 << 30, 2, 1, FAKE, FAKE, s) == B.MX_ERR_UNSUPPORTED
+    assert q(FAKE, 0, (1 << 30) + 1, 64, 64, 2, 1, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    # producer: bf16 rows of up to 3072 take 2 x 512 lanes per 32-row group
+    assert rq(rows=1 << 27, d=32, ld=32) == B.MX_ERR_UNSUPPORTED
+    # fp32 (the two-pass kernel): 256 lanes per group
+    assert rq(rows=1 << 30, d=32, ld=32, src_type=1) == B.MX_ERR_UNSUPPORTED
+    # GEMM: 2^14 x 2^14 tiles of 256 lanes; a stage of 2^21 row groups x 3072 bytes
+    assert g(m=1 << 22, n=1 << 22, ldo=1 << 22) == B.MX_ERR_UNSUPPORTED
+    assert g(m=1 << 26, n=64) == B.MX_ERR_UNSUPPORTED
+    assert g(m=64, n=1 << 26, ldo=1 << 26) == B.MX_ERR_UNSUPPORTED
+    assert g(m=1 << 25, n=1 << 25, ldo=1 << 25) == B.MX_ERR_SHAPE  # 2^34 tiles
+    # split-K: one workgroup of 256 lanes per 64 weight rows
+    assert sk(n=1 << 30, k=128, splits=1, ldo=1 << 30) == B.MX_ERR_UNSUPPORTED
+
+
 def test_packed_bytes(L):
     assert mx.mx_packed_bytes(300, 416, "rows", 0) == 300 * 416 * 3 // 4
     assert mx.mx_packed_bytes(300, 416, "rows", 1) == 300 * 13

@@ -93,3 +93,27 @@ def test_tiled_round_trip_fp4_fp8():
         c, sc, pad_c, pad_s = tiled_to_rows(ct.ravel(), st.ravel(), rows, k, bits)
         assert np.array_equal(c, packed) and not pad_c.any()
         assert np.array_equal(O.unpack(c, k, fmt), codes)
+
+
+def test_rows_gather_matches_the_whole_view():
+    """mx_rows_gather (the large-size tests' device-side row pick) returns the
+    same bytes as tiled_to_rows over the whole tensor, for every element width,
+    ragged rows and K, rows in any order and repeated."""
+    import types
+
+    import torch
+
+    from tests.parity import mx_rows_gather
+
+    rng = np.random.default_rng(5)
+    for fmt, bits in (("e2m3", 6), ("e2m1", 4), ("e4m3", 8)):
+        rows, k = 77, 416  # 3 groups (ragged), 4 stages (ragged)
+        stages, groups = 4, 3
+        codes = rng.integers(0, 256, size=stages * groups * 512 * bits, dtype=np.uint8)
+        scales = rng.integers(0, 256, size=stages * groups * 128, dtype=np.uint8)
+        t = types.SimpleNamespace(codes=torch.from_numpy(codes), scales=torch.from_numpy(scales), fmt=fmt,
+                                  rows=rows, k=k, layout="tiled")
+        c, s, _, _ = tiled_to_rows(codes, scales, rows, k, bits)
+        pick = np.array([76, 0, 31, 32, 33, 64, 5, 5])
+        gc, gs = mx_rows_gather(t, pick)
+        assert np.array_equal(gc, c[pick]) and np.array_equal(gs, s[pick])
