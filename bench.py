@@ -655,8 +655,8 @@ def oracle_per_config(w1, w2) -> dict:
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skinny-iters", type=int, default=100)
     p.add_argument("--no-tune", action="store_true", help="use the library's default launch configuration")
