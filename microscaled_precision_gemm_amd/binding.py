@@ -276,6 +276,14 @@ def mx_rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor | None = None, shif
                 raise ValueError(f"{name} must be a contiguous fp32 tensor")
             if v.shape[-1] != d:
                 raise ValueError(f"{name} must have d = {d} features")
+    if gamma is not None and gamma.numel() != d:
+        raise ValueError(f"gamma must be [{d}]")
+    if rows_per_cond > 0 and rows > 0:
+        # the kernel reads conditioning row r // rows_per_cond for every row r
+        n_cond = -(-rows // rows_per_cond)
+        for name, v in (("shift", shift), ("scale", scale)):
+            if v is not None and v.numel() < n_cond * d:
+                raise ValueError(f"{name} must hold ceil(rows / rows_per_cond) = {n_cond} rows of {d} features")
     if out is not None:
         if out.rows != rows or out.k != d or out.layout != "tiled" or out.fmt != fmt:
             raise ValueError(f"out must be a tiled [rows, d] {fmt} MX matrix")

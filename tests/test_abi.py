@@ -337,6 +337,18 @@ def test_quantize_and_producer_bindings_check_out_before_launch(L):
         mx.mx_rmsnorm_quantize(x, gamma=torch.ones(64, dtype=torch.float32))
     with pytest.raises(ValueError, match="GPU"):
         mx.mx_rmsnorm_quantize(x, gamma=torch.ones(128, dtype=torch.float32), out=_cpu_mx(32, 128))
+    with pytest.raises(ValueError, match="gamma"):
+        mx.mx_rmsnorm_quantize(x, gamma=torch.ones(2, 128, dtype=torch.float32))
+    # the kernel reads conditioning row r // rows_per_cond for every row r: 96
+    # rows at 32 rows per conditioning need 3 rows of shift and of scale
+    x96 = torch.zeros(96, 128, dtype=torch.bfloat16)
+    two = torch.zeros(2, 128, dtype=torch.float32)
+    with pytest.raises(ValueError, match="shift must hold"):
+        mx.mx_rmsnorm_quantize(x96, shift=two, rows_per_cond=32)
+    with pytest.raises(ValueError, match="scale must hold"):
+        mx.mx_rmsnorm_quantize(x96, scale=torch.zeros(128, dtype=torch.float32), rows_per_cond=64)
+    with pytest.raises(ValueError, match="GPU"):  # 2 rows at 64 rows per conditioning: sizes pass
+        mx.mx_rmsnorm_quantize(x96, shift=two, scale=two, rows_per_cond=64)
 
 
 def _cpu_mx(rows, k, fmt="e2m3"):
