@@ -126,7 +126,7 @@ def test_exhaustive_round_trip(fmt):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
-@pytest.mark.parametrize("shift", [-130, -20, -1, 3, 60, 100])
+@pytest.mark.parametrize("shift", [-120, -20, -1, 3, 60, 100])
 def test_round_trip_under_any_scale(fmt, shift):
     """Scaling a block by 2**k changes only the scale byte (by k), never the codes."""
     vals = O.element_values(fmt)
@@ -139,9 +139,7 @@ def test_round_trip_under_any_scale(fmt, shift):
     base[0, 1:] = vals[pick]
     base[1, 1:] = vals[half + pick]
     c0, s0 = O.quantize(base, fmt)
-    scaled = np.ldexp(base, shift)
-    if not np.all(np.isfinite(scaled)) or shift < -120:
-        pytest.skip("scale outside the normal E8M0 range for this table")
+    scaled = np.ldexp(base, shift)  # scale bytes 7 .. 227: inside the E8M0 range, no clamp
     c1, s1 = O.quantize(scaled, fmt)
     np.testing.assert_array_equal(c0, c1)
     np.testing.assert_array_equal(s1.astype(int), s0.astype(int) + shift)
