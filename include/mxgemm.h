@@ -295,7 +295,7 @@ typedef struct {
                         only, else MX_ERR_UNSUPPORTED)                                      */
   int32_t waves;     /* waves per workgroup: 4 (default) or, with tile_n = 256, 8 (2 x 4 waves
                         of 128 x 64, two per SIMD, sharing the tile's operand ring; any format
-                        pair, not MX_EPI_SWIGLU, else MX_ERR_UNSUPPORTED)                     */
+                        pair and epilogue; with tile_n = 128, MX_ERR_UNSUPPORTED)             */
 } mx_gemm_config;
 
 /* mx_gemm_default_config - fill *config with the generic configuration
@@ -311,9 +311,8 @@ void mx_gemm_default_config(mx_gemm_config* config);
  * kernels", found library GEMMs doing exactly that).  The rule, from timings
  * of every candidate on the workload shapes on MI355X:
  *   - FP8 operands, or MX_EPI_SWIGLU: the generic configuration;
- *   - 6-bit operands with MX_OUT_MX and k <= 4096: tile_n 128, group_m 8;
- *   - otherwise (4- and 6-bit operands, f32 / bf16 output, or MX output with
- *     long K): 8 waves, group_m 4.
+ *   - otherwise (4- and 6-bit operands): 8 waves on 256-feature tiles, with
+ *     group_m 8 for MX_OUT_MX and group_m 4 for f32 / bf16 output.
  * Arguments as mx_gemm's; nothing is validated (an invalid call still fails
  * in mx_gemm).
  */

@@ -310,7 +310,7 @@ void mx_gemm_select_config(int64_t m, int64_t n, int64_t k, int32_t a_fmt, int32
   (void)m;
   (void)n;
   const bool fp8 = fmt_bits(a_fmt) == 8 || fmt_bits(w_fmt) == 8;
-  if (fp8 || epilogue == MX_EPI_SWIGLU) return;  // 8 waves slow FP8 down; the SwiGLU pairing takes 4 waves
+  if (fp8 || epilogue == MX_EPI_SWIGLU) return;  // 8 waves slow FP8 down; SwiGLU keeps the default until timed
   // the 4- and 6-bit types: two waves per SIMD hide the operand reads from
   // LDS behind the other wave's matrix work; with the MX epilogue (fc1's
   // shape) a wider tile walk as well
@@ -350,8 +350,8 @@ static int gemm_call(const void* a_src, int32_t a_src_type, int64_t lda, const v
   if (!fp6_fmt(w_fmt) && (epilogue != MX_EPI_NONE || out_kind == MX_OUT_MX)) return MX_ERR_UNSUPPORTED;
   // 128-feature tiles: the 6-bit pairs
   if (cfg.tile_n == 128 && !fp6_fmt(w_fmt)) return MX_ERR_UNSUPPORTED;
-  // eight waves: 256-feature tiles, not the SwiGLU pairing
-  if (cfg.waves == 8 && (cfg.tile_n != 256 || epilogue == MX_EPI_SWIGLU)) return MX_ERR_UNSUPPORTED;
+  // eight waves: 256-feature tiles
+  if (cfg.waves == 8 && cfg.tile_n != 256) return MX_ERR_UNSUPPORTED;
   const int64_t n_out = epilogue == MX_EPI_SWIGLU ? n / 2 : n;
   if (!out) return MX_ERR_NULL;
   if (out_kind == MX_OUT_MX) {

@@ -236,11 +236,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int WF, int XF, int OUT, int EPI, int OFMT, int TN = 256, int WV = 4>
 __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const GemmArgs g) {
   using R = Ring<WF, XF, TN, WV>;
-  static_assert(WV == 4 || EPI != kEpiSwiglu, "the SwiGLU pairing takes 4 waves");
   constexpr bool kSwiglu = EPI == kEpiSwiglu;
-  // SwiGLU on 128-feature tiles: the tile's 128 weight rows are one run of 64
-  // gate rows and the 64 up rows of the same features, so wave wn takes gate
-  // group wn and up group 2 + wn as its two fragments (32 output features).
+  // SwiGLU where a wave holds two weight fragments (128-feature tiles with 4
+  // waves, 256-feature tiles with 8): each run of 128 weight rows is 64 gate
+  // rows and the 64 up rows of the same features, so the wave takes gate group
+  // g and up group 2 + g of one run (run wn / 2, g = wn % 2) as its two
+  // fragments, 32 output features, and each gate value's up value is in the
+  // same lane.  With four fragments per wave (256-feature tiles, 4 waves) the
+  // wave's 128 rows are one whole run.
+  constexpr bool kSwPair = kSwiglu && R::kFW == 2;
   constexpr bool kSwNarrow = kSwiglu && TN == 128;
   __shared__ __attribute__((aligned(16))) uint8_t lds[R::kLds];
   constexpr int kLayout = OUT == kOutMx ? kLayoutMx : kLayoutContig;
@@ -322,14 +326,15 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
   const int h = lane >> 5, j = lane & 31;
   const int wrow = feature_of_row<kLayout>(j);
   constexpr int kFW = R::kFW, kMP = R::kMfmaPhase;
-  // chunk of the wave's first weight fragment (in units of kWaveChunksW) and
-  // the chunk stride between its fragments
-  constexpr int kWaveChunksW = kSwNarrow ? 1 : kFW, kFragChunksW = kSwNarrow ? 2 : 1;
-  const int w16 = R::kOffW + wn * kWaveChunksW * R::kChunkW + h * R::kHalfW + wrow * 16;
+  // chunk of the wave's first weight fragment and the chunk stride between
+  // its fragments
+  const int wchunk = kSwPair ? 4 * (wn / 2) + wn % 2 : wn * kFW;
+  constexpr int kFragChunksW = kSwPair ? 2 : 1;
+  const int w16 = R::kOffW + wchunk * R::kChunkW + h * R::kHalfW + wrow * 16;
   const int x16 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 16;
-  const int w8 = R::kOffW + wn * kWaveChunksW * R::kChunkW + h * R::kHalfW + wrow * 8;
+  const int w8 = R::kOffW + wchunk * R::kChunkW + h * R::kHalfW + wrow * 8;
   const int x8 = R::kOffX + wm * 4 * R::kChunkX + h * R::kHalfX + j * 8;
-  const int wsc = R::kOffWs + wn * kWaveChunksW * kChunkScales + wrow * 4 + 2 * h;
+  const int wsc = R::kOffWs + wchunk * kChunkScales + wrow * 4 + 2 * h;
   const int xsc = R::kOffXs + wm * 4 * kChunkScales + j * 4 + 2 * h;
 
   v16f acc[kFW][4];
@@ -646,10 +651,10 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
       convert_pair(va, vb, q, sbyte);
       store_block(q, sbyte, m, gm, stage, 2 * pr + h);
     };
-    if constexpr (kSwNarrow) {
-      // SwiGLU on 128-feature tiles: the wave's 32 output features nw0/2 .. +31
-      // are one block; pair token fragments fp and fp + 1 instead (lane half h:
-      // the block of token fragment fp + h)
+    if constexpr (kSwPair) {
+      // SwiGLU with two fragments per wave: the wave's 32 output features
+      // nw0/2 .. +31 are one block; pair token fragments fp and fp + 1 instead
+      // (lane half h: the block of token fragment fp + h)
       const int ob = nw0 / 2;
       const int stage = ob / kTileStageK, qb = (ob % kTileStageK) / 32;
 #pragma unroll
@@ -665,9 +670,12 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
         convert_pair(va, vb, q, sbyte);
         const int mrow0 = mw0 + (fp + h) * 32;
         store_block(q, sbyte, mrow0 + j, mrow0 / kTileGroupRows, stage, qb);
-        // the stage's other 64 features have no tile when the output ends here:
-        // write their layout padding (block index past n_out / 32)
-        if (qb < 2 && n0 / 2 + 64 >= n_out) store_block(q, sbyte, mrow0 + j, mrow0 / kTileGroupRows, stage, qb + 2);
+        // 128-feature tiles (64 output features, half a stage): the stage's
+        // other 64 features have no tile when the output ends here, so write
+        // their layout padding (block index past n_out / 32).  A 256-feature
+        // tile covers its whole output stage, every block by its own wave.
+        if (kSwNarrow && qb < 2 && n0 / 2 + 64 >= n_out)
+          store_block(q, sbyte, mrow0 + j, mrow0 / kTileGroupRows, stage, qb + 2);
       }
       return;
     }
@@ -784,10 +792,10 @@ hipError_t launch_variant(const GemmArgs& a, int epilogue, int out_kind, int out
   if (a.waves == 8) {
     if (epilogue == kEpiGeluTanh)
       launch_epi<WF, XF, kEpiGeluTanh, 256, 8>(a, out_kind, out_fmt, grid, stream);
-    else if (epilogue == kEpiNone)
-      launch_epi<WF, XF, kEpiNone, 256, 8>(a, out_kind, out_fmt, grid, stream);
+    else if (epilogue == kEpiSwiglu)
+      launch_epi<WF, XF, kEpiSwiglu, 256, 8>(a, out_kind, out_fmt, grid, stream);
     else
-      return hipErrorInvalidValue;  // SwiGLU needs 128 weight rows per wave (rejected before this point)
+      launch_epi<WF, XF, kEpiNone, 256, 8>(a, out_kind, out_fmt, grid, stream);
     return hipGetLastError();
   }
   if (epilogue == kEpiGeluTanh)

@@ -61,12 +61,12 @@ FP6 = ("e2m3", "e3m2")
 
 def supports(config: tuple[int, int, int, int], a_fmt: str, w_fmt: str, epilogue: str) -> bool:
     """Whether mx_gemm accepts this configuration for the call: 128-feature
-    tiles take 6-bit operands (every epilogue), 8 waves 256-feature tiles
-    without the SwiGLU pairing."""
+    tiles take 6-bit operands (every epilogue) and 4 waves; 256-feature tiles
+    take 4 or 8 waves (every pair and epilogue)."""
     _, _, tile_n, waves = config
     if tile_n == 128:
         return waves == 4 and a_fmt in FP6 and w_fmt in FP6
-    return waves == 4 or epilogue != "swiglu"
+    return waves in (4, 8)
 
 
 def device_name(device: torch.device | None = None) -> str:

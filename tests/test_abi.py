@@ -193,13 +193,15 @@ def test_gemm_config_validation(L):
     assert L.mx_gemm_with_config(*dict(args, epi=2, n=128, m=0).values(), ctypes.byref(narrow), NULL) == B.MX_OK
     assert L.mx_gemm_with_config(*dict(args, a_fmt=0, w_fmt=0).values(), ctypes.byref(narrow),
                                  NULL) == B.MX_ERR_UNSUPPORTED
-    # eight waves: 256-feature tiles of every pair, not SwiGLU, not with 128-feature tiles
+    # eight waves: 256-feature tiles of every pair and epilogue, not with 128-feature tiles
     eight = B.MXGemmConfig(4, 1, 256, 8)
     assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(eight), NULL) == B.MX_OK
     assert L.mx_gemm_with_config(*dict(args, m=0, a_fmt=0, w_fmt=0).values(), ctypes.byref(eight),
                                  NULL) == B.MX_OK
-    assert L.mx_gemm_with_config(*dict(args, epi=2, n=128).values(), ctypes.byref(eight),
-                                 NULL) == B.MX_ERR_UNSUPPORTED
+    assert L.mx_gemm_with_config(*dict(args, epi=2, n=128, m=0).values(), ctypes.byref(eight),
+                                 NULL) == B.MX_OK
+    assert L.mx_gemm_with_config(*dict(args, epi=2, n=192).values(), ctypes.byref(eight),
+                                 NULL) == B.MX_ERR_UNSUPPORTED  # gate/up runs of 128 rows
     narrow8 = B.MXGemmConfig(4, 1, 128, 8)
     assert L.mx_gemm_with_config(*dict(args, m=0).values(), ctypes.byref(narrow8), NULL) == B.MX_ERR_UNSUPPORTED
 

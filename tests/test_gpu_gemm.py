@@ -324,17 +324,16 @@ def test_determinism_guard_bands_and_poison(cfg):
     assert torch.equal(o.codes, o2.codes) and torch.equal(o.scales, o2.scales)
     assert not torch.any(o.scales == 0xFF)
     mx_rows_view(o)  # padding of the tiled output written as 0 codes / 127 scales
-    if cfg != EIGHT:
-        # SwiGLU (n = 544 stacked rows is not whole runs of 128: use 512) into a strided view
-        ws = mx.mx_quantize(w[:512].cuda(), "e2m3")
-        big = torch.full((m + 8, 256 + 24), float("nan"), dtype=torch.float32, device="cuda")
-        big[m:, :] = 12345.0
-        big[:, 256:] = 12345.0
-        mx.mx_gemm(aq, ws, out_kind="f32", epilogue="swiglu", out=big[:m, :256], config=cfg)
-        ref = mx.mx_gemm(aq, ws, out_kind="f32", epilogue="swiglu")
-        torch.cuda.synchronize()
-        assert torch.equal(big[:m, :256], ref)
-        assert torch.all(big[m:, :] == 12345.0) and torch.all(big[:, 256:] == 12345.0)
+    # SwiGLU (n = 544 stacked rows is not whole runs of 128: use 512) into a strided view
+    ws = mx.mx_quantize(w[:512].cuda(), "e2m3")
+    big = torch.full((m + 8, 256 + 24), float("nan"), dtype=torch.float32, device="cuda")
+    big[m:, :] = 12345.0
+    big[:, 256:] = 12345.0
+    mx.mx_gemm(aq, ws, out_kind="f32", epilogue="swiglu", out=big[:m, :256], config=cfg)
+    ref = mx.mx_gemm(aq, ws, out_kind="f32", epilogue="swiglu")
+    torch.cuda.synchronize()
+    assert torch.equal(big[:m, :256], ref)
+    assert torch.all(big[m:, :] == 12345.0) and torch.all(big[:, 256:] == 12345.0)
 
 
 def test_edge_shapes():
@@ -477,11 +476,13 @@ def test_swiglu_f32_and_bf16(a_fmt, w_fmt, m, h, k):
     wq = _gpu_weights(w, w_fmt, qw)
     o32 = mx.mx_gemm(a.cuda(), wq, out_kind="f32", epilogue="swiglu", a_fmt=a_fmt)
     o16 = mx.mx_gemm(a.cuda(), wq, out_kind="bf16", epilogue="swiglu", a_fmt=a_fmt)
-    # 128-row tiles (one gate/up run per tile): the same bytes
-    n32 = mx.mx_gemm(a.cuda(), wq, out_kind="f32", epilogue="swiglu", a_fmt=a_fmt, config=NARROW)
-    n16 = mx.mx_gemm(a.cuda(), wq, out_kind="bf16", epilogue="swiglu", a_fmt=a_fmt, config=NARROW)
-    torch.cuda.synchronize()
-    assert torch.equal(n32, o32) and torch.equal(n16, o16)
+    # 128-row tiles (one gate/up run per tile) and 8-wave 256-row tiles (a
+    # wave per gate/up group pair): the same bytes
+    for cfg in (NARROW, EIGHT):
+        c32 = mx.mx_gemm(a.cuda(), wq, out_kind="f32", epilogue="swiglu", a_fmt=a_fmt, config=cfg)
+        c16 = mx.mx_gemm(a.cuda(), wq, out_kind="bf16", epilogue="swiglu", a_fmt=a_fmt, config=cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(c32, o32) and torch.equal(c16, o16), cfg
     assert tuple(o32.shape) == (m, h)
     bound = swiglu_bound(gate, up, sg, su, out)
     got = to_np(o32).astype(np.float64)
@@ -493,7 +494,7 @@ def test_swiglu_f32_and_bf16(a_fmt, w_fmt, m, h, k):
     assert bad.size == 0, f"{len(bad)} bf16 SwiGLU outputs off; first {bad[0].tolist()}"
 
 
-@pytest.mark.parametrize("cfg", [None, NARROW], ids=["tile256", "tile128"])
+@pytest.mark.parametrize("cfg", [None, NARROW, EIGHT], ids=["tile256", "tile128", "tile256x8"])
 @pytest.mark.parametrize("out_fmt", ["e2m3", "e3m2"])
 @pytest.mark.parametrize("m,h,k", [(300, 320, 416), (64, 64, 128), (40, 192, 256)])
 def test_swiglu_mx_out(out_fmt, m, h, k, cfg):
@@ -501,7 +502,8 @@ def test_swiglu_mx_out(out_fmt, m, h, k, cfg):
     boundary-aware rule; the padding of the tiled output is checked too (the
     output buffer starts filled with 0xA5, so padding left unwritten fails).
     h = 320 and 192 end half-way through a 128-feature output stage: with
-    128-row tiles the last tile writes the stage's other half as padding."""
+    128-row tiles the last tile writes the stage's other half as padding, with
+    256-row tiles the waves of the tile's missing run write it."""
     from tests.parity import check_mx_values, swiglu_bound
     a, w, qa, qw, out, gate, up, sg, su = _swiglu_operands(m, h, k, seed=3 * m + h)
     say(f"gemm swiglu mx-out {m}x{2 * h}x{k} out={out_fmt} config={cfg}")

@@ -228,11 +228,12 @@ def test_swiglu_fc1_full_size_mx():
     wq = mx.mx_quantize(wt.to(dev), "e2m3")
     hq = mx.MXTensor.empty(w.m, h, "e2m3", "tiled", dev)
     mx.mx_gemm(xq, wq, out_kind="mx", epilogue="swiglu", out=hq)
-    # 128-row tiles (one gate/up run each): the same bytes
-    hn = mx.mx_gemm(xq, wq, out_kind="mx", epilogue="swiglu", config=(4, 1, 128, 4))
-    torch.cuda.synchronize()
-    assert torch.equal(hq.codes, hn.codes) and torch.equal(hq.scales, hn.scales)
-    del hn
+    # 128-row tiles (one gate/up run each) and 8-wave 256-row tiles: the same bytes
+    for cfg in ((4, 1, 128, 4), (4, 1, 256, 8)):
+        hn = mx.mx_gemm(xq, wq, out_kind="mx", epilogue="swiglu", config=cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(hq.codes, hn.codes) and torch.equal(hq.scales, hn.scales), cfg
+        del hn
     gc, gs = mx_rows_view(hq)
     codes_g = O.unpack(gc[rows], h)[:, feats]
     out, g, u, sg, su = _swiglu_sample_ref(x, wt, rows, feats, h)
