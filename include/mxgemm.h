@@ -310,9 +310,10 @@ void mx_gemm_default_config(mx_gemm_config* config);
  * configuration; the Hedra post, section "We tuned before writing custom
  * kernels", found library GEMMs doing exactly that).  The rule, from timings
  * of every candidate on the workload shapes on MI355X:
- *   - FP8 operands, or MX_EPI_SWIGLU: the generic configuration;
+ *   - FP8 operands: the generic configuration;
  *   - otherwise (4- and 6-bit operands): 8 waves on 256-feature tiles, with
- *     group_m 8 for MX_OUT_MX and group_m 4 for f32 / bf16 output.
+ *     group_m 8 for MX_OUT_MX after MX_EPI_NONE or MX_EPI_GELU_TANH and
+ *     group_m 4 otherwise.
  * Arguments as mx_gemm's; nothing is validated (an invalid call still fails
  * in mx_gemm).
  */

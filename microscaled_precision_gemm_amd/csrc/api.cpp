@@ -310,12 +310,12 @@ void mx_gemm_select_config(int64_t m, int64_t n, int64_t k, int32_t a_fmt, int32
   (void)m;
   (void)n;
   const bool fp8 = fmt_bits(a_fmt) == 8 || fmt_bits(w_fmt) == 8;
-  if (fp8 || epilogue == MX_EPI_SWIGLU) return;  // 8 waves slow FP8 down; SwiGLU keeps the default until timed
+  if (fp8) return;  // 8 waves slow FP8 down (two ring slots at 8 bits)
   // the 4- and 6-bit types: two waves per SIMD hide the operand reads from
-  // LDS behind the other wave's matrix work; with the MX epilogue (fc1's
-  // shape) a wider tile walk as well
+  // LDS behind the other wave's matrix work; with the GELU / identity MX
+  // epilogue (fc1's shape) a wider tile walk as well
   config->waves = 8;
-  if (out_kind == MX_OUT_MX) config->group_m = 8;
+  if (out_kind == MX_OUT_MX && epilogue != MX_EPI_SWIGLU) config->group_m = 8;
 }
 
 int mx_gemm(const void* a_src, int32_t a_src_type, int64_t lda, const void* a_codes, const uint8_t* a_scales,

@@ -78,7 +78,7 @@ def test_library_shape_rule():
     assert sel(4096, 3072, 3072).key() == (4, 1, 256, 8)
     assert sel(20480, 12288, 3072, "e2m1", "e2m1").key() == (4, 1, 256, 8)
     assert sel(20480, 12288, 3072, "e4m3", "e4m3").key() == (4, 1, 256, 4)
-    assert sel(20480, 16384, 3072, epilogue="swiglu", out_kind="mx").key() == (4, 1, 256, 4)
+    assert sel(20480, 16384, 3072, epilogue="swiglu", out_kind="mx").key() == (4, 1, 256, 8)
     assert sel(20480, 12288, 8192, epilogue="gelu_tanh", out_kind="mx").key() == (8, 1, 256, 8)
     assert mx.mx_gemm_default_config().key() == (4, 1, 256, 4)
     for af, wf in (("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e2m1", "e2m1"), ("e5m2", "e4m3")):
