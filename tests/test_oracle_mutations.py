@@ -114,6 +114,64 @@ def _bias_off(fmt):
 
 
 _ORIG_PACK = O.pack
+_ORIG_E8M0 = O.e8m0_value
+_ORIG_UNPACK = O.unpack
+_ORIG_QUANTIZE = O.quantize
+_ORIG_GEMM = O.gemm_ref
+
+
+def _e8m0_bias_128(u):
+    """The scale byte decoded with bias 128 instead of 127."""
+    return _ORIG_E8M0(np.asarray(u).astype(np.int64) - 1)
+
+
+def _unpack_msb_first(packed, k, fmt="e2m3"):
+    """6-bit codes read from the top of each 24-bit word down."""
+    if O.element_bits(fmt) != 6:
+        return _ORIG_UNPACK(packed, k, fmt)
+    packed = np.asarray(packed, dtype=np.uint32)
+    rows = packed.shape[0]
+    b = packed.reshape(rows, k // 4, 3)
+    w = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16)
+    q = np.stack([(w >> (6 * (3 - i))) & 63 for i in range(4)], axis=-1)
+    return q.reshape(rows, k).astype(np.uint8)
+
+
+def _rms_mean_over_rows(x, gamma=None, shift=None, scale=None, rows_per_cond=None, eps=1e-6):
+    """The mean of squares taken down the columns instead of along the row."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x / np.sqrt(np.mean(x * x, axis=0, keepdims=True) + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma)[None, :]
+    rows = x.shape[0]
+    c = np.arange(rows) // (rows if rows_per_cond is None else rows_per_cond)
+    if scale is not None:
+        y = y * (1.0 + np.asarray(scale)[c])
+    if shift is not None:
+        y = y + np.asarray(shift)[c]
+    return y
+
+
+def _quantize_no_saturation(x, fmt="e2m3"):
+    """Magnitudes above the largest element wrap to the zero code instead of
+    clamping to it."""
+    codes, scales = _ORIG_QUANTIZE(x, fmt)
+    x = np.asarray(x, dtype=np.float64)
+    rows, k = x.shape
+    sc = O.e8m0_value(scales)
+    r = np.abs(x.reshape(rows, k // 32, 32)) / sc[:, :, None]
+    over = (r > O.magnitudes(fmt).max()).reshape(rows, k)
+    half = 1 << (O.element_bits(fmt) - 1)
+    return np.where(over, codes & half, codes).astype(np.uint8), scales
+
+
+def _gemm_k_reversed_w(a, w):
+    """W's K axis read in reverse (a transposed-index slip)."""
+    return _ORIG_GEMM(a, np.asarray(w)[:, ::-1])
+
+
+def _check_fp32_loose(gpu, c, s):
+    return np.abs(np.asarray(gpu, dtype=np.float64) - c) <= 1e-4 * s
 
 
 MUTANTS = [
@@ -135,6 +193,13 @@ MUTANTS = [
       lambda: pins.test_fp8_decode_matches_torch("e4m3", pins.torch.float8_e4m3fn)]),
     ("pack", _fp4_nibbles_swapped, [pins.test_pack_cases_fp4_fp8]),
     ("emax_elem", _emax_plus_one, [lambda: pins.test_quantize_matches_exact_brute_force("e5m2")]),
+    ("e8m0_value", _e8m0_bias_128, [lambda: pins.test_exhaustive_round_trip("e2m3")]),
+    ("unpack", _unpack_msb_first, [pins.test_pack_round_trip_random]),
+    ("rmsnorm_modulate", _rms_mean_over_rows, [pins.test_rmsnorm_matches_torch]),
+    ("quantize", _quantize_no_saturation, [pins.test_block_cases]),
+    ("gemm_ref", _gemm_k_reversed_w,
+     [lambda: pins.test_gemm_exact_integer_brute_force("e2m3", "e3m2", 4, 4, 32)]),
+    ("check_fp32", _check_fp32_loose, [pins.test_tolerance_checks]),
 ]
 
 
