@@ -101,6 +101,9 @@
  *     4 GiB, or when a kernel would need 2^32 lanes or more (a dispatch holds
  *     its grid size in 32 bits).  Inside those limits every byte offset is
  *     computed in 64 bits, so buffers may be far larger than 4 GiB;
+ *   - the header is plain C99 as well as C++: a C program compiles it with
+ *     -D__HIP_PLATFORM_AMD__ -I/opt/rocm/include (what hipcc passes, for
+ *     hipStream_t) and links -lmxgemm; tests/abi_from_c.c does exactly that;
  *   - launch log: with the environment variable MXGEMM_LOG=1 (read once, at
  *     the first call), every call of mx_quantize, mx_rmsnorm_quantize,
  *     mx_gemm, mx_gemm_with_config, mx_gemm_splitk and

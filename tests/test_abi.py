@@ -282,6 +282,26 @@ def test_size_limits_rejected_before_launch(L):
     assert sk(n=1 << 30, k=128, splits=1, ldo=1 << 30) == B.MX_ERR_UNSUPPORTED
 
 
+def test_abi_from_plain_c(L, tmp_path):
+    """tests/abi_from_c.c: the header compiles as C99 with gcc, the program
+    links against libmxgemm.so, and the calls that need no device (version,
+    status strings, sizes, configurations, argument errors) answer as the
+    header says."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    exe = tmp_path / "abi_from_c"
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", os.path.join(ROOT, "tests", "abi_from_c.c"), "-L", os.path.dirname(B.LIB_PATH),
+           "-lmxgemm", f"-Wl,-rpath,{os.path.dirname(B.LIB_PATH)}", "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert run.stdout.count("ok  ") == 16, run.stdout
+
+
 def test_packed_bytes(L):
     assert mx.mx_packed_bytes(300, 416, "rows", 0) == 300 * 416 * 3 // 4
     assert mx.mx_packed_bytes(300, 416, "rows", 1) == 300 * 13
