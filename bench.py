@@ -262,6 +262,41 @@ def bench_proj(table, iters: int = 50):
             "algorithmic_bytes": alg, "gb_s": round(alg / c["median"] / 1e6, 1)}
 
 
+def bench_mlp_share(table, m: int = 2560, iters: int = 50):
+    """The MLP step on one GPU's share of the 20480 tokens when sequence
+    parallelism spreads them over 8 GPUs (2560 tokens: quantize x, fc1 GELU ->
+    E2M3, fc2 bf16), with the same weights, three rotating buffer sets and
+    the tuning table's configurations (the nearest tuned shapes)."""
+    fc1, fc2 = syn.WORKLOADS["fc1"], syn.WORKLOADS["fc2"]
+    d, hdim = fc1.k, fc1.n
+    dev = torch.device("cuda:0")
+    x_host = syn.make_a(fc1, m=m)
+    xs = [x_host.to(dev) for _ in range(SETS)]
+    w1s = [mx.mx_quantize(syn.make_w(fc1).to(dev), "e2m3") for _ in range(SETS)]
+    w2s = [mx.mx_quantize(syn.make_w(fc2).to(dev), "e2m3") for _ in range(SETS)]
+    xqs = [mx.MXTensor.empty(m, d, "e2m3", "tiled", dev) for _ in range(SETS)]
+    hs = [mx.MXTensor.empty(m, hdim, "e2m3", "tiled", dev) for _ in range(SETS)]
+    ys = [torch.empty((m, d), dtype=torch.bfloat16, device=dev) for _ in range(SETS)]
+    cfg1 = (table.lookup(m, hdim, d, epilogue="gelu_tanh", out_kind="mx")
+            or mx.mx_gemm_select_config(m, hdim, d, epilogue="gelu_tanh", out_kind="mx"))
+    cfg2 = table.lookup(m, d, hdim) or mx.mx_gemm_select_config(m, d, hdim)
+
+    def step(i):
+        j = i % SETS
+        mx.mx_quantize(xs[j], "e2m3", "tiled", out=xqs[j])
+        mx.mx_gemm(xqs[j], w1s[j], out_kind="mx", epilogue="gelu_tanh", out=hs[j], config=cfg1)
+        mx.mx_gemm(hs[j], w2s[j], out_kind="bf16", out=ys[j], config=cfg2)
+
+    settle(lambda: step(0))
+    t = time_batches(step, iters)
+    flops = 2 * 2.0 * m * d * hdim
+    return {"workload": f"DiT MLP step on {m} tokens (one GPU's share of 20480 over 8 GPUs): quantize x, "
+                        f"fc1 {m}x3072x12288 (GELU -> E2M3), fc2 {m}x12288x3072 (bf16 out)",
+            "tokens": m, "ms_per_step": t, "tflops": round(flops / t["median"] / 1e9, 1),
+            "frac": round(flops / t["median"] / 1e9 / PEAK_MXFP6_TFLOPS, 4),
+            "configs": [list(cfg1.key()), list(cfg2.key())]}
+
+
 def bench_tiny(iters: int = 50):
     """The tiny 256^3 GEMM (E2M3 x E2M3, fp32 out, activations quantized in
     the call): launch-latency bound, reported for completeness."""
@@ -686,6 +721,8 @@ def main():
     skinny = [bench_skinny(mm, ss, args.skinny_iters) for ss in (16, 8) for mm in (16, 8)]
     proj = bench_proj(table if not args.no_tune else tuning.TuningTable())
     tiny = bench_tiny()
+    share = bench_mlp_share(table if not args.no_tune else tuning.TuningTable())
+    share["full_step_ms_over_8"] = round(ms_step / 8, 4)
     swiglu = bench_swiglu_mlp(table if not args.no_tune else tuning.TuningTable(), args.steps, args.warmup)
     producer = bench_producer()
     stacked = bench_stacked_projection(table if not args.no_tune else tuning.TuningTable())
@@ -729,6 +766,7 @@ def main():
                               **r["producer_step"]},
         "proj": proj,
         "tiny": tiny,
+        "share_of_8_gpus": share,
         "skinny_splitk": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s_.items()} for s_ in skinny],
         "swiglu_mlp": swiglu,
         "producer": producer,

@@ -4,7 +4,8 @@ save the table:
     python -m microscaled_precision_gemm_amd.tune_workloads OUT.json
 
 The shapes are the DiT MLP (fc1 with the GELU -> E2M3 epilogue, fc2 to
-bf16), its SwiGLU variant (gate/up with the SwiGLU -> E2M3 epilogue, down
+bf16), the same two GEMMs on one GPU's share of the tokens over 8 GPUs (2560
+tokens), its SwiGLU variant (gate/up with the SwiGLU -> E2M3 epilogue, down
 projection to bf16), the attention projection, and fc1's shape in each
 operand format (bf16 out), all on seeded synthetic operands of the workloads'
 distributions.  The table shipped with the package (``tuning.SHIPPED_TABLE``)
@@ -50,6 +51,15 @@ def tune_all(table: TuningTable, log=print) -> TuningTable:
     h = mx.mx_gemm(xq, w1, out_kind="mx", epilogue="swiglu")
     w2 = mx.mx_quantize(syn.make_w(s2).to(dev), "e2m3")
     show("SwiGLU down", tune_gemm(table, h, w2, out_kind="bf16"))
+    del xq, w1, h, w2
+
+    # one GPU's share of the 20480 tokens over 8 GPUs (sequence parallelism)
+    xq = mx.mx_quantize(syn.make_a(fc1, m=2560).to(dev), "e2m3")
+    w1 = mx.mx_quantize(syn.make_w(fc1).to(dev), "e2m3")
+    show("fc1 share of 8 GPUs", tune_gemm(table, xq, w1, out_kind="mx", epilogue="gelu_tanh"))
+    h = mx.mx_gemm(xq, w1, out_kind="mx", epilogue="gelu_tanh")
+    w2 = mx.mx_quantize(syn.make_w(fc2).to(dev), "e2m3")
+    show("fc2 share of 8 GPUs", tune_gemm(table, h, w2, out_kind="bf16"))
     del xq, w1, h, w2
 
     p = syn.WORKLOADS["proj"]

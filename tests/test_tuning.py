@@ -156,7 +156,9 @@ def test_shipped_table_covers_the_workloads():
              dict(m=20480, n=3072, k=12288),
              dict(m=20480, n=16384, k=3072, epilogue="swiglu", out_kind="mx"),
              dict(m=20480, n=3072, k=8192),
-             dict(m=4096, n=3072, k=3072)]
+             dict(m=4096, n=3072, k=3072),
+             dict(m=2560, n=12288, k=3072, epilogue="gelu_tanh", out_kind="mx"),
+             dict(m=2560, n=3072, k=12288)]
     calls += [dict(m=20480, n=12288, k=3072, a_fmt=f, w_fmt=f) for f in ("e2m3", "e2m1", "e4m3")]
     for c in calls:
         cfg = t.lookup(device=dev, **c)
@@ -167,15 +169,15 @@ def test_shipped_table_covers_the_workloads():
 
 @pytest.mark.gpu
 def test_warm_start_for_an_untuned_token_count():
-    """2560 tokens (one GPU's share of the 20480 when the tokens are split
-    eight ways) is not in the shipped table.  lookup() gives it the fc1
-    entry's configuration (not the generic one), whose output is
-    bit-identical to the generic configuration's and to the shape rule's; a
+    """12288 tokens (a shorter sequence than the workload's 20480) is not in
+    the shipped table.  lookup() gives it the configuration of the nearest
+    tuned fc1 shape, the 20480-token entry (not the generic one), whose output
+    is bit-identical to the generic configuration's and to the shape rule's; a
     warm-started tune starts from that entry and keeps a configuration no
     slower than the generic one."""
     from tests.parity import say
     torch.manual_seed(1)
-    m, k, n = 2560, 3072, 12288
+    m, k, n = 12288, 3072, 12288
     shipped = T.TuningTable(T.SHIPPED_TABLE)
     dev = T.device_name()
     src = shipped.source(m, n, k, epilogue="gelu_tanh", out_kind="mx")
@@ -186,7 +188,7 @@ def test_warm_start_for_an_untuned_token_count():
     assert cfg.key() != mx.mx_gemm_default_config().key()
     a = mx.mx_quantize(torch.randn(m, k, device="cuda").to(torch.bfloat16), "e2m3")
     w = mx.mx_quantize((torch.randn(n, k, device="cuda") * 0.02).to(torch.bfloat16), "e2m3")
-    say("warm-started tuning 2560x3072x12288 gelu->mx")
+    say("warm-started tuning 12288x3072x12288 gelu->mx")
     outs = [mx.mx_gemm(a, w, out_kind="mx", epilogue="gelu_tanh", config=c)
             for c in (cfg, mx.mx_gemm_default_config(), None)]
     torch.cuda.synchronize()
