@@ -1,5 +1,5 @@
-"""Randomized shapes, deterministic: a seeded draw of GEMM, split-K and
-quantizer calls over ragged sizes, every element format pair, output kind,
+"""Randomized shapes, deterministic: a seeded draw of GEMM, split-K,
+quantizer and producer calls over ragged sizes, every element format pair, output kind,
 epilogue and launch configuration the library accepts, each checked against
 the oracle at the bar of its kind.  The draw is fixed at import (the test
 ids name each case), so a failure reproduces by its id.
@@ -184,3 +184,43 @@ def test_random_quantize(case):
     torch.cuda.synchronize()
     codes, scales = O.quantize(xt[:, :k].to(torch.float64).numpy(), fmt)
     assert_mx_equal(q, codes, scales, f"quantize {case}")
+
+
+def _draw_producer_cases(count=16, seed=2027):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        rows = int(rng.integers(1, 300))
+        # half up to 3072 (bf16 rows stay in registers), half up to 6368 (the two-pass kernel)
+        d = int(32 * rng.integers(1, 97 if rng.random() < 0.5 else 200))
+        per = int(32 * rng.integers(1, 5)) if rng.random() < 0.7 else 0  # 0: no modulation
+        cases.append((i, ["bf16", "f32"][rng.integers(0, 2)], ["e2m3", "e3m2"][rng.integers(0, 2)], rows, d, per,
+                      bool(rng.random() < 0.7), int(8 * rng.integers(0, 3))))
+    return cases
+
+
+PRODUCER_CASES = _draw_producer_cases()
+
+
+@pytest.mark.parametrize("case", PRODUCER_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}-{c[3]}x{c[4]}-per{c[5]}-g{int(c[6])}+{c[7]}" for c in PRODUCER_CASES])
+def test_random_producer(case):
+    from tests.parity import rmsnorm_bound
+    i, src, fmt, rows, d, per, with_gamma, pad = case
+    say(f"fuzz producer {case}")
+    rng = np.random.default_rng([6000, i])
+    x = (rng.standard_normal((rows, d + pad)) * np.exp2(rng.integers(-6, 7, (rows, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).to(torch.bfloat16 if src == "bf16" else torch.float32)
+    n_cond = -(-rows // per) if per else 0
+    gamma = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32) if with_gamma else None
+    shift = (0.5 * rng.standard_normal((n_cond, d))).astype(np.float32) if per else None
+    scale = (0.3 * rng.standard_normal((n_cond, d))).astype(np.float32) if per else None
+    dev = lambda v: None if v is None else torch.from_numpy(v).cuda()  # noqa: E731
+    hq = mx.mx_rmsnorm_quantize(xt.cuda()[:, :d], dev(gamma), dev(shift), dev(scale), per, 1e-6, fmt)
+    torch.cuda.synchronize()
+    x64 = xt[:, :d].to(torch.float64).numpy()
+    y = O.rmsnorm_modulate(x64, gamma, shift, scale, per if per else None, 1e-6)
+    y32 = y.astype(np.float32).astype(np.float64)
+    gc, gs = mx_rows_view(hq)
+    stats = check_mx_values(gc, gs, y32, rmsnorm_bound(x64, gamma, scale, per if per else None, 1e-6, y32), fmt)
+    assert stats["exact"] >= 0.999 * stats["elements"], stats
