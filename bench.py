@@ -703,7 +703,7 @@ def main():
                    help="also run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = p.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU (the sharded path is a design, not a measurement here); --gpus must be 1"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
