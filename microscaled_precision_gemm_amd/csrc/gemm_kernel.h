@@ -448,7 +448,8 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
   // copies scheduled after it.
   // Phase 1: sub-step 1 MFMAs, reads of the next stage's sub-step 0 operands
   // and scales, and the first kFirst copies of stage ks2 into slot slot2.
-  auto phase1 = [&](const Half& r, const Scales& c, int ks2, int slot2, int nsl, Half& nr, Scales& ns) {
+  auto phase1 = [&](const Half& r, const Scales& c, int ks2, int slot2, int nsl, Half& nr, Scales& ns, auto copy_tag) {
+    constexpr bool kCopy = decltype(copy_tag)::value;
     const int so = nsl * R::kSlot;
     static_for(
         [&](auto i) {
@@ -462,7 +463,8 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
               if constexpr (decltype(k)::value < nsr) read_scale(ns, so, std::integral_constant<int, s0 + decltype(k)::value>{});
             }, SeqN<kMP>{});
           }
-          constexpr int n = copies_after(I, R::kFirst, 1, kMP), c0 = first_copy_after(I, R::kFirst, 1, kMP);
+          constexpr int n = kCopy ? copies_after(I, R::kFirst, 1, kMP) : 0;
+          constexpr int c0 = first_copy_after(I, R::kFirst, 1, kMP);
 #pragma unroll
           for (int k = 0; k < n; ++k) issue_one(c0 + k, ks2, slot2);
         },
@@ -473,21 +475,23 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           constexpr int ds = (I < kNF ? (frag_is_w(I) ? kDsW : kDsX) : 0) + scale_reads_after(I, kNF, kNF, kMP);
           if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
-          constexpr int n = copies_after(I, R::kFirst, 1, kMP);
+          constexpr int n = kCopy ? copies_after(I, R::kFirst, 1, kMP) : 0;
           if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
         },
         SeqN<kMP>{});
   };
   // Phase 0: sub-step 0 MFMAs, reads of the same stage's sub-step 1
   // operands, and copies kFirst.. of stage ks2 into slot slot2.
-  auto phase0 = [&](const Half& r, const Scales& c, int sl, Half& nr, int ks2, int slot2) {
+  auto phase0 = [&](const Half& r, const Scales& c, int sl, Half& nr, int ks2, int slot2, auto copy_tag) {
+    constexpr bool kCopy = decltype(copy_tag)::value;
     const int so = sl * R::kSlot;
     static_for(
         [&](auto i) {
           constexpr int I = decltype(i)::value;
           mfma(r, c, i, sub0{});
           if constexpr (I < kNF) read_frag(nr, so, i, sub1{});
-          constexpr int n = copies_after(I, R::kSecond, 0, kMP), c0 = first_copy_after(I, R::kSecond, 0, kMP);
+          constexpr int n = kCopy ? copies_after(I, R::kSecond, 0, kMP) : 0;
+          constexpr int c0 = first_copy_after(I, R::kSecond, 0, kMP);
 #pragma unroll
           for (int k = 0; k < n; ++k) issue_one(R::kFirst + c0 + k, ks2, slot2);
         },
@@ -498,11 +502,13 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           constexpr int ds = I < kNF ? (frag_is_w(I) ? kDsW : kDsX) : 0;
           if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
-          constexpr int n = copies_after(I, R::kSecond, 0, kMP);
+          constexpr int n = kCopy ? copies_after(I, R::kSecond, 0, kMP) : 0;
           if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);
         },
         SeqN<kMP>{});
   };
+  using copies = std::true_type;
+  using no_copies = std::false_type;
   auto next_slot = [](int sl) { return sl + 1 == R::kSlots ? 0 : sl + 1; };
 
   // ---- main loop over the ring, with the operand registers double buffered
@@ -539,17 +545,63 @@ __global__ __launch_bounds__(64 * WV, TN == 256 ? 1 : 2) void gemm_kernel(const 
   for (; ks + R::kSlots < nk; ++ks) {
     const int nsl = next_slot(slot);
     Half rb;
-    phase0(ra, sc, slot, rb, ks + 2, next_slot(nsl));
+    phase0(ra, sc, slot, rb, ks + 2, next_slot(nsl), copies{});
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kMidWait));
     __builtin_amdgcn_s_barrier();
     Scales sn;
-    phase1(rb, sc, ks + R::kSlots, slot, nsl, ra, sn);
+    phase1(rb, sc, ks + R::kSlots, slot, nsl, ra, sn, copies{});
     __builtin_amdgcn_sched_barrier(0);
     sc = sn;
     slot = nsl;
   }
-  for (; ks < nk; ++ks) {
+  // The last kSlots stages, straight-line, with the steady state's phases:
+  // only the copies that still exist (with three slots, the second half of
+  // stage nk - 1's, in the first of them), and the wait for the next stage
+  // tightened to every copy once no copy of a later stage is outstanding.
+  // Sharing the phases keeps the steady state's register allocation: the
+  // generic loop below spilled address registers in the 6- and 8-bit kernels,
+  // and each reload waited for every copy in flight (fc1: 508 -> 480 us,
+  // bit-identical).  4-bit operands keep the loop, which does not spill there
+  // and measured 2.5 % faster with 8 waves.
+  if (R::kBW != 4 && nk >= R::kSlots) {
+    if constexpr (R::kSlots == 3) {
+      const int nsl = next_slot(slot);
+      Half rb;
+      phase0(ra, sc, slot, rb, ks + 2, next_slot(nsl), copies{});
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(R::kCopies));
+      __builtin_amdgcn_s_barrier();
+      Scales sn;
+      phase1(rb, sc, 0, 0, nsl, ra, sn, no_copies{});
+      __builtin_amdgcn_sched_barrier(0);
+      sc = sn;
+      slot = nsl;
+      ++ks;
+    }
+    {
+      const int nsl = next_slot(slot);
+      Half rb;
+      phase0(ra, sc, slot, rb, 0, 0, no_copies{});
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      __builtin_amdgcn_s_barrier();
+      Scales sn;
+      phase1(rb, sc, 0, 0, nsl, ra, sn, no_copies{});
+      __builtin_amdgcn_sched_barrier(0);
+      sc = sn;
+      slot = nsl;
+      ++ks;
+    }
+    {
+      Half rb;
+      phase0(ra, sc, slot, rb, 0, 0, no_copies{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(rb, sc, sub1{});
+      ks = nk;
+    }
+  }
+  for (; ks < nk; ++ks) {  // K shorter than the ring (and the 4-bit operands' tail)
     const int nsl = next_slot(slot);
     if constexpr (R::kSlots == 3) {
       if (ks + 2 < nk) issue_range(ks + 2, next_slot(nsl), R::kFirst, R::kSecond);
