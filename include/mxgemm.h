@@ -94,7 +94,8 @@
  *   - MX_ERR_HIP reports a failed launch (hipGetLastError); a fault inside a
  *     kernel surfaces at the caller's next synchronization instead;
  *   - device pointers must be 16-byte aligned unless stated otherwise;
- *   - size limits: every dimension is at most 2^30 (else MX_ERR_SHAPE).
+ *   - size limits: every dimension, leading dimensions included, is at most
+ *     2^30 (else MX_ERR_SHAPE).
  *     Beyond that a request returns MX_ERR_UNSUPPORTED, before anything is
  *     launched, when a tiled MX matrix would hold 2^40 code bytes or more,
  *     when one 128-element stage of a GEMM operand (all its rows) would reach

@@ -79,7 +79,7 @@ int check_quantize_args(const void* src, int32_t src_type, int64_t rows, int64_t
   if (rows < 0 || k < 0 || k % 32 != 0 || rows > kMaxDim || k > kMaxDim) return MX_ERR_SHAPE;
   if (rows == 0 || k == 0) return MX_OK;
   if (!src || !codes || !scales) return MX_ERR_NULL;
-  if (ld_src < k) return MX_ERR_SHAPE;
+  if (ld_src < k || ld_src > kMaxDim) return MX_ERR_SHAPE;
   const int64_t esize = src_type == MX_SRC_BF16 ? 2 : 4;
   if (!aligned(src, 16) || (ld_src * esize) % 16 != 0) return MX_ERR_ALIGN;
   if (!aligned(codes, 16) || !aligned(scales, 4)) return MX_ERR_ALIGN;
@@ -121,7 +121,7 @@ int check_gemm_common(const void* a_src, int32_t a_src_type, int64_t lda, const 
   if ((a_src != nullptr) == (a_codes != nullptr)) return MX_ERR_NULL;  // exactly one activation form
   if (a_src) {
     if (a_src_type != MX_SRC_BF16 && a_src_type != MX_SRC_F32) return MX_ERR_FORMAT;
-    if (lda < k) return MX_ERR_SHAPE;
+    if (lda < k || lda > kMaxDim) return MX_ERR_SHAPE;
     const int64_t esize = a_src_type == MX_SRC_BF16 ? 2 : 4;
     if (!aligned(a_src, 16) || (lda * esize) % 16 != 0) return MX_ERR_ALIGN;
   } else {
@@ -144,7 +144,7 @@ int check_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const void*
   if (!fp6_fmt(a_fmt) || !fp6_fmt(w_fmt)) return MX_ERR_UNSUPPORTED;
   if (out_kind != MX_OUT_F32 && out_kind != MX_OUT_BF16) return MX_ERR_FORMAT;
   if (!out) return MX_ERR_NULL;
-  if (ldo < n) return MX_ERR_SHAPE;
+  if (ldo < n || ldo > kMaxDim) return MX_ERR_SHAPE;
   if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
   if (splits > kMaxSplits || k % (kTileStageK * (int64_t)splits) != 0) return MX_ERR_UNSUPPORTED;
   if (splitk_grid_items(n) > kMaxGridItems) return MX_ERR_UNSUPPORTED;
@@ -361,7 +361,7 @@ static int gemm_call(const void* a_src, int32_t a_src_type, int64_t lda, const v
     if (n_out % 32 != 0) return MX_ERR_UNSUPPORTED;
     if (!aligned(out, 16) || !aligned(out_scales, 4)) return MX_ERR_ALIGN;
   } else {
-    if (ldo < n_out) return MX_ERR_SHAPE;
+    if (ldo < n_out || ldo > kMaxDim) return MX_ERR_SHAPE;
     if (!aligned(out, out_kind == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
   }
   const size_t need = mx_gemm_workspace_size(m, n, k, a_src != nullptr, 0);

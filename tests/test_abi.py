@@ -280,6 +280,17 @@ def test_size_limits_rejected_before_launch(L):
     assert g(m=1 << 25, n=1 << 25, ldo=1 << 25) == B.MX_ERR_SHAPE  # 2^34 tiles
     # split-K: one workgroup of 256 lanes per 64 weight rows
     assert sk(n=1 << 30, k=128, splits=1, ldo=1 << 30) == B.MX_ERR_UNSUPPORTED
+    # leading dimensions are dimensions too: above 2^30 elements is MX_ERR_SHAPE
+    big = (1 << 30) + 64
+    assert q(FAKE, 0, 4, 64, big, 2, 1, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert q(FAKE, 1, 4, 64, big, 2, 0, FAKE, FAKE, s) == B.MX_ERR_SHAPE
+    assert rq(ld=big) == B.MX_ERR_SHAPE
+    assert g(a_src=FAKE, lda=big, a_codes=NULL, a_scales=NULL) == B.MX_ERR_SHAPE
+    assert g(ldo=big) == B.MX_ERR_SHAPE
+    assert g(out_kind=0, ldo=big) == B.MX_ERR_SHAPE
+    assert sk(ldo=big) == B.MX_ERR_SHAPE
+    assert sk(a_src=FAKE, lda=big, a_codes=NULL, a_scales=NULL) == B.MX_ERR_SHAPE
+    assert sk_noalloc(lda=big) == B.MX_ERR_SHAPE
 
 
 def test_abi_from_plain_c(L, tmp_path):
