@@ -369,8 +369,10 @@ int mx_gemm_splitk(const void* a_src, int32_t a_src_type, int64_t lda, const voi
  * of the library (1.5625 MiB: one 32-row group of k <= MX_NOALLOC_MAX_K
  * 6-bit codes and their scales), which each GPU the library runs on holds
  * until the process ends; its address is looked up once per device, on the
- * first call with that device current.  The caller still owns a_src / the
- * quantized operands, the weights and out.
+ * first call with that device current.  The array used is the one of the
+ * device current in the calling thread, so `stream` must belong to that
+ * device (unlike the other calls, which follow the stream).  The caller still
+ * owns a_src / the quantized operands, the weights and out.
  *
  * Arguments, results and errors as mx_gemm_splitk without the workspace
  * (the results are bit-identical to it), plus MX_ERR_SCRATCH when

@@ -414,9 +414,11 @@ def mx_gemm_splitk(a: torch.Tensor | MXTensor, w: MXTensor, splits: int, out_kin
     if noalloc:
         if workspace is not None:
             raise ValueError("mx_gemm_splitk_noalloc takes no workspace")
-        st = lib().mx_gemm_splitk_noalloc(_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af,
-                                          _ptr(w.codes), _ptr(w.scales), _fmt(w.fmt), m, n, k, splits, kind, _ptr(out),
-                                          out.stride(0), _stream(dev))
+        # the library's scratch is the current device's: make it the operands' device
+        with torch.cuda.device(dev):
+            st = lib().mx_gemm_splitk_noalloc(_ptr(a_src), src_type, lda, _ptr(a_codes), _ptr(a_scales), af,
+                                              _ptr(w.codes), _ptr(w.scales), _fmt(w.fmt), m, n, k, splits, kind,
+                                              _ptr(out), out.stride(0), _stream(dev))
         _check(st, "mx_gemm_splitk_noalloc")
         return out
     need = mx_gemm_workspace_size(m, n, k, a_src is not None, splits)
