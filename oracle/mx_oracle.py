@@ -50,7 +50,7 @@ computes, in float64 with numpy:
   NaN).  The same scale rule and rounding apply; special codes are never
   produced (finite magnitudes above the largest saturate to it).
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
 
 * all-zero block -> the scale exponent clamps to -127 (byte 0x00), codes +-0;
 * the sign bit of each code is the sign bit of the source value, so -0.0 and
