@@ -109,8 +109,11 @@ __device__ __forceinline__ v8i op1(const Pieces& p) {
 // LDS_SCALES: every wave streams at most kLdsStages stages.
 template <int WF, int XF, int OUT, bool LDS_SCALES>
 __global__ __launch_bounds__(kSkThreads) void splitk_kernel(const SplitKArgs g) {
-  // partial sums [split][token][feature], tokens 0..15, features of both groups
-  __shared__ __attribute__((aligned(16))) float part[kMaxSplits][16][32 * kSkGroups];
+  // partial sums [split][token][feature], tokens 0..15, features of both groups.
+  // Rows are padded by 4 floats: the 16 token lanes of a half-wave store 16
+  // bytes each at the same feature offset, and with 256-byte rows they would
+  // all land on the same four banks; 272-byte rows put them on 64 distinct banks.
+  __shared__ __attribute__((aligned(16))) float part[kMaxSplits][16][32 * kSkGroups + 4];
   // per wave: the scale bytes of its stages, in stage order
   __shared__ __attribute__((aligned(16))) uint8_t scw[LDS_SCALES ? kSkWaves : 1][LDS_SCALES ? kLdsStages : 1][kRecW];
   __shared__ __attribute__((aligned(16))) uint8_t scx[LDS_SCALES ? kSkWaves : 1][LDS_SCALES ? kLdsStages : 1][kRecX];
