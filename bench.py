@@ -744,6 +744,11 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp6_e2m3",
         "data": "synthetic",
+        "inputs": {"generator": "numpy default_rng([workload index, stream]); stream 0 = activations, 1 = weights, "
+                                "2 = the outlier-channel choice; float32 draws rounded to bfloat16 (RNE)",
+                   "seeds": {name: {"activations": [w.index, 0], "weights": [w.index, 1]}
+                             for name, w in syn.WORKLOADS.items()},
+                   "mlp_step": "x = fc1 activations, W1 = fc1 weights, W2 = fc2 weights; fc2 reads fc1's output"},
         "config": {"workload": "DiT MLP forward: quantize x, fc1 20480x3072x12288 (GELU-tanh -> E2M3), "
                                "fc2 20480x12288x3072 (bf16 out)",
                    "tokens": 20480, "d_model": 3072, "d_hidden": 12288, "buffer_sets": SETS,
