@@ -89,6 +89,9 @@
  *     long as their buffers do not overlap.  The one exception is
  *     mx_gemm_splitk_noalloc, whose calls on one GPU share a static device
  *     scratch array (see there);
+ *   - within one call, outputs (out, out_scales, codes, scales, the
+ *     workspace) must not overlap each other or any input: inputs are read
+ *     while outputs are written, and overlapping buffers are not detected;
  *   - argument errors are detected on the host before anything is launched
  *     and return a negative status; nothing is written in that case;
  *   - MX_ERR_HIP reports a failed launch (hipGetLastError); a fault inside a
